@@ -1,0 +1,217 @@
+/*
+ * mla.h -- C ABI of libmla: absorbed Multi-head Latent Attention (MLA) decode
+ * over a paged latent cache, and the cache append that fills it, on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed (sources cited by page title and section):
+ *
+ *  - Cache contents.  Each token of each sequence holds one row of
+ *    d_c + R values: the RMS-normalised latent c^ (d_c channels) followed by
+ *    the rotary key k^R (R channels).  "KV Compression -- DeepSeek-V3",
+ *    "How it works" (one map W_kv,a emits latent then pre-rotation key; the
+ *    latent is RMS-normalised; 512 + 64 values per token per layer) and
+ *    "DeepSeek-V2: MLA Explained", "Caching Strategy".
+ *
+ *  - Decode.  For sequence b, query row s and head i the result equals naive
+ *    MLA attention ("DeepSeek-V2: MLA Explained", "MLA Full Formulas",
+ *    sections 2 and 3):
+ *        o_i = sum_j softmax_j( (q^C_i . W_UK[i] c^_j + q^R_i . k^R_j) * scale )
+ *                    * W_UV[i] c^_j
+ *    computed in the weight-absorbed order the pages describe ("DeepSeek-V2:
+ *    MLA Explained", "Optimization Note"; "Latent Attention.", "Compress, then
+ *    rebuild"): q_lat = W_UK[i]^T q^C_i once per step, scores against the
+ *    cached latents, softmax, o_lat = sum_j p_j c^_j, then o_i = W_UV[i] o_lat.
+ *    Per-head keys and values are never formed.  scale defaults to
+ *    1/sqrt(qk_nope_dim + qk_rope_dim) (section 3's 1/sqrt(d_h + d_h^R)).
+ *    Row s sees tokens 0 .. seq_lens[b] - q_len + s (causal between the q_len
+ *    new tokens, which are already in the cache).
+ *
+ *  - Append.  For new token t of sequence b at position p = start_pos[b] + t:
+ *        x = W_kv,a h ;  row = [ RMSNorm(x[0:d_c]) * gamma ; RoPE(x[d_c:], p) ]
+ *    written to slot (block_table[b][p / block_size], p % block_size).
+ *    RMSNorm: x / sqrt(mean(x^2) + eps).  RoPE: pair (x[2k], x[2k+1]) rotated
+ *    by p * rope_base^(-2k/R).
+ *
+ * Conventions for every entry point:
+ *
+ *  - All tensors are dense, row-major, in device memory owned by the caller.
+ *    The library allocates nothing and keeps no state between calls; every
+ *    call is reentrant.  Buffers must stay alive until `stream` passes the
+ *    enqueued work.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; nothing synchronises the host.  seq_lens, start_pos and
+ *    block_table are read on the device only.
+ *  - Host-side validation runs before any launch.  A non-MLA_OK status means
+ *    nothing was enqueued, except MLA_ERR_HIP, which reports a failed launch.
+ *    mla_last_error() returns a message describing the last failure on the
+ *    calling thread.
+ *  - Device-side contract (not checked): block ids in block_table that a
+ *    sequence's tokens reach lie in [0, num_blocks); 1 <= q_len <= seq_lens[b]
+ *    (a row that would see no token produces zeros and lse = -inf).
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL            */
+    MLA_ERR_BAD_SHAPE = 2,           /* a size is out of range                */
+    MLA_ERR_UNSUPPORTED = 3,         /* dims / dtype combination not built    */
+    MLA_ERR_ALIGNMENT = 4,           /* a pointer is not 16-byte aligned      */
+    MLA_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < the size query      */
+    MLA_ERR_HIP = 6                  /* a HIP launch or runtime call failed   */
+} mla_status;
+
+typedef enum {
+    MLA_F32 = 0,
+    MLA_BF16 = 1,
+    MLA_FP8_E4M3 = 2  /* OCP e4m3 ("e4m3fn"): bias 7, max 448, no infinities */
+} mla_dtype;
+
+/* Shape and storage types of one MLA layer.
+ *
+ * Two code paths exist:
+ *  - the MFMA path, for the DeepSeek-V3 head shape: n_heads 128,
+ *    kv_lora_rank 512, qk_rope_dim 64, qk_nope_dim 128, v_head_dim 128,
+ *    block_size 64, act_dtype BF16, cache_dtype BF16 or FP8_E4M3;
+ *  - a portable path for any other shape within the limits below
+ *    (n_heads <= 1024, kv_lora_rank <= 1024, qk_rope_dim <= 256 and even,
+ *    qk_nope_dim <= 512, v_head_dim <= 512, 1 <= block_size <= 4096),
+ *    act_dtype F32 or BF16, cache_dtype F32, BF16 or FP8_E4M3.
+ * Both compute in fp32 and give the same result up to rounding. */
+typedef struct {
+    int32_t n_heads;       /* H                                              */
+    int32_t kv_lora_rank;  /* d_c: latent width                              */
+    int32_t qk_rope_dim;   /* R = d_h^R: rotary key / query width            */
+    int32_t qk_nope_dim;   /* N = d_h: per-head content query width          */
+    int32_t v_head_dim;    /* V: per-head output width                       */
+    int32_t block_size;    /* tokens per cache block                         */
+    int32_t cache_dtype;   /* mla_dtype of the cache pool                    */
+    int32_t act_dtype;     /* mla_dtype of q, weights, h, gamma and out      */
+    float softmax_scale;   /* 0 => 1/sqrt(qk_nope_dim + qk_rope_dim)         */
+} mla_dims;
+
+/* Status name, e.g. "MLA_ERR_BAD_SHAPE". Never NULL. */
+const char* mla_status_string(mla_status status);
+
+/* Message for the last non-OK status returned on the calling thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char* mla_last_error(void);
+
+/* Bytes of one cache row: (kv_lora_rank + qk_rope_dim) * element size.
+ * Returns 0 for an invalid dims pointer or dtype. */
+size_t mla_cache_row_bytes(const mla_dims* dims);
+
+/* Bytes of one cache block: block_size * mla_cache_row_bytes(dims).  The pool
+ * is an array of these, [num_blocks][block_size][kv_lora_rank + qk_rope_dim].
+ * With FP8_E4M3 the per-token fp32 scales live in a separate array
+ * cache_scale[num_blocks][block_size]. */
+size_t mla_cache_block_bytes(const mla_dims* dims);
+
+/* Workspace bytes mla_cache_append needs for `batch * n_new` new tokens. */
+mla_status mla_cache_append_workspace_size(const mla_dims* dims, int32_t batch,
+                                           int32_t n_new, int32_t d_model,
+                                           size_t* bytes);
+
+/* Project, normalise, rotate and store `n_new` new tokens per sequence.
+ *
+ *  h             [batch][n_new][d_model]            act_dtype
+ *  w_kv_a        [kv_lora_rank + qk_rope_dim][d_model] act_dtype; latent rows first
+ *  kv_norm_gamma [kv_lora_rank]                     act_dtype
+ *  rms_eps       RMSNorm epsilon (added to mean(x^2))
+ *  rope_base     RoPE base (10000 for DeepSeek)
+ *  block_table   [batch][max_blocks_per_seq] int32, device
+ *  start_pos     [batch] int32, device: position of sequence b's first new token
+ *  cache_pool    [num_blocks][block_size][kv_lora_rank + qk_rope_dim] cache_dtype
+ *  cache_scale   [num_blocks][block_size] float, FP8_E4M3 only (else NULL):
+ *                receives amax/448 of each written row; the row holds
+ *                round-to-nearest-even(x / scale), saturated to +-448
+ *  workspace     device scratch of at least mla_cache_append_workspace_size bytes
+ *
+ * Only the batch * n_new addressed rows (and their scales) are written.  bf16
+ * and fp8 stores round to nearest even.  d_model must be a multiple of 8. */
+mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t n_new,
+                            int32_t d_model, const void* h, const void* w_kv_a,
+                            const void* kv_norm_gamma, float rms_eps, float rope_base,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* start_pos, void* cache_pool,
+                            float* cache_scale, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Split-KV partitions mla_decode_absorbed uses when num_splits == 0: a
+ * function of batch and q_len only (the host never reads sequence lengths). */
+int32_t mla_decode_default_splits(const mla_dims* dims, int32_t batch, int32_t q_len);
+
+/* Workspace bytes mla_decode_absorbed needs.  num_splits 0 = the default. */
+mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch,
+                                     int32_t q_len, int32_t num_splits,
+                                     size_t* bytes);
+
+/* Stages of one decode, for mla_decode_absorbed_stages. */
+enum {
+    MLA_STAGE_ABSORB_Q = 1,  /* q_lat = W_UK^T q_nope, packed with q_pe        */
+    MLA_STAGE_SPLIT_KV = 2,  /* per-partition attention over the latent cache */
+    MLA_STAGE_COMBINE = 4,   /* log-sum-exp merge of partitions, then W_UV    */
+    MLA_STAGE_ALL = 7
+};
+
+/* One absorbed-MLA decode step over a paged latent cache.
+ *
+ *  q_nope       [batch][q_len][n_heads][qk_nope_dim] act_dtype
+ *  q_pe         [batch][q_len][n_heads][qk_rope_dim] act_dtype, already rotated
+ *  w_uk         [n_heads][qk_nope_dim][kv_lora_rank] act_dtype (k^C = W_UK[i] c^)
+ *  w_uv         [n_heads][v_head_dim][kv_lora_rank]  act_dtype (v^C = W_UV[i] c^)
+ *  cache_pool   [num_blocks][block_size][kv_lora_rank + qk_rope_dim] cache_dtype
+ *  cache_scale  [num_blocks][block_size] float (FP8_E4M3 only, else NULL):
+ *               a cached value is float(code) * scale of its token
+ *  block_table  [batch][max_blocks_per_seq] int32, device
+ *  seq_lens     [batch] int32, device: tokens of sequence b, the q_len new
+ *               ones included
+ *  num_splits   split-KV partitions per (sequence, query row), 0 = default,
+ *               at most 256.  Partition k of a row that sees n tokens covers
+ *               tokens [k*P, (k+1)*P) with P = ceil(n / (num_splits *
+ *               block_size)) * block_size; empty partitions are skipped.
+ *  out          [batch][q_len][n_heads][v_head_dim] act_dtype
+ *  lse          [batch][q_len][n_heads] float or NULL: natural-log
+ *               log-sum-exp of the scaled scores (-inf for a row with no token)
+ *  workspace    device scratch of at least mla_decode_workspace_size bytes
+ *
+ * The MFMA path needs q_nope, q_pe, w_uk, w_uv, cache_pool and out 16-byte
+ * aligned.  seq_lens is not updated. */
+mla_status mla_decode_absorbed(const mla_dims* dims, int32_t batch, int32_t q_len,
+                               const void* q_nope, const void* q_pe,
+                               const void* w_uk, const void* w_uv,
+                               const void* cache_pool, const float* cache_scale,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, int32_t num_splits,
+                               void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* mla_decode_absorbed restricted to the stages in `stages` (MLA_STAGE_* bits),
+ * for timing or overlapping the stages separately.  Running ABSORB_Q, then
+ * SPLIT_KV, then COMBINE with the same arguments and workspace equals one
+ * mla_decode_absorbed call; each stage reads what the previous one left in
+ * the workspace. */
+mla_status mla_decode_absorbed_stages(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                      const void* q_nope, const void* q_pe,
+                                      const void* w_uk, const void* w_uv,
+                                      const void* cache_pool, const float* cache_scale,
+                                      const int32_t* block_table,
+                                      int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t num_splits,
+                                      void* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, uint32_t stages,
+                                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

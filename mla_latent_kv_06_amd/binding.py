@@ -1,0 +1,246 @@
+"""ctypes binding of libmla (C ABI in include/mla.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, then their data pointers and torch's current HIP stream are handed
+to the library.  Every step of the computation runs in the library's kernels.
+Importing this module loads ``libmla.so`` and raises if it has not been built
+(``python -m mla_latent_kv_06_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loads the HIP runtime the library binds to
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"libmla.so not found at {_LIB_PATH}; build it with "
+                      "`python -m mla_latent_kv_06_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+# ---- mirror of include/mla.h ---------------------------------------------------
+
+MLA_OK = 0
+STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_BAD_SHAPE",
+                3: "MLA_ERR_UNSUPPORTED", 4: "MLA_ERR_ALIGNMENT",
+                5: "MLA_ERR_WORKSPACE_TOO_SMALL", 6: "MLA_ERR_HIP"}
+MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+STAGE_ABSORB_Q, STAGE_SPLIT_KV, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
+
+DTYPE_CODES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
+_TORCH_OF = {MLA_F32: (torch.float32,), MLA_BF16: (torch.bfloat16,),
+             MLA_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn)}
+
+EXPORTED = ("mla_status_string", "mla_last_error", "mla_cache_row_bytes",
+            "mla_cache_block_bytes", "mla_cache_append_workspace_size", "mla_cache_append",
+            "mla_decode_default_splits", "mla_decode_workspace_size", "mla_decode_absorbed",
+            "mla_decode_absorbed_stages")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("kv_lora_rank", ctypes.c_int32),
+                ("qk_rope_dim", ctypes.c_int32), ("qk_nope_dim", ctypes.c_int32),
+                ("v_head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("cache_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+    @classmethod
+    def make(cls, n_heads, kv_lora_rank, qk_rope_dim, qk_nope_dim, v_head_dim, block_size,
+             cache_dtype="bf16", act_dtype="bf16", softmax_scale=0.0):
+        cd = DTYPE_CODES[cache_dtype] if isinstance(cache_dtype, str) else cache_dtype
+        ad = DTYPE_CODES[act_dtype] if isinstance(act_dtype, str) else act_dtype
+        return cls(n_heads, kv_lora_rank, qk_rope_dim, qk_nope_dim, v_head_dim, block_size,
+                   cd, ad, softmax_scale)
+
+    @classmethod
+    def from_workload(cls, wl, softmax_scale=0.0):
+        return cls.make(wl.n_heads, wl.kv_lora_rank, wl.qk_rope_dim, wl.qk_nope_dim,
+                        wl.v_head_dim, wl.block_size, wl.cache_dtype, wl.act_dtype,
+                        softmax_scale)
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_DP = ctypes.POINTER(Dims)
+
+_lib.mla_status_string.restype = ctypes.c_char_p
+_lib.mla_status_string.argtypes = [ctypes.c_int]
+_lib.mla_last_error.restype = ctypes.c_char_p
+_lib.mla_last_error.argtypes = []
+_lib.mla_cache_row_bytes.restype = _SZ
+_lib.mla_cache_row_bytes.argtypes = [_DP]
+_lib.mla_cache_block_bytes.restype = _SZ
+_lib.mla_cache_block_bytes.argtypes = [_DP]
+_lib.mla_cache_append_workspace_size.restype = ctypes.c_int
+_lib.mla_cache_append_workspace_size.argtypes = [_DP, _I, _I, _I, ctypes.POINTER(_SZ)]
+_lib.mla_cache_append.restype = ctypes.c_int
+_lib.mla_cache_append.argtypes = [_DP, _I, _I, _I, _P, _P, _P, ctypes.c_float, ctypes.c_float,
+                                  _P, _I, _P, _P, _P, _P, _SZ, _P]
+_lib.mla_decode_default_splits.restype = _I
+_lib.mla_decode_default_splits.argtypes = [_DP, _I, _I]
+_lib.mla_decode_workspace_size.restype = ctypes.c_int
+_lib.mla_decode_workspace_size.argtypes = [_DP, _I, _I, _I, ctypes.POINTER(_SZ)]
+_lib.mla_decode_absorbed.restype = ctypes.c_int
+_lib.mla_decode_absorbed.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I,
+                                     _P, _P, _P, _SZ, _P]
+_lib.mla_decode_absorbed_stages.restype = ctypes.c_int
+_lib.mla_decode_absorbed_stages.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I,
+                                            _P, _P, _P, _SZ, ctypes.c_uint32, _P]
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.mla_last_error().decode()
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def _check(st: int, where: str):
+    if st != MLA_OK:
+        raise MLAError(st, where)
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.mla_status_string(status).decode()
+
+
+def cache_row_bytes(dims: Dims) -> int:
+    return _lib.mla_cache_row_bytes(ctypes.byref(dims))
+
+
+def cache_block_bytes(dims: Dims) -> int:
+    return _lib.mla_cache_block_bytes(ctypes.byref(dims))
+
+
+def default_splits(dims: Dims, batch: int, q_len: int) -> int:
+    return _lib.mla_decode_default_splits(ctypes.byref(dims), batch, q_len)
+
+
+def decode_workspace_size(dims: Dims, batch: int, q_len: int, num_splits: int = 0) -> int:
+    n = _SZ(0)
+    _check(_lib.mla_decode_workspace_size(ctypes.byref(dims), batch, q_len, num_splits,
+                                          ctypes.byref(n)), "mla_decode_workspace_size")
+    return n.value
+
+
+def append_workspace_size(dims: Dims, batch: int, n_new: int, d_model: int) -> int:
+    n = _SZ(0)
+    _check(_lib.mla_cache_append_workspace_size(ctypes.byref(dims), batch, n_new, d_model,
+                                                ctypes.byref(n)), "mla_cache_append_workspace_size")
+    return n.value
+
+
+# ---- tensor marshalling ------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtypes, shape=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def decode(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_table, seq_lens,
+           num_splits: int = 0, out=None, lse=None, workspace=None,
+           stages: int = STAGE_ALL, want_lse: bool = True):
+    """One absorbed-MLA decode step (mla_decode_absorbed[_stages]).
+
+    q_nope [B, Sq, H, N], q_pe [B, Sq, H, R] (act dtype); w_uk [H, N, d_c],
+    w_uv [H, V, d_c]; cache_pool [num_blocks, block_size, d_c + R] (cache dtype);
+    cache_scale [num_blocks, block_size] float32 (fp8 only); block_table
+    [B, max_blocks] int32; seq_lens [B] int32.  Returns (out, lse)."""
+    act = _TORCH_OF[dims.act_dtype]
+    B, Sq = q_nope.shape[0], q_nope.shape[1]
+    H, N, R = dims.n_heads, dims.qk_nope_dim, dims.qk_rope_dim
+    dc, V = dims.kv_lora_rank, dims.v_head_dim
+    dev = q_nope.device
+    _need(q_nope, "q_nope", act, (B, Sq, H, N), dev)
+    _need(q_pe, "q_pe", act, (B, Sq, H, R), dev)
+    _need(w_uk, "w_uk", act, (H, N, dc), dev)
+    _need(w_uv, "w_uv", act, (H, V, dc), dev)
+    _need(cache_pool, "cache_pool", _TORCH_OF[dims.cache_dtype], None, dev)
+    if cache_pool.dim() != 3 or cache_pool.shape[1:] != (dims.block_size, dc + R):
+        raise ValueError(f"cache_pool shape {tuple(cache_pool.shape)}")
+    if dims.cache_dtype == MLA_FP8_E4M3:
+        _need(cache_scale, "cache_scale", (torch.float32,), cache_pool.shape[:2], dev)
+    _need(block_table, "block_table", (torch.int32,), None, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table shape {tuple(block_table.shape)}")
+    _need(seq_lens, "seq_lens", (torch.int32,), (B,), dev)
+    if out is None:
+        out = torch.empty((B, Sq, H, V), dtype=act[0], device=dev)
+    _need(out, "out", act, (B, Sq, H, V), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), (B, Sq, H), dev)
+    ws_bytes = decode_workspace_size(dims, B, Sq, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), None, dev)
+    st = _lib.mla_decode_absorbed_stages(
+        ctypes.byref(dims), B, Sq, _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+        _ptr(cache_pool), _ptr(cache_scale), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), num_splits, _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel(), stages, _stream(dev))
+    _check(st, "mla_decode_absorbed_stages")
+    return out, lse
+
+
+def append(dims: Dims, h, w_kv_a, kv_norm_gamma, block_table, start_pos, cache_pool,
+           cache_scale=None, rms_eps: float = 1e-6, rope_base: float = 10000.0, workspace=None):
+    """Write the cache rows of h's new tokens (mla_cache_append).
+
+    h [B, n_new, d] (act dtype); w_kv_a [d_c + R, d]; kv_norm_gamma [d_c];
+    block_table [B, max_blocks] int32; start_pos [B] int32."""
+    act = _TORCH_OF[dims.act_dtype]
+    B, n_new, d = h.shape
+    dc, R = dims.kv_lora_rank, dims.qk_rope_dim
+    dev = h.device
+    _need(h, "h", act, None, dev)
+    _need(w_kv_a, "w_kv_a", act, (dc + R, d), dev)
+    _need(kv_norm_gamma, "kv_norm_gamma", act, (dc,), dev)
+    _need(block_table, "block_table", (torch.int32,), None, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table shape {tuple(block_table.shape)}")
+    _need(start_pos, "start_pos", (torch.int32,), (B,), dev)
+    _need(cache_pool, "cache_pool", _TORCH_OF[dims.cache_dtype], None, dev)
+    if dims.cache_dtype == MLA_FP8_E4M3:
+        _need(cache_scale, "cache_scale", (torch.float32,), cache_pool.shape[:2], dev)
+    ws_bytes = append_workspace_size(dims, B, n_new, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), None, dev)
+    st = _lib.mla_cache_append(
+        ctypes.byref(dims), B, n_new, d, _ptr(h), _ptr(w_kv_a), _ptr(kv_norm_gamma),
+        float(rms_eps), float(rope_base), _ptr(block_table), block_table.shape[1],
+        _ptr(start_pos), _ptr(cache_pool), _ptr(cache_scale), _ptr(workspace),
+        workspace.numel(), _stream(dev))
+    _check(st, "mla_cache_append")
+
+
+def softmax_scale(dims: Dims) -> float:
+    return dims.softmax_scale or 1.0 / math.sqrt(dims.qk_nope_dim + dims.qk_rope_dim)

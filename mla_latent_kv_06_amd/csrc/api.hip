@@ -1,0 +1,313 @@
+// C ABI of libmla (include/mla.h): argument validation, workspace layout and
+// dispatch to the MFMA or portable kernels.  Every check runs on the host
+// before anything is enqueued.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mla_status fail(mla_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+mla_status ok() {
+    g_err[0] = '\0';
+    return MLA_OK;
+}
+
+size_t elem_bytes(int dt) {
+    switch (dt) {
+        case MLA_F32: return 4;
+        case MLA_BF16: return 2;
+        case MLA_FP8_E4M3: return 1;
+        default: return 0;
+    }
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mla_status check_dims(const mla_dims* d) {
+    if (d == nullptr) return fail(MLA_ERR_NULL_POINTER, "dims is NULL");
+    if (d->n_heads < 1 || d->n_heads > 1024)
+        return fail(MLA_ERR_BAD_SHAPE, "n_heads=%d outside [1, 1024]", d->n_heads);
+    if (d->kv_lora_rank < 1 || d->kv_lora_rank > 1024)
+        return fail(MLA_ERR_BAD_SHAPE, "kv_lora_rank=%d outside [1, 1024]", d->kv_lora_rank);
+    if (d->qk_rope_dim < 0 || d->qk_rope_dim > 256 || (d->qk_rope_dim & 1))
+        return fail(MLA_ERR_BAD_SHAPE, "qk_rope_dim=%d must be even and in [0, 256]", d->qk_rope_dim);
+    if (d->qk_nope_dim < 1 || d->qk_nope_dim > 512)
+        return fail(MLA_ERR_BAD_SHAPE, "qk_nope_dim=%d outside [1, 512]", d->qk_nope_dim);
+    if (d->v_head_dim < 1 || d->v_head_dim > 512)
+        return fail(MLA_ERR_BAD_SHAPE, "v_head_dim=%d outside [1, 512]", d->v_head_dim);
+    if (d->block_size < 1 || d->block_size > 4096)
+        return fail(MLA_ERR_BAD_SHAPE, "block_size=%d outside [1, 4096]", d->block_size);
+    if (elem_bytes(d->cache_dtype) == 0)
+        return fail(MLA_ERR_UNSUPPORTED, "cache_dtype=%d unknown", d->cache_dtype);
+    if (d->act_dtype != MLA_F32 && d->act_dtype != MLA_BF16)
+        return fail(MLA_ERR_UNSUPPORTED, "act_dtype=%d must be MLA_F32 or MLA_BF16", d->act_dtype);
+    if (!(d->softmax_scale >= 0.f) || std::isinf(d->softmax_scale))
+        return fail(MLA_ERR_BAD_SHAPE, "softmax_scale must be finite and >= 0");
+    return MLA_OK;
+}
+
+float resolved_scale(const mla_dims& d) {
+    return d.softmax_scale > 0.f ? d.softmax_scale
+                                 : 1.0f / std::sqrt((float)(d.qk_nope_dim + d.qk_rope_dim));
+}
+
+int default_splits(int batch, int q_len) {
+    const long long rows = (long long)batch * q_len;
+    if (rows <= 0) return 1;
+    long long s = (mla::kNumCUs + rows - 1) / rows;
+    if (s > 64) s = 64;
+    return (int)(s < 1 ? 1 : s);
+}
+
+struct DecodeWs {
+    size_t qbuf, part_o, part_lse, total;
+};
+
+DecodeWs decode_ws(const mla_dims& d, int batch, int q_len, int splits) {
+    const bool mfma = mla::is_v3_shape(d);
+    const size_t R = (size_t)batch * q_len, H = d.n_heads;
+    DecodeWs w;
+    w.qbuf = 0;
+    size_t qb = R * H * (d.kv_lora_rank + d.qk_rope_dim) * (mfma ? 2 : 4);
+    w.part_o = align_up(qb, 256);
+    w.part_lse = w.part_o + align_up(R * splits * H * d.kv_lora_rank * sizeof(float), 256);
+    w.total = w.part_lse + align_up(R * splits * H * sizeof(float), 256);
+    return w;
+}
+
+constexpr int kAppendChunk = 512;
+
+int append_kc(int d_model) { return (d_model + kAppendChunk - 1) / kAppendChunk; }
+
+bool append_uses_mfma(const mla_dims& d, int d_model) {
+    return d.act_dtype == MLA_BF16 && (d.kv_lora_rank + d.qk_rope_dim) % 32 == 0 &&
+           d_model % 16 == 0;
+}
+
+mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
+                       const void* q_pe, const void* w_uk, const void* w_uv, const void* cache_pool,
+                       const float* cache_scale, const int32_t* block_table,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_splits,
+                       void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       unsigned stages, void* stream) {
+    if (mla_status st = check_dims(dims); st != MLA_OK) return st;
+    const mla_dims& d = *dims;
+    if (batch < 0 || q_len < 1 || q_len > 1024)
+        return fail(MLA_ERR_BAD_SHAPE, "batch=%d must be >= 0 and q_len=%d in [1, 1024]", batch, q_len);
+    if (num_splits < 0 || num_splits > mla::kMaxSplits)
+        return fail(MLA_ERR_BAD_SHAPE, "num_splits=%d outside [0, %d]", num_splits, mla::kMaxSplits);
+    if (stages == 0 || (stages & ~(unsigned)MLA_STAGE_ALL))
+        return fail(MLA_ERR_BAD_SHAPE, "stages=0x%x: use MLA_STAGE_* bits", stages);
+    if (batch == 0) return ok();
+    if (max_blocks_per_seq < 1) return fail(MLA_ERR_BAD_SHAPE, "max_blocks_per_seq must be >= 1");
+    const int splits = num_splits == 0 ? default_splits(batch, q_len) : num_splits;
+    if ((stages & MLA_STAGE_ABSORB_Q) && (!q_nope || !q_pe || !w_uk))
+        return fail(MLA_ERR_NULL_POINTER, "q_nope, q_pe and w_uk are required");
+    if ((stages & MLA_STAGE_SPLIT_KV) && (!cache_pool || !block_table || !seq_lens))
+        return fail(MLA_ERR_NULL_POINTER, "cache_pool, block_table and seq_lens are required");
+    if ((stages & MLA_STAGE_SPLIT_KV) && d.cache_dtype == MLA_FP8_E4M3 && !cache_scale)
+        return fail(MLA_ERR_NULL_POINTER, "cache_scale is required for an FP8 cache");
+    if ((stages & MLA_STAGE_COMBINE) && (!w_uv || !out))
+        return fail(MLA_ERR_NULL_POINTER, "w_uv and out are required");
+    if (!workspace) return fail(MLA_ERR_NULL_POINTER, "workspace is NULL");
+    const DecodeWs ws = decode_ws(d, batch, q_len, splits);
+    if (workspace_bytes < ws.total)
+        return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu", workspace_bytes, ws.total);
+    const bool mfma = mla::is_v3_shape(d);
+    if (mfma) {
+        const void* ptrs[] = {q_nope, q_pe, w_uk, w_uv, cache_pool, out, workspace};
+        for (const void* p : ptrs)
+            if (p && !aligned16(p)) return fail(MLA_ERR_ALIGNMENT, "tensor at %p is not 16-byte aligned", p);
+        if (cache_scale && ((uintptr_t)cache_scale & 15u))
+            return fail(MLA_ERR_ALIGNMENT, "cache_scale is not 16-byte aligned");
+    } else if (!aligned16(workspace)) {
+        return fail(MLA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+    }
+    mla::DecodeLaunch a;
+    a.H = d.n_heads;
+    a.DC = d.kv_lora_rank;
+    a.DR = d.qk_rope_dim;
+    a.N = d.qk_nope_dim;
+    a.V = d.v_head_dim;
+    a.BS = d.block_size;
+    a.cache_dtype = d.cache_dtype;
+    a.act_dtype = d.act_dtype;
+    a.scale = resolved_scale(d);
+    a.batch = batch;
+    a.q_len = q_len;
+    a.num_splits = splits;
+    a.q_nope = q_nope;
+    a.q_pe = q_pe;
+    a.w_uk = w_uk;
+    a.w_uv = w_uv;
+    a.pool = cache_pool;
+    a.pool_scale = cache_scale;
+    a.block_table = block_table;
+    a.max_blocks = max_blocks_per_seq;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.lse = lse;
+    char* base = static_cast<char*>(workspace);
+    a.qbuf = base + ws.qbuf;
+    a.part_o = reinterpret_cast<float*>(base + ws.part_o);
+    a.part_lse = reinterpret_cast<float*>(base + ws.part_lse);
+    a.stream = static_cast<hipStream_t>(stream);
+    const hipError_t e = mfma ? mla::launch_decode_mfma(a, stages) : mla::launch_decode_generic(a, stages);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+    switch (s) {
+        case MLA_OK: return "MLA_OK";
+        case MLA_ERR_NULL_POINTER: return "MLA_ERR_NULL_POINTER";
+        case MLA_ERR_BAD_SHAPE: return "MLA_ERR_BAD_SHAPE";
+        case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+        case MLA_ERR_ALIGNMENT: return "MLA_ERR_ALIGNMENT";
+        case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+        case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    }
+    return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+size_t mla_cache_row_bytes(const mla_dims* d) {
+    if (check_dims(d) != MLA_OK) return 0;
+    return (size_t)(d->kv_lora_rank + d->qk_rope_dim) * elem_bytes(d->cache_dtype);
+}
+
+size_t mla_cache_block_bytes(const mla_dims* d) {
+    const size_t row = mla_cache_row_bytes(d);
+    return row ? row * (size_t)d->block_size : 0;
+}
+
+mla_status mla_cache_append_workspace_size(const mla_dims* dims, int32_t batch, int32_t n_new,
+                                           int32_t d_model, size_t* bytes) {
+    if (mla_status st = check_dims(dims); st != MLA_OK) return st;
+    if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes is NULL");
+    if (batch < 0 || n_new < 0 || d_model < 1)
+        return fail(MLA_ERR_BAD_SHAPE, "batch=%d n_new=%d d_model=%d", batch, n_new, d_model);
+    const int kc = append_uses_mfma(*dims, d_model) ? append_kc(d_model) : 1;
+    *bytes = align_up((size_t)kc * batch * n_new * (dims->kv_lora_rank + dims->qk_rope_dim) * 4, 256);
+    return ok();
+}
+
+mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t n_new, int32_t d_model,
+                            const void* h, const void* w_kv_a, const void* kv_norm_gamma,
+                            float rms_eps, float rope_base, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, const int32_t* start_pos, void* cache_pool,
+                            float* cache_scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    if (mla_status st = check_dims(dims); st != MLA_OK) return st;
+    const mla_dims& d = *dims;
+    if (batch < 0 || n_new < 0 || d_model < 1 || d_model % 8)
+        return fail(MLA_ERR_BAD_SHAPE, "batch=%d n_new=%d d_model=%d (multiple of 8 required)", batch,
+                    n_new, d_model);
+    if (batch == 0 || n_new == 0) return ok();
+    if (!h || !w_kv_a || !kv_norm_gamma || !block_table || !start_pos || !cache_pool || !workspace)
+        return fail(MLA_ERR_NULL_POINTER, "h, w_kv_a, kv_norm_gamma, block_table, start_pos, "
+                                          "cache_pool and workspace are required");
+    if (d.cache_dtype == MLA_FP8_E4M3 && !cache_scale)
+        return fail(MLA_ERR_NULL_POINTER, "cache_scale is required for an FP8 cache");
+    if (max_blocks_per_seq < 1) return fail(MLA_ERR_BAD_SHAPE, "max_blocks_per_seq must be >= 1");
+    if (!(rms_eps >= 0.f) || !(rope_base > 0.f) || std::isinf(rope_base))
+        return fail(MLA_ERR_BAD_SHAPE, "rms_eps must be >= 0 and rope_base finite and > 0");
+    size_t need = 0;
+    mla_cache_append_workspace_size(dims, batch, n_new, d_model, &need);
+    if (workspace_bytes < need)
+        return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu", workspace_bytes, need);
+    const bool mfma = append_uses_mfma(d, d_model);
+    if (mfma && (!aligned16(h) || !aligned16(w_kv_a)))
+        return fail(MLA_ERR_ALIGNMENT, "h and w_kv_a must be 16-byte aligned");
+    if (!aligned16(workspace)) return fail(MLA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+    mla::AppendLaunch a;
+    a.DC = d.kv_lora_rank;
+    a.DR = d.qk_rope_dim;
+    a.BS = d.block_size;
+    a.cache_dtype = d.cache_dtype;
+    a.act_dtype = d.act_dtype;
+    a.batch = batch;
+    a.n_new = n_new;
+    a.d_model = d_model;
+    a.h = h;
+    a.w_kv_a = w_kv_a;
+    a.gamma = kv_norm_gamma;
+    a.eps = rms_eps;
+    a.rope_base = rope_base;
+    a.block_table = block_table;
+    a.max_blocks = max_blocks_per_seq;
+    a.start_pos = start_pos;
+    a.pool = cache_pool;
+    a.pool_scale = cache_scale;
+    a.part = static_cast<float*>(workspace);
+    a.kc = mfma ? append_kc(d_model) : 1;
+    a.kchunk = mfma ? kAppendChunk : d_model;
+    a.stream = static_cast<hipStream_t>(stream);
+    const hipError_t e = mla::launch_append(a, mfma);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int32_t mla_decode_default_splits(const mla_dims* dims, int32_t batch, int32_t q_len) {
+    (void)dims;
+    return default_splits(batch, q_len);
+}
+
+mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                     int32_t num_splits, size_t* bytes) {
+    if (mla_status st = check_dims(dims); st != MLA_OK) return st;
+    if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes is NULL");
+    if (batch < 0 || q_len < 1 || q_len > 1024)
+        return fail(MLA_ERR_BAD_SHAPE, "batch=%d q_len=%d", batch, q_len);
+    if (num_splits < 0 || num_splits > mla::kMaxSplits)
+        return fail(MLA_ERR_BAD_SHAPE, "num_splits=%d outside [0, %d]", num_splits, mla::kMaxSplits);
+    const int splits = num_splits == 0 ? default_splits(batch, q_len) : num_splits;
+    *bytes = decode_ws(*dims, batch, q_len, splits).total;
+    return ok();
+}
+
+mla_status mla_decode_absorbed(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
+                               const void* q_pe, const void* w_uk, const void* w_uv,
+                               const void* cache_pool, const float* cache_scale,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, int32_t num_splits, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                       block_table, max_blocks_per_seq, seq_lens, num_splits, out, lse, workspace,
+                       workspace_bytes, MLA_STAGE_ALL, stream);
+}
+
+mla_status mla_decode_absorbed_stages(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                      const void* q_nope, const void* q_pe, const void* w_uk,
+                                      const void* w_uv, const void* cache_pool,
+                                      const float* cache_scale, const int32_t* block_table,
+                                      int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                      int32_t num_splits, void* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, uint32_t stages, void* stream) {
+    return decode_impl(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                       block_table, max_blocks_per_seq, seq_lens, num_splits, out, lse, workspace,
+                       workspace_bytes, stages, stream);
+}
+
+}  // extern "C"

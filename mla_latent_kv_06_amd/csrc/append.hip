@@ -1,0 +1,168 @@
+// Latent-cache append: for every new token, x = W_kv,a h (d -> d_c + R), then
+// [RMSNorm(x[0:d_c]) * gamma ; RoPE(x[d_c:], position)] is written into the
+// token's paged slot ("KV Compression -- DeepSeek-V3", "How it works").
+//
+// Two kernels: a split-K projection writing fp32 partial sums to the
+// workspace (MFMA for bf16 activations, fp32 VALU otherwise), then one
+// workgroup per token that adds the partials in a fixed order (so results do
+// not depend on scheduling), normalises, rotates, rounds and stores.
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace mla {
+namespace {
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// One wave per (32 outputs, 32 tokens, K chunk):
+//   part[kc][t][o] = sum_{d in chunk} W[o][d] h[t][d]
+// as x^T = W . h^T with both operands streamed straight from global memory.
+__global__ __launch_bounds__(256) void append_gemm_mfma(const unsigned short* __restrict__ h,
+                                                        const unsigned short* __restrict__ w,
+                                                        int T, int d, int Dout, int kc_count,
+                                                        int kchunk, float* __restrict__ part) {
+    const int lane = threadIdx.x & 63;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int job = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int n_mb = Dout / 32, n_nb = (T + 31) / 32;
+    if (job >= n_mb * n_nb * kc_count) return;
+    const int mb = job % n_mb;
+    const int nb = (job / n_mb) % n_nb;
+    const int kc = job / (n_mb * n_nb);
+    const int o = mb * 32 + l32;
+    const int t = nb * 32 + l32;
+    const int k_lo = kc * kchunk, k_hi = min(d, k_lo + kchunk);
+    const unsigned short* wp = w + (size_t)o * d + hf * 8;
+    const unsigned short* hp = h + (size_t)min(t, T - 1) * d + hf * 8;
+    const bool tok_ok = t < T;
+    f32x16 acc = {};
+    for (int k = k_lo; k < k_hi; k += 16) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(wp + k);
+        bf16x8 b = *reinterpret_cast<const bf16x8*>(hp + k);
+        if (!tok_ok) b = bf16x8{};
+        acc = mfma32(a, b, acc);
+    }
+    if (tok_ok) {
+        float* dst = part + ((size_t)kc * T + t) * Dout + mb * 32 + 4 * hf;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            f32x4 v = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+            *reinterpret_cast<f32x4*>(dst + 8 * g) = v;
+        }
+    }
+}
+
+// grid: ceil(T * Dout / 256); one thread per (token, output), whole K.
+template <int ADT>
+__global__ __launch_bounds__(256) void append_gemm_generic(const void* __restrict__ h,
+                                                           const void* __restrict__ w, int T, int d,
+                                                           int Dout, float* __restrict__ part) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long long)T * Dout) return;
+    const int t = (int)(i / Dout), o = (int)(i % Dout);
+    float acc = 0.f;
+    for (int k = 0; k < d; ++k)
+        acc += load_act<ADT>(w, (size_t)o * d + k) * load_act<ADT>(h, (size_t)t * d + k);
+    part[i] = acc;
+}
+
+// grid: T tokens, 256 threads.
+template <int ADT, int CDT>
+__global__ __launch_bounds__(256) void append_finalize(
+    const float* __restrict__ part, int kc_count, int T, int DC, int DR,
+    const void* __restrict__ gamma, float eps, float rope_base,
+    const int* __restrict__ block_table, int max_blocks, const int* __restrict__ start_pos,
+    int n_new, int BSZ, void* __restrict__ pool, float* __restrict__ pool_scale) {
+    __shared__ float y[2048];
+    __shared__ float red[16];
+    const int t = blockIdx.x;
+    const int Dout = DC + DR;
+    float ss = 0.f;
+    for (int o = threadIdx.x; o < Dout; o += 256) {
+        float x = 0.f;
+        for (int kc = 0; kc < kc_count; ++kc) x += part[((size_t)kc * T + t) * Dout + o];
+        y[o] = x;
+        if (o < DC) ss += x * x;
+    }
+    ss = block_sum(ss, red);                      // also publishes y[]
+    const float inv = 1.0f / sqrtf(ss / (float)DC + eps);
+    const int b = t / n_new;
+    const int pos = start_pos[b] + (t - b * n_new);
+    // RoPE pairs (x[2k], x[2k+1]); angle pos * base^(-2k/R) in double
+    float yo[8];
+    int cnt = 0;
+    for (int o = threadIdx.x; o < Dout; o += 256, ++cnt) {
+        float v;
+        if (o < DC) {
+            v = y[o] * inv * load_act<ADT>(gamma, o);
+        } else {
+            const int k = (o - DC) >> 1;
+            const double ang = (double)pos * pow((double)rope_base, -2.0 * k / (double)DR);
+            double sn, cs;
+            sincos(ang, &sn, &cs);
+            const double x0 = y[DC + 2 * k], x1 = y[DC + 2 * k + 1];
+            v = (float)(((o - DC) & 1) ? x0 * sn + x1 * cs : x0 * cs - x1 * sn);
+        }
+        yo[cnt] = v;
+    }
+    const size_t phys = (size_t)block_table[(size_t)b * max_blocks + pos / BSZ] * BSZ + pos % BSZ;
+    if constexpr (CDT == MLA_FP8_E4M3) {
+        float amax = 0.f;
+        cnt = 0;
+        for (int o = threadIdx.x; o < Dout; o += 256, ++cnt) amax = fmaxf(amax, fabsf(yo[cnt]));
+        amax = block_max(amax, red);
+        const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+        unsigned char* dst = static_cast<unsigned char*>(pool) + phys * Dout;
+        cnt = 0;
+        for (int o = threadIdx.x; o < Dout; o += 256, ++cnt)
+            dst[o] = static_cast<unsigned char>(f32_to_e4m3_rne_sat(yo[cnt] / sc));
+        if (threadIdx.x == 0) pool_scale[phys] = sc;
+    } else {
+        cnt = 0;
+        for (int o = threadIdx.x; o < Dout; o += 256, ++cnt) store_act<CDT>(pool, phys * Dout + o, yo[cnt]);
+    }
+}
+
+template <int ADT, int CDT>
+hipError_t finalize(const AppendLaunch& a) {
+    const int T = a.batch * a.n_new;
+    append_finalize<ADT, CDT><<<T, 256, 0, a.stream>>>(
+        a.part, a.kc, T, a.DC, a.DR, a.gamma, a.eps, a.rope_base, a.block_table, a.max_blocks,
+        a.start_pos, a.n_new, a.BS, a.pool, a.pool_scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendLaunch& a, bool mfma_gemm) {
+    const int T = a.batch * a.n_new;
+    if (T == 0) return hipSuccess;
+    const int Dout = a.DC + a.DR;
+    if (mfma_gemm) {
+        const int jobs = (Dout / 32) * ((T + 31) / 32) * a.kc;
+        append_gemm_mfma<<<(jobs + 3) / 4, 256, 0, a.stream>>>(
+            static_cast<const unsigned short*>(a.h), static_cast<const unsigned short*>(a.w_kv_a), T,
+            a.d_model, Dout, a.kc, a.kchunk, a.part);
+    } else {
+        const long long n = (long long)T * Dout;
+        const unsigned grid = (unsigned)((n + 255) / 256);
+        if (a.act_dtype == MLA_BF16)
+            append_gemm_generic<MLA_BF16><<<grid, 256, 0, a.stream>>>(a.h, a.w_kv_a, T, a.d_model, Dout, a.part);
+        else
+            append_gemm_generic<MLA_F32><<<grid, 256, 0, a.stream>>>(a.h, a.w_kv_a, T, a.d_model, Dout, a.part);
+    }
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if (a.act_dtype == MLA_BF16) {
+        if (a.cache_dtype == MLA_BF16) return finalize<MLA_BF16, MLA_BF16>(a);
+        if (a.cache_dtype == MLA_FP8_E4M3) return finalize<MLA_BF16, MLA_FP8_E4M3>(a);
+        return finalize<MLA_BF16, MLA_F32>(a);
+    }
+    if (a.cache_dtype == MLA_BF16) return finalize<MLA_F32, MLA_BF16>(a);
+    if (a.cache_dtype == MLA_FP8_E4M3) return finalize<MLA_F32, MLA_FP8_E4M3>(a);
+    return finalize<MLA_F32, MLA_F32>(a);
+}
+
+}  // namespace mla

@@ -1,0 +1,67 @@
+// Host-side launch interface between the C ABI layer (api.hip) and the
+// kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+namespace mla {
+
+// MI355X compute units; the default split count aims to give every CU work.
+constexpr int kNumCUs = 256;
+constexpr int kMaxSplits = 256;
+
+struct DecodeLaunch {
+    // shape
+    int H, DC, DR, N, V, BS;
+    int cache_dtype, act_dtype;
+    float scale;                 // softmax scale (natural units)
+    int batch, q_len, num_splits;
+    // tensors
+    const void* q_nope;
+    const void* q_pe;
+    const void* w_uk;
+    const void* w_uv;
+    const void* pool;
+    const float* pool_scale;
+    const int32_t* block_table;
+    int max_blocks;
+    const int32_t* seq_lens;
+    void* out;
+    float* lse;
+    // workspace carve-up
+    void* qbuf;                  // [R][H][DC+DR]: bf16 (MFMA path) or f32 (portable)
+    float* part_o;               // [R][S][H][DC]
+    float* part_lse;             // [R][S][H]
+    hipStream_t stream;
+};
+
+struct AppendLaunch {
+    int DC, DR, BS;
+    int cache_dtype, act_dtype;
+    int batch, n_new, d_model;
+    const void* h;
+    const void* w_kv_a;
+    const void* gamma;
+    float eps, rope_base;
+    const int32_t* block_table;
+    int max_blocks;
+    const int32_t* start_pos;
+    void* pool;
+    float* pool_scale;
+    float* part;                 // [KC][T][DC+DR] f32
+    int kc;                      // K chunks in `part`
+    int kchunk;                  // d_model columns per chunk
+    hipStream_t stream;
+};
+
+bool is_v3_shape(const mla_dims& d);
+
+hipError_t launch_decode_mfma(const DecodeLaunch& a, unsigned stages);
+hipError_t launch_decode_generic(const DecodeLaunch& a, unsigned stages);
+hipError_t launch_append(const AppendLaunch& a, bool mfma_gemm);
+
+}  // namespace mla

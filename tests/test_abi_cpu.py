@@ -1,0 +1,130 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and its host-only functions (sizes, workspace queries, argument
+validation) behave as documented.  No kernel is launched."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from oracle import sizes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+LIB = os.path.join(ROOT, "mla_latent_kv_06_amd", "libmla.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmla.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+
+
+@pytest.fixture(scope="module")
+def b():
+    from mla_latent_kv_06_amd import binding
+    return binding
+
+
+def test_binding_mirrors_header(b):
+    assert sorted(b.EXPORTED) == _declared_functions()
+
+
+def v3_dims(b, cache="bf16"):
+    return b.Dims.make(128, 512, 64, 128, 128, 64, cache, "bf16")
+
+
+def test_row_and_block_bytes_match_closed_forms(b):
+    for cache, elem in (("bf16", 2), ("fp8", 1), ("f32", 4)):
+        d = v3_dims(b, cache)
+        assert b.cache_row_bytes(d) == sizes.mla_elems_per_token_layer(512, 64) * elem
+        assert b.cache_block_bytes(d) == sizes.pool_bytes(1, 64, 512, 64, elem)
+    # 61 layers of bf16 rows: the 70.3 KB per token of the V3 shape
+    assert 61 * b.cache_row_bytes(v3_dims(b)) == sizes.mla_bytes_per_token(61, 512, 64, 2)
+
+
+def test_status_strings(b):
+    assert b.status_string(0) == "MLA_OK"
+    assert b.status_string(5) == "MLA_ERR_WORKSPACE_TOO_SMALL"
+    assert b.status_string(99) == "MLA_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(b):
+    d = v3_dims(b)
+    assert b.default_splits(d, 64, 1) == 4
+    assert b.default_splits(d, 1, 1) == 64
+    assert b.default_splits(d, 128, 2) == 1
+    n1 = b.decode_workspace_size(d, 64, 1, 4)
+    n2 = b.decode_workspace_size(d, 64, 1, 8)
+    assert n2 > n1 > 64 * 4 * 128 * 512 * 4
+    assert b.decode_workspace_size(d, 64, 1, 0) == n1
+    assert b.append_workspace_size(d, 64, 1, 7168) >= 14 * 64 * 576 * 4
+
+
+def _call_decode(b, dims, **kw):
+    args = dict(batch=2, q_len=1, q_nope=16, q_pe=16, w_uk=16, w_uv=16, pool=16, scale=None,
+                bt=16, max_blocks=4, seq_lens=16, splits=0, out=16, lse=None, ws=16,
+                ws_bytes=1 << 40, stages=7)
+    args.update(kw)
+    P = lambda v: None if v is None else ctypes.c_void_p(v)
+    return b.lib().mla_decode_absorbed_stages(
+        ctypes.byref(dims), args["batch"], args["q_len"], P(args["q_nope"]), P(args["q_pe"]),
+        P(args["w_uk"]), P(args["w_uv"]), P(args["pool"]), P(args["scale"]), P(args["bt"]),
+        args["max_blocks"], P(args["seq_lens"]), args["splits"], P(args["out"]), P(args["lse"]),
+        P(args["ws"]), args["ws_bytes"], args["stages"], None)
+
+
+def test_decode_validation_rejects_before_launch(b):
+    d = v3_dims(b)
+    assert _call_decode(b, d, q_nope=None) == 1                  # NULL_POINTER
+    assert _call_decode(b, d, q_len=0) == 2                      # BAD_SHAPE
+    assert _call_decode(b, d, splits=257) == 2
+    assert _call_decode(b, d, stages=8) == 2
+    assert _call_decode(b, d, ws_bytes=10) == 5                  # WORKSPACE_TOO_SMALL
+    assert _call_decode(b, d, q_nope=18) == 4                    # ALIGNMENT (MFMA path)
+    assert _call_decode(b, v3_dims(b, "fp8")) == 1               # fp8 needs cache_scale
+    bad = b.Dims.make(0, 512, 64, 128, 128, 64)
+    assert _call_decode(b, bad) == 2
+    bad = b.Dims.make(128, 512, 63, 128, 128, 64)
+    assert _call_decode(b, bad) == 2                             # odd rope width
+    bad = b.Dims.make(128, 512, 64, 128, 128, 64, "bf16", "fp8")
+    assert _call_decode(b, bad) == 3                             # UNSUPPORTED act dtype
+    assert "act_dtype" in b.lib().mla_last_error().decode()
+    assert _call_decode(b, d, batch=0) == 0                      # nothing to do
+
+
+def test_append_validation_rejects_before_launch(b):
+    d = v3_dims(b)
+    lib = b.lib()
+    P = ctypes.c_void_p
+    def call(**kw):
+        a = dict(batch=2, n_new=1, d_model=7168, h=16, w=16, g=16, bt=16, sp=16, pool=16,
+                 scale=None, ws=16, ws_bytes=1 << 40, eps=1e-6, base=10000.0)
+        a.update(kw)
+        pp = lambda v: None if v is None else P(v)
+        return lib.mla_cache_append(ctypes.byref(d), a["batch"], a["n_new"], a["d_model"],
+                                    pp(a["h"]), pp(a["w"]), pp(a["g"]), a["eps"], a["base"],
+                                    pp(a["bt"]), 4, pp(a["sp"]), pp(a["pool"]), pp(a["scale"]),
+                                    pp(a["ws"]), a["ws_bytes"], None)
+    assert call(h=None) == 1
+    assert call(d_model=7) == 2
+    assert call(ws_bytes=8) == 5
+    assert call(base=-1.0) == 2
+    assert call(h=24) == 4
+    assert call(n_new=0) == 0
