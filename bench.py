@@ -1,0 +1,254 @@
+"""Benchmark: absorbed-MLA decode tokens/s + latent-cache HBM GB/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--layers NL] [--splits S] [--no-cpu-baseline] [--report FILE]
+
+One step = the whole hot path for one layer over one batch: the cache append
+of one new token per sequence (wkv_a projection, RMSNorm, RoPE, paged write)
+followed by the absorbed decode (q absorption, split-KV attention over the
+paged latent cache, log-sum-exp combine, W_UV).  Steps rotate over NL
+independent layer copies (own pool, weights, queries) so the working set is
+far larger than the 256 MB last-level cache; inputs are resident in HBM before
+timing starts.  Prints ONE JSON line on stdout; details go to stderr.
+
+Default workload: DeepSeek-V3 head shape (128 heads, latent 512, rotary 64),
+bf16, batch 64, every sequence 8192 tokens after the append, paged blocks of 64
+with a randomly permuted block table.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak) at bs64, ctx 8k"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="v3_b64_ctx8k_paged_bf16")
+    p.add_argument("--layers", type=int, default=8)
+    p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seqs", type=int, default=2)
+    p.add_argument("--report", default=None)
+    return p.parse_args()
+
+
+class Layer:
+    """One layer's device tensors."""
+
+    def __init__(self, wl, li, dims, dev, torch, synth, b):
+        seed = 1000 + li
+        B, H = wl.batch, wl.n_heads
+        bf = torch.bfloat16
+
+        def up(x):
+            return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(bf)
+
+        self.q_nope = up(synth.q_nope(wl, seed))
+        self.q_pe = up(synth.q_pe(wl, seed))
+        self.w_uk = up(synth.w_uk(wl, seed))
+        self.w_uv = up(synth.w_uv(wl, seed))
+        self.w_kv_a = up(synth.w_kv_a(wl, seed))
+        self.gamma = torch.ones(wl.kv_lora_rank, dtype=bf, device=dev)
+        self.h = up(synth.hidden(wl, seed=seed))
+        cached = synth.cached_lengths(wl, seed)
+        seq_lens = (cached + wl.q_len).astype(np.int32)
+        table, nblk = synth.block_tables(seq_lens, wl.block_size, wl.paged, seed)
+        self.seq_lens_host = seq_lens
+        self.table_host = table
+        self.block_table = torch.from_numpy(table).to(dev)
+        self.seq_lens = torch.from_numpy(seq_lens).to(dev)
+        self.start_pos = torch.from_numpy(cached.astype(np.int32)).to(dev)
+        # cache rows: N(0,1) bf16 drawn on the device (unit RMS in expectation);
+        # decode time does not depend on the values
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        self.pool = torch.empty((nblk, wl.block_size, wl.row_width), dtype=bf, device=dev)
+        flat = self.pool.view(-1, wl.row_width)
+        step = 1 << 16
+        for i in range(0, flat.shape[0], step):
+            flat[i:i + step] = torch.randn(flat[i:i + step].shape, generator=g, device=dev,
+                                           dtype=torch.float32).to(bf)
+        self.scale = None
+        self.out = torch.empty((B, wl.q_len, H, wl.v_head_dim), dtype=bf, device=dev)
+        self.lse = torch.empty((B, wl.q_len, H), dtype=torch.float32, device=dev)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mla_latent_kv_06_amd import synth
+    from mla_latent_kv_06_amd import binding as b
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[args.workload]
+    if wl.cache_dtype != "bf16" or wl.act_dtype != "bf16":
+        raise SystemExit("bench.py times bf16 workloads")
+    dims = b.Dims.from_workload(wl)
+    B, Sq, H = wl.batch, wl.q_len, wl.n_heads
+    splits = args.splits or b.default_splits(dims, B, Sq)
+
+    t_setup = time.time()
+    layers = [Layer(wl, li, dims, dev, torch, synth, b) for li in range(args.layers)]
+    ws_dec = torch.empty(b.decode_workspace_size(dims, B, Sq, splits), dtype=torch.uint8, device=dev)
+    ws_app = torch.empty(max(1, b.append_workspace_size(dims, B, Sq, wl.d_model)),
+                         dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s: {args.layers} layers, "
+        f"pool {layers[0].pool.numel() * 2 / 1e6:.1f} MB each, splits {splits}")
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(L, ev=None):
+        b.append(dims, L.h, L.w_kv_a, L.gamma, L.block_table, L.start_pos, L.pool, None,
+                 rms_eps=1e-6, rope_base=10000.0, workspace=ws_app)
+        common = (dims, L.q_nope, L.q_pe, L.w_uk, L.w_uv, L.pool, None, L.block_table, L.seq_lens)
+        b.decode(*common, num_splits=splits, out=L.out, lse=L.lse, workspace=ws_dec,
+                 stages=b.STAGE_ABSORB_Q)
+        if ev is not None:
+            ev[0].record(stream)
+        b.decode(*common, num_splits=splits, out=L.out, lse=L.lse, workspace=ws_dec,
+                 stages=b.STAGE_SPLIT_KV)
+        if ev is not None:
+            ev[1].record(stream)
+        b.decode(*common, num_splits=splits, out=L.out, lse=L.lse, workspace=ws_dec,
+                 stages=b.STAGE_COMBINE)
+
+    for i in range(args.warmup):
+        step(layers[i % len(layers)])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(K):
+        step(layers[i % len(layers)], evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / K
+    k_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    k_avg_s = float(k_ms.mean()) / 1e3
+
+    tokens_per_step = B * Sq
+    value = tokens_per_step / (ms_step / 1e3)
+    # algorithmic work of the split-KV kernel: every visible cache token's
+    # 576-element row is read once; 2*H*(576+512) flops per token and query row
+    seq_lens = layers[0].seq_lens_host.astype(np.int64)
+    cache_bytes = int(seq_lens.sum()) * wl.row_width * 2
+    flops = sum(int(L - Sq + s + 1) for L in seq_lens for s in range(Sq)) * 2 * H * (wl.row_width + wl.kv_lora_rank)
+    achieved = cache_bytes / k_avg_s / 1e9
+    step_gbs = cache_bytes / (ms_step / 1e3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us  ({value:.4g} tok/s)  split-KV kernel {k_avg_s * 1e6:.1f} us "
+        f"(p10 {np.percentile(k_ms, 10) * 1e3:.1f} / p90 {np.percentile(k_ms, 90) * 1e3:.1f})")
+    log(f"cache {cache_bytes / 1e6:.1f} MB: kernel {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s), "
+        f"step {step_gbs:.0f} GB/s; kernel {flops / k_avg_s / 1e12:.0f} TFLOP/s "
+        f"({flops / k_avg_s / 1e12 / BF16_PEAK_TFLOPS:.1%} of bf16 MFMA peak)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": B, "ctx": int(seq_lens.max()), "q_len": Sq,
+            "heads": H, "kv_lora_rank": wl.kv_lora_rank, "rope_dim": wl.qk_rope_dim,
+            "block_size": wl.block_size, "paged": wl.paged, "num_splits": splits,
+            "layers_rotated": args.layers,
+            "step": "cache append of 1 token/seq + absorbed decode, one layer",
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "split_kv_kernel<bf16>",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes": cache_bytes,
+            "avg_launch_us": round(k_avg_s * 1e6, 2),
+            "mfma_tflops": round(flops / k_avg_s / 1e12, 1),
+            "mfma_frac": round(flops / k_avg_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, wl, layers[0], torch)
+
+    print(json.dumps(result), flush=True)
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump(result, f, indent=1)
+
+
+def cpu_baseline(args, wl, L, torch):
+    """The CPU oracle (naive float64 decode) on a bounded sample of the same
+    workload: the first --cpu-seqs sequences of layer 0, all heads, read back
+    from the device.  Also checks the GPU output for those sequences."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    n = min(args.cpu_seqs, wl.batch)
+    D = wl.row_width
+    torch.cuda.synchronize()
+
+    def f64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    pool_rows = f64(L.pool.view(-1, D))
+    rows = [oracle.gather_sequence(pool_rows, L.table_host[i], int(L.seq_lens_host[i]), wl.block_size)
+            for i in range(n)]
+    qn, qp = f64(L.q_nope[:n]), f64(L.q_pe[:n])
+    wuk, wuv = f64(L.w_uk), f64(L.w_uv)
+    t = time.time()
+    ref, _ = oracle.decode_naive(qn, qp, wuk, wuv, rows, wl.q_len)
+    dt = time.time() - t
+    got = f64(L.out[:n])
+    err = float(np.max(np.abs(got - ref)))
+    log(f"cpu oracle: {n} sequences in {dt:.1f}s on {threads} threads; GPU vs oracle max-abs {err:.2e}")
+    return {"value": round(n * wl.q_len / dt, 4), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} of {wl.batch} sequences (ctx {int(L.seq_lens_host[0])}, all "
+                      f"{wl.n_heads} heads), naive float64 decode, {dt:.1f}s",
+            "gpu_vs_oracle_max_abs": err}
+
+
+if __name__ == "__main__":
+    main()

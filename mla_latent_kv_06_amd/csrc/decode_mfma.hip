@@ -377,7 +377,9 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                     continue;
                 }
                 if (mode == 0 && t == t0 && hb == 0) m_ref = hmax;
-                if (mode == 0 && hmax > m_ref + kMaxLead) abort_flag[t & 1] = 1;
+                // (cannot fire in the exact-reference pass: the scan saw the
+                // same maxima, so at most three passes run)
+                if (hmax > m_ref + kMaxLead) abort_flag[t & 1] = 1;
 
                 float psum = 0.f;
                 bf16x8 pf[2];
