@@ -30,10 +30,38 @@ import numpy as np
 METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak) at bs64, ctx 8k"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("decode_mfma.hip", "common.hpp", "internal.hpp")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "split_kv_kernel_v3_b64_ctx8k_bf16_hbm_traffic.txt")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    """First 16 hex digits of sha256 over the split-KV kernel's source files."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mla_latent_kv_06_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload):
+    """HBM bytes per split-KV launch from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, copy-calibrated), or None when that summary
+    was taken on other kernel sources or another workload."""
+    import re
+    if workload != "v3_b64_ctx8k_paged_bf16" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    d = re.search(r"first 16 hex\):\s*([0-9a-f]{16})", text)
+    t = re.search(r"total HBM traffic per launch\s*=\s*([0-9,]+) B", text)
+    if not d or not t or d.group(1) != kernel_source_digest():
+        return None
+    return int(t.group(1).replace(",", ""))
 
 
 def parse():
@@ -45,8 +73,11 @@ def parse():
     p.add_argument("--layers", type=int, default=8)
     p.add_argument("--splits", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seqs", type=int, default=2)
+    p.add_argument("--cpu-seqs", type=int, default=32)
     p.add_argument("--report", default=None)
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="instead: copy a buffer of this many bytes 5 times (calibrates "
+                        "hardware byte counters against a kernel of known traffic)")
     return p.parse_args()
 
 
@@ -103,6 +134,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_bytes:
+        n = args.copy_bytes // 16 * 16
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 5 times")
+        return
     wl = synth.WORKLOADS[args.workload]
     if wl.cache_dtype != "bf16" or wl.act_dtype != "bf16":
         raise SystemExit("bench.py times bf16 workloads")
@@ -197,7 +237,8 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "split_kv_kernel<bf16>",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": profiled_traffic(wl.name), "traffic_unit": "bytes per launch",
             "algorithmic_bytes": cache_bytes,
             "avg_launch_us": round(k_avg_s * 1e6, 2),
             "mfma_tflops": round(flops / k_avg_s / 1e12, 1),

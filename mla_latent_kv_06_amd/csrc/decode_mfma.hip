@@ -42,15 +42,18 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // LDS tile layout.  Chunk c (8 bf16 channels) of token row t lives at chunk
-// position  P(t, c) = (c >> 3) * 512 + t * 8 + ((c & 7) ^ f(t)),
-// f(t) = ((t & 3) << 1) | ((t >> 2) & 1): groups of 8 chunks are stored row
-// by row, the chunk slot XOR-permuted per row.  Then
-//  - 8 consecutive rows reading one chunk (the 16-byte score-operand reads)
-//    hit 8 different slots, i.e. disjoint banks;
-//  - 4 consecutive rows x 2 adjacent chunks (the transposed 8-byte value
-//    reads of one 16-lane group) hit 8 different slots;
-//  - every global->LDS instruction copies 8 rows x 128 contiguous bytes.
-__device__ __forceinline__ int fswz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// position  P(t, c) = (c >> 3) * 512 + t * 8 + ((c & 7) ^ g(t)):  groups of 8
+// chunks are stored row by row, the chunk slot XOR-permuted per row by
+//   g(t) = f(t & 7) ^ (2 * bit3(t)),  f(u) = ((u & 3) << 1) | ((u >> 2) & 1).
+// With either 32 or 64 LDS banks this keeps
+//  - 16 consecutive rows reading one chunk (the 16-byte score-operand reads)
+//    on disjoint banks, and
+//  - 4 consecutive rows x 2 adjacent chunks (the 8-byte transposed value reads
+//    of one 16-lane group) on disjoint banks,
+// while every global->LDS instruction still copies 8 rows x 128 contiguous bytes.
+__device__ __forceinline__ int fswz(int t) {
+    return (((t & 3) << 1) | ((t >> 2) & 1)) ^ ((t >> 2) & 2);
+}
 __device__ __forceinline__ int tpos(int t, int c) {
     return ((c >> 3) << 9) + (t << 3) + ((c & 7) ^ fswz(t));
 }
@@ -154,37 +157,43 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
 // 2. split-KV attention over the latent cache
 // ---------------------------------------------------------------------------
 
+// LDS-typed byte pointer.  Tile helpers take these so that the compiler's
+// alias analysis can tell the tile being read from the one being filled.
+typedef MLA_LDS unsigned char lds_u8;
+
 // Issue the asynchronous copy of one bf16 cache block (64 rows x 1152 B,
 // contiguous in memory) into an LDS tile.  Instruction i = 8 cg + q fills
 // positions 64 i .. 64 i + 63: rows 8q .. 8q+7, chunk group cg.  Lane l takes
-// row 8q + l/8 and slot l%8, i.e. chunk 8 cg + ((l%8) ^ f(l/8)).
+// row 8q + l/8 and slot l%8, i.e. chunk 8 cg + ((l%8) ^ g(8q + l/8)).
 __device__ __forceinline__ void issue_tile_bf16(const unsigned char* __restrict__ gtile,
-                                                unsigned char* ltile, int w, int lane) {
-    const unsigned lane_off = (lane >> 3) * ROWB + (((lane & 7) ^ fswz(lane >> 3)) << 4);
+                                                lds_u8* ltile, int w, int lane) {
+    // row 8q + l/8 has g = f(l/8) ^ 2 (q & 1): two per-lane offsets
+    const unsigned off0 = (lane >> 3) * ROWB + (((lane & 7) ^ fswz(lane >> 3)) << 4);
+    const unsigned off1 = (lane >> 3) * ROWB + (((lane & 7) ^ fswz((lane >> 3) + 8)) << 4);
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(gtile, GTILE);
 #pragma unroll
     for (int k = 0; k < 18; ++k) {
         const int i = w * 18 + k;                      // wave-uniform
         const int cg = i >> 3, q = i & 7;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(ltile + i * 1024), 16,
-                                                 lane_off, q * 8 * ROWB + cg * 128, 0, 0);
+                                                 (q & 1) ? off1 : off0, q * 8 * ROWB + cg * 128,
+                                                 0, 0);
     }
 }
 
 // Zero rows valid .. 63 of an LDS tile (their cache slots hold no token).
-__device__ __forceinline__ void zero_rows(unsigned char* ltile, int valid, int tid) {
+__device__ __forceinline__ void zero_rows(lds_u8* ltile, int valid, int tid) {
     for (int p = valid * NCH + tid; p < BS * NCH; p += 256) {
         const int t = p / NCH, c = p - t * NCH;
-        *reinterpret_cast<u32x4*>(ltile + tpos(t, c) * 16) = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<MLA_LDS u32x4*>(ltile + tpos(t, c) * 16) = u32x4{0, 0, 0, 0};
     }
 }
 
 // Asynchronous copy of one fp8 cache block (64 rows x 576 B, contiguous) into
-// row-major LDS staging, plus its 64 per-token scales.
+// row-major LDS staging, plus its 64 per-token scales after it.
 __device__ __forceinline__ void issue_tile_fp8(const unsigned char* __restrict__ gtile,
                                                const float* __restrict__ gscale,
-                                               unsigned char* lstage, float* lscale,
-                                               int w, int lane) {
+                                               lds_u8* lstage, int w, int lane) {
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(gtile, F8TILE);
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
@@ -192,22 +201,26 @@ __device__ __forceinline__ void issue_tile_fp8(const unsigned char* __restrict__
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(lstage + i * 1024), 16,
                                                  lane * 16, i * 1024, 0, 0);
     }
-    if (w == 0 && lane < 16)
-        __builtin_amdgcn_global_load_lds((const void*)(gscale + lane * 4), (MLA_LDS void*)lscale,
-                                         16, 0, 0);
+    if (w == 0) {
+        const __amdgpu_buffer_rsrc_t srs = make_rsrc(gscale, BS * 4);
+        if (lane < 16)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (MLA_LDS void*)(lstage + F8TILE), 16,
+                                                     lane * 16, 0, 0, 0);
+    }
 }
 
-// fp8 staging -> dequantised bf16 swizzled tile (value * token scale, RNE).
-// Rows at or beyond `valid` become zeros.
-__device__ __forceinline__ void convert_tile_fp8(const unsigned char* lstage, const float* lscale,
-                                                 unsigned char* ltile, int tid, int valid) {
+// fp8 staging (+ scales) -> dequantised bf16 swizzled tile (value * token
+// scale, RNE).  Rows at or beyond `valid` become zeros.
+__device__ __forceinline__ void convert_tile_fp8(const lds_u8* lstage, lds_u8* ltile, int tid,
+                                                 int valid) {
+    const MLA_LDS float* lscale = reinterpret_cast<const MLA_LDS float*>(lstage + F8TILE);
 #pragma unroll 1
     for (int k = 0; k < 9; ++k) {
         const int p = k * 256 + tid;                   // 2304 fp8 chunks
         const int t = p / F8CHUNKS, c = p - t * F8CHUNKS;
         u32x4 outw[2];
         if (t < valid) {
-            const u32x4 raw = *reinterpret_cast<const u32x4*>(lstage + p * 16);
+            const u32x4 raw = *reinterpret_cast<const MLA_LDS u32x4*>(lstage + p * 16);
             const float sc = lscale[t];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -222,17 +235,19 @@ __device__ __forceinline__ void convert_tile_fp8(const unsigned char* lstage, co
             outw[0] = u32x4{0, 0, 0, 0};
             outw[1] = u32x4{0, 0, 0, 0};
         }
-        *reinterpret_cast<u32x4*>(ltile + tpos(t, 2 * c) * 16) = outw[0];
-        *reinterpret_cast<u32x4*>(ltile + tpos(t, 2 * c + 1) * 16) = outw[1];
+        *reinterpret_cast<MLA_LDS u32x4*>(ltile + tpos(t, 2 * c) * 16) = outw[0];
+        *reinterpret_cast<MLA_LDS u32x4*>(ltile + tpos(t, 2 * c + 1) * 16) = outw[1];
     }
 }
 
 // Workgroup (row, split): row = b * q_len + s handles query token s of
 // sequence b for all 128 heads over cache tiles [t0, t1) of its visible range.
-// Wave w owns heads 32w .. 32w+31 for the whole tile loop:
-//   S^T (64 tokens x 32 heads) = K_tile (64 x 576) . Q_w^T   [2 x 36 MFMA]
-//   O^T (512 cols x 32 heads) += V^T (512 x 64) . P^T        [16 x 4 MFMA]
-// so softmax statistics and rescaling stay inside the wave.
+// Wave w owns heads 32w .. 32w+31 for the whole tile loop; each 64-token tile
+// is processed as two halves of 32 tokens:
+//   S^T (32 tokens x 32 heads) = K_half (32 x 576) . Q_w^T   [36 MFMA]
+//   O^T (512 cols x 32 heads) += V^T (512 x 32) . P^T         [32 MFMA]
+// so softmax statistics stay inside the wave.  Q_w stays in VGPRs (its rotary
+// part in LDS on the bf16 path) and O^T in AGPRs for the whole loop.
 template <bool FP8>
 __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const unsigned short* __restrict__ qbuf,      // [R][H][576] bf16
@@ -242,8 +257,15 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const int* __restrict__ seq_lens, int q_len, int num_splits, float scale_log2,
     float* __restrict__ part_o,                   // [R][S][H][512]
     float* __restrict__ part_lse) {               // [R][S][H]
-    constexpr int LDS_BYTES = (FP8 ? (TILE + 2 * F8TILE + 2 * 256) : (2 * TILE)) + 16;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+    // bf16: two tiles + the rotary queries of all heads (16 KB) = 160 KiB;
+    // fp8: one bf16 tile + two fp8 staging tiles with scales (rotary queries in VGPRs)
+    constexpr bool QPE_LDS = !FP8;
+    constexpr int QPE_BYTES = H * DR * 2;
+    constexpr int STAGE = F8TILE + 256;           // fp8 staging buffer: codes + scales
+    constexpr int LDS_BYTES = FP8 ? (TILE + 2 * STAGE) : (2 * TILE + QPE_BYTES);
+    constexpr int NQ = QPE_LDS ? 32 : 36;          // query K-steps kept in VGPRs
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[LDS_BYTES];
+    lds_u8* smem = (lds_u8*)smem_raw;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in an SGPR
@@ -264,171 +286,208 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const int* btab = block_table + (size_t)b * max_blocks;
     const int head = w * 32 + l32;
 
+    // bf16: tiles at 0 and TILE, rotary queries at 2 TILE.
+    // fp8: the bf16 tile at 0, staging buffers at TILE and TILE + STAGE.
+    lds_u8* qpe = smem + 2 * TILE;
+
     // this wave's 32 query rows, as MFMA B fragments: lane (hf, l32) holds
     // channels 16 ks + 8 hf .. +8 of head 32 w + l32
-    bf16x8 qf[36];
+    bf16x8 qf[NQ];
     {
         const unsigned short* qrow = qbuf + ((size_t)row * H + head) * D + hf * 8;
 #pragma unroll
-        for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+        for (int ks = 0; ks < NQ; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
     }
-
-    unsigned char* tiles = smem;                       // bf16 tile(s)
-    unsigned char* stage = smem + TILE;                // fp8 staging (FP8 only)
-    float* sscale = reinterpret_cast<float*>(smem + TILE + 2 * F8TILE);
+    if constexpr (QPE_LDS) {
+        // q_pe of all heads: head h's chunk c (8 channels) at h*128 + ((c ^ g(h)) << 4)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = k * 256 + tid;               // 1024 chunks
+            const int h = i >> 3, c = i & 7;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(qbuf + ((size_t)row * H + h) * D + DC + c * 8);
+            *reinterpret_cast<MLA_LDS u32x4*>(qpe + h * 128 + ((c ^ fswz(h & 15)) << 4)) = v;
+        }
+    }
+    const lds_u8* qpe_lane = qpe + head * 128;
+    const int qpe_g = fswz(head & 15);
 
     auto valid_of = [&](int t) { return min(BS, n_vis - t * BS); };
-    auto issue = [&](int t, int buf) {
+    // asynchronous load of tile t into `dst` (a bf16 tile, or fp8 staging)
+    auto issue = [&](int t, lds_u8* dst) {
         const size_t blk = (size_t)btab[t];
         if constexpr (FP8) {
-            issue_tile_fp8(pool + blk * F8TILE, pool_scale + blk * BS, stage + buf * F8TILE,
-                           sscale + buf * 64, w, lane);
+            issue_tile_fp8(pool + blk * F8TILE, pool_scale + blk * BS, dst, w, lane);
         } else {
-            issue_tile_bf16(pool + blk * GTILE, tiles + buf * TILE, w, lane);
+            issue_tile_bf16(pool + blk * GTILE, dst, w, lane);
         }
     };
 
-    // Softmax without rescaling the accumulators: every weight of a pass is
-    // exp2(s - m_ref) for one reference m_ref per head.  The first pass takes
-    // m_ref from the first tile; if a later tile's maximum exceeds it by more
-    // than kMaxLead (weights up to 2^64 stay far from fp32 overflow), the pass
-    // is abandoned, one scan computes the exact maximum and a last pass runs
-    // with it.  (Scaling O inside the loop would force the 256 accumulators out
-    // of AGPRs.)
-    // per-lane LDS byte offsets of the score-operand reads (chunk 2 ks + hf of
-    // row l32, by ks % 4) and of the transposed value reads (by cm % 2): in a
-    // 16-lane group, lane 4r + b reads row 4 hf + r, channels 4b .. 4b+3 of a
-    // 16-channel column block
-    int qk_off[4], tr_off[2];
+    // Per-lane LDS byte offsets.  Score operand (chunk 2 ks + hf of row
+    // 32 hb + l32): by ks % 4.  Transposed value reads (in a 16-lane group,
+    // lane 4r + b reads row 4 hf + r (+8), channels 4b .. 4b+3 of a 16-channel
+    // block): by cm % 2 and by the +8 row offset.
+    int qk_off[4], tr_off[2][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qk_off[j] = (l32 * 8 + ((2 * j + hf) ^ fswz(l32))) * 16;
+    for (int j = 0; j < 4; ++j) qk_off[j] = (l32 * 8 + ((2 * j + hf) ^ fswz(l32 & 15))) * 16;
     {
         const int r = (lane & 15) >> 2, g1 = (lane >> 4) & 1, b1 = (lane >> 1) & 1;
-        const int f = (r << 1) | hf;                   // fswz(4 hf + r)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            tr_off[j] = ((4 * hf + r) * 8 + ((4 * j + 2 * g1 + b1) ^ f)) * 16 + (lane & 1) * 8;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int t = 8 * e + 4 * hf + r;      // row within a 16-row group
+                tr_off[j][e] = (t * 8 + ((4 * j + 2 * g1 + b1) ^ fswz(t))) * 16 + (lane & 1) * 8;
+            }
     }
+
+    // Softmax without rescaling the accumulators: every weight of a pass is
+    // exp2(s - m_ref) for one reference m_ref per head.  The first pass takes
+    // m_ref from the first half-tile; if a later half-tile's maximum exceeds it
+    // by more than kMaxLead (weights stay below 2^64, far from fp32 overflow)
+    // the pass's result is discarded, one scan computes the exact maximum and
+    // a last pass runs with it.  (Scaling O inside the loop would force the
+    // 256 accumulators out of AGPRs.)  The waves vote after the loop, in LDS.
     constexpr float kMaxLead = 64.0f;
-    // Overflow flags, one per tile parity: iteration t sets flag[t & 1] and
-    // the top of iteration t + 1 reads it after the barrier, so no wave can
-    // see a flag another wave sets later in the same iteration.
-    int* abort_flag = reinterpret_cast<int*>(smem + LDS_BYTES - 16);
     f32x16 o[16];
     float m_ref = kNegInf, l_run = 0.f;
+    bool overflow = false;
     int mode = 0;                        // 0: first-tile reference, 1: max scan, 2: exact reference
+
+    // One tile: start the load of the next tile into `nxt` (when there is
+    // one), then attend over the 64 cache rows in `tile`.  The two buffers
+    // never overlap; saying so (restrict) lets the compiler keep the
+    // transposed value reads from waiting on the load in flight.
+    auto run_tile = [&](int t, const lds_u8* __restrict__ tile, lds_u8* __restrict__ nxt,
+                        bool has_next) __attribute__((always_inline)) {
+        const int valid = valid_of(t);
+        if (has_next) issue(t + 1, nxt);
+#pragma unroll 1
+        for (int hb = 0; hb < 2; ++hb) {
+            if (hb * 32 >= valid) break;
+            // ---- S^T = K . Q^T: rows 32 hb + l32 -----------------------------------
+            const lds_u8* kbase = tile + hb * 32 * 128;
+            auto ka = [&](int ks) {
+                return *reinterpret_cast<const MLA_LDS bf16x8*>(kbase + qk_off[ks & 3] + (ks >> 2) * 8192);
+            };
+            auto qb = [&](int ks) -> bf16x8 {
+                if (ks < NQ) return qf[ks];
+                const int c = 2 * (ks - 32) + hf;
+                return *reinterpret_cast<const MLA_LDS bf16x8*>(qpe_lane + ((c ^ qpe_g) << 4));
+            };
+            f32x16 sacc = {};
+            bf16x8 a0 = ka(0), a1 = ka(1), a2;
+#pragma unroll
+            for (int ks = 0; ks < 36; ++ks) {
+                if (ks + 2 < 36) a2 = ka(ks + 2);
+                sacc = mfma32(a0, qb(ks), sacc);
+                a0 = a1;
+                a1 = a2;
+            }
+            // lane holds head `head`, tokens 32 hb + 8 (i/4) + 4 hf + (i%4)
+            float sv[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sv[i] = sacc[i] * scale_log2;
+            if (valid < BS) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int tok = hb * 32 + (i >> 2) * 8 + 4 * hf + (i & 3);
+                    if (tok >= valid) sv[i] = kNegInf;
+                }
+            }
+            float hmax = sv[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) hmax = fmaxf(hmax, sv[i]);
+            hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
+            if (mode == 1) {
+                m_ref = fmaxf(m_ref, hmax);
+                continue;
+            }
+            if (mode == 0 && t == t0 && hb == 0) m_ref = hmax;
+            // (cannot hold in the exact-reference pass: the scan saw the same
+            // maxima, so at most three passes run)
+            overflow |= hmax > m_ref + kMaxLead;
+
+            float psum = 0.f;
+            bf16x8 pf[2];
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                u16x8 pu;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float pv = __builtin_amdgcn_exp2f(sv[k2 * 8 + j] - m_ref);
+                    psum += pv;
+                    pu[j] = f32_to_bf16_bits(pv);
+                }
+                pf[k2] = __builtin_bit_cast(bf16x8, pu);
+            }
+            psum += __shfl_xor(psum, 32, 64);
+            l_run += psum;
+
+            // ---- O^T += V^T . P^T (latent columns of the same rows) -----------------
+            // K-step k2 covers tokens 32 hb + 16 k2 + {0..3, 8..11} (lanes 0-31)
+            // and {4..7, 12..15} (lanes 32-63), matching P's layout.  Fragments
+            // are read one step ahead; k2 runs outermost so that consecutive
+            // MFMAs update different accumulators.
+            auto va = [&](int k2, int cm) {
+                const lds_u8* vb = tile + (cm >> 1) * 8192 + (hb * 32 + k2 * 16) * 128;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (MLA_LDS bf16x4*)(vb + tr_off[cm & 1][0]));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (MLA_LDS bf16x4*)(vb + tr_off[cm & 1][1]));     // rows +8 are in the offset
+                return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            bf16x8 v0 = va(0, 0), v1;
+#pragma unroll
+            for (int st = 0; st < 32; ++st) {
+                const int k2 = st >> 4, cm = st & 15;
+                if (st + 1 < 32) v1 = va((st + 1) >> 4, (st + 1) & 15);
+                o[cm] = mfma32(v0, pf[k2], o[cm]);
+                v0 = v1;
+            }
+        }
+    };
+
     for (;;) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[i] = f32x16{};
         l_run = 0.f;
-        if (tid == 0) abort_flag[0] = abort_flag[1] = 0;
-        bool aborted = false;
-        issue(t0, 0);
+        overflow = false;
+        issue(t0, FP8 ? smem + TILE : smem);
         for (int t = t0; t < t1; ++t) {
             const int cur = (t - t0) & 1;
-            const int valid = valid_of(t);
             wait_vmem_all();
             __syncthreads();             // tile t landed; previous tile fully consumed
-            if (t > t0 && abort_flag[(t - 1) & 1]) { aborted = true; break; }
-            if (t + 1 < t1) issue(t + 1, cur ^ 1);
-            const unsigned char* tile;
+            const bool has_next = t + 1 < t1;
             if constexpr (FP8) {
-                convert_tile_fp8(stage + cur * F8TILE, sscale + cur * 64, tiles, tid, valid);
+                lds_u8* st_cur = smem + TILE + cur * STAGE;
+                lds_u8* st_nxt = smem + TILE + (cur ^ 1) * STAGE;
+                convert_tile_fp8(st_cur, smem, tid, valid_of(t));
                 __syncthreads();
-                tile = tiles;
+                run_tile(t, smem, st_nxt, has_next);
             } else {
-                tile = tiles + cur * TILE;
-                if (valid < BS) {        // last, partial tile of the sequence
-                    zero_rows(tiles + cur * TILE, valid, tid);
+                lds_u8* cur_tile = smem + cur * TILE;
+                lds_u8* nxt_tile = smem + (cur ^ 1) * TILE;
+                if (valid_of(t) < BS) {  // last, partial tile of the sequence
+                    zero_rows(cur_tile, valid_of(t), tid);
                     __syncthreads();
                 }
-            }
-
-            // Two halves of 32 tokens; each: scores for 32 tokens x 32 heads,
-            // weights, then their contribution to O.
-#pragma unroll 1
-            for (int hb = 0; hb < 2; ++hb) {
-                if (hb * 32 >= valid) break;
-                // ---- S^T = K . Q^T: rows 32 hb + l32 -------------------------------
-                f32x16 sacc = {};
-#pragma unroll
-                for (int ks = 0; ks < 36; ++ks) {
-                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(
-                        tile + qk_off[ks & 3] + (ks >> 2) * 8192 + hb * 32 * 128);
-                    sacc = mfma32(av, qf[ks], sacc);
-                }
-                // lane holds head `head`, tokens 32 hb + 8 (i/4) + 4 hf + (i%4)
-                float sv[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sv[i] = sacc[i] * scale_log2;
-                if (valid < BS) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int tok = hb * 32 + (i >> 2) * 8 + 4 * hf + (i & 3);
-                        if (tok >= valid) sv[i] = kNegInf;
-                    }
-                }
-                float hmax = sv[0];
-#pragma unroll
-                for (int i = 1; i < 16; ++i) hmax = fmaxf(hmax, sv[i]);
-                hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
-                if (mode == 1) {
-                    m_ref = fmaxf(m_ref, hmax);
-                    continue;
-                }
-                if (mode == 0 && t == t0 && hb == 0) m_ref = hmax;
-                // (cannot fire in the exact-reference pass: the scan saw the
-                // same maxima, so at most three passes run)
-                if (hmax > m_ref + kMaxLead) abort_flag[t & 1] = 1;
-
-                float psum = 0.f;
-                bf16x8 pf[2];
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
-                    u16x8 pu;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float pv = __builtin_amdgcn_exp2f(sv[k2 * 8 + j] - m_ref);
-                        psum += pv;
-                        pu[j] = f32_to_bf16_bits(pv);
-                    }
-                    pf[k2] = __builtin_bit_cast(bf16x8, pu);
-                }
-                psum += __shfl_xor(psum, 32, 64);
-                l_run += psum;
-
-                // ---- O^T += V^T . P^T (latent columns of the same rows) -------------
-                // K-step k2 covers tokens 32 hb + 16 k2 + {0..3, 8..11} (lanes
-                // 0-31) and {4..7, 12..15} (lanes 32-63), matching P's layout.
-#pragma unroll
-                for (int cm = 0; cm < 16; ++cm) {
-                    const unsigned char* vb = tile + tr_off[cm & 1] + (cm >> 1) * 8192;
-#pragma unroll
-                    for (int k2 = 0; k2 < 2; ++k2) {
-                        const int tb = hb * 32 + k2 * 16;
-                        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                            (MLA_LDS bf16x4*)(vb + tb * 128));
-                        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                            (MLA_LDS bf16x4*)(vb + (tb + 8) * 128));
-                        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        o[cm] = mfma32(va, pf[k2], o[cm]);
-                    }
-                }
+                run_tile(t, cur_tile, nxt_tile, has_next);
             }
         }
-        if (!aborted) {
-            __syncthreads();             // the last tile's overflow check
-            aborted = abort_flag[(t1 - 1) & 1] != 0;
-        }
-        if (aborted) {
-            __syncthreads();             // everyone has read the flag before it is reset
+        // ---- vote: did any wave's weights run past the reference? ------------------
+        __syncthreads();                 // all waves are done with the tiles
+        MLA_LDS int* votes = reinterpret_cast<MLA_LDS int*>(smem);
+        if (lane == 0) votes[w] = __builtin_amdgcn_ballot_w64(overflow) != 0;
+        __syncthreads();
+        const bool redo = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+        __syncthreads();                 // votes read before the next pass reuses the tiles
+        if (redo) {
             mode = 1;
             m_ref = kNegInf;
             continue;
         }
         if (mode == 1) {
             mode = 2;
-            __syncthreads();
             continue;
         }
         break;
