@@ -494,16 +494,34 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     }
 
     // ---- epilogue: normalised partial o_lat and log-sum-exp ------------------------
+    // A lane holds 16-byte pieces of 32 different head rows, so stores straight
+    // from the accumulators would scatter 32-byte pieces over 2 KB strides.
+    // Instead each wave transposes through its own LDS region (the tiles are
+    // free after the vote barrier), 256 columns at a time, and writes every
+    // head row as 1 KB contiguous stores.  Row stride 260 floats: the 16-byte
+    // writes of 16 consecutive lanes (16 head rows) fall on distinct banks.
+    constexpr int OSTR = 260;
     const float inv_l = 1.0f / l_run;
-    float* po = part_o + (((size_t)row * num_splits + split) * H + head) * DC + 4 * hf;
+    MLA_LDS float* ost = reinterpret_cast<MLA_LDS float*>(smem + w * (32 * OSTR * 4));
+    float* po = part_o + (((size_t)row * num_splits + split) * H + w * 32) * DC + lane * 4;
 #pragma unroll
-    for (int cm = 0; cm < 16; ++cm)
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            f32x4 v = {o[cm][4 * g] * inv_l, o[cm][4 * g + 1] * inv_l, o[cm][4 * g + 2] * inv_l,
-                       o[cm][4 * g + 3] * inv_l};
-            *reinterpret_cast<f32x4*>(po + cm * 32 + g * 8) = v;
+        for (int c8 = 0; c8 < 8; ++c8)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int cm = half * 8 + c8;
+                const f32x4 v = {o[cm][4 * g] * inv_l, o[cm][4 * g + 1] * inv_l,
+                                 o[cm][4 * g + 2] * inv_l, o[cm][4 * g + 3] * inv_l};
+                *reinterpret_cast<MLA_LDS f32x4*>(ost + l32 * OSTR + c8 * 32 + g * 8 + 4 * hf) = v;
+            }
+        // LDS operations of one wave complete in order: the reads see the writes
+#pragma unroll
+        for (int hh = 0; hh < 32; ++hh) {
+            const f32x4 v = *reinterpret_cast<const MLA_LDS f32x4*>(ost + hh * OSTR + lane * 4);
+            *reinterpret_cast<f32x4*>(po + hh * DC + half * 256) = v;
         }
+    }
     if (hf == 0) lse_dst[head] = (m_ref + __builtin_log2f(l_run)) * kLn2;
 }
 
