@@ -91,9 +91,7 @@ DecodeWs decode_ws(const mla_dims& d, int batch, int q_len, int splits) {
     return w;
 }
 
-constexpr int kAppendChunk = 512;
-
-int append_kc(int d_model) { return (d_model + kAppendChunk - 1) / kAppendChunk; }
+int append_kc(int d_model) { return (d_model + mla::kAppendChunk - 1) / mla::kAppendChunk; }
 
 bool append_uses_mfma(const mla_dims& d, int d_model) {
     return d.act_dtype == MLA_BF16 && (d.kv_lora_rank + d.qk_rope_dim) % 32 == 0 &&
@@ -262,7 +260,7 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t n_new, 
     a.pool_scale = cache_scale;
     a.part = static_cast<float*>(workspace);
     a.kc = mfma ? append_kc(d_model) : 1;
-    a.kchunk = mfma ? kAppendChunk : d_model;
+    a.kchunk = mfma ? mla::kAppendChunk : d_model;
     a.stream = static_cast<hipStream_t>(stream);
     const hipError_t e = mla::launch_append(a, mfma);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -17,9 +17,11 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// One wave per (32 outputs, 32 tokens, K chunk):
+// One wave per (32 outputs, 32 tokens, K chunk of at most kAppendChunk):
 //   part[kc][t][o] = sum_{d in chunk} W[o][d] h[t][d]
-// as x^T = W . h^T with both operands streamed straight from global memory.
+// as x^T = W . h^T with both operands streamed straight from global memory;
+// all of a chunk's fragments are loaded before the first MFMA, so a wave
+// waits for memory once.
 __global__ __launch_bounds__(256) void append_gemm_mfma(const unsigned short* __restrict__ h,
                                                         const unsigned short* __restrict__ w,
                                                         int T, int d, int Dout, int kc_count,
@@ -38,13 +40,21 @@ __global__ __launch_bounds__(256) void append_gemm_mfma(const unsigned short* __
     const unsigned short* wp = w + (size_t)o * d + hf * 8;
     const unsigned short* hp = h + (size_t)min(t, T - 1) * d + hf * 8;
     const bool tok_ok = t < T;
-    f32x16 acc = {};
-    for (int k = k_lo; k < k_hi; k += 16) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(wp + k);
-        bf16x8 b = *reinterpret_cast<const bf16x8*>(hp + k);
-        if (!tok_ok) b = bf16x8{};
-        acc = mfma32(a, b, acc);
+    constexpr int NK = kAppendChunk / 16;
+    bf16x8 av[NK], bv[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        const int k = k_lo + i * 16;
+        av[i] = bf16x8{};
+        bv[i] = bf16x8{};
+        if (k < k_hi) {
+            av[i] = *reinterpret_cast<const bf16x8*>(wp + k);
+            if (tok_ok) bv[i] = *reinterpret_cast<const bf16x8*>(hp + k);
+        }
     }
+    f32x16 acc = {};
+#pragma unroll
+    for (int i = 0; i < NK; ++i) acc = mfma32(av[i], bv[i], acc);
     if (tok_ok) {
         float* dst = part + ((size_t)kc * T + t) * Dout + mb * 32 + 4 * hf;
 #pragma unroll
@@ -81,11 +91,36 @@ __global__ __launch_bounds__(256) void append_finalize(
     const int t = blockIdx.x;
     const int Dout = DC + DR;
     float ss = 0.f;
-    for (int o = threadIdx.x; o < Dout; o += 256) {
-        float x = 0.f;
-        for (int kc = 0; kc < kc_count; ++kc) x += part[((size_t)kc * T + t) * Dout + o];
-        y[o] = x;
-        if (o < DC) ss += x * x;
+    // Sum of the split-K partials, chunk by chunk in increasing order.  Common
+    // shapes (Dout <= 768, kc_count <= 32) issue every load of the thread
+    // before the first add, so the sum costs one memory round trip.
+    if (Dout <= 3 * 256 && kc_count <= 32) {
+        float pv[3][32];
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int o = threadIdx.x + u * 256;
+#pragma unroll
+            for (int kc = 0; kc < 32; ++kc)
+                pv[u][kc] = (o < Dout && kc < kc_count) ? part[((size_t)kc * T + t) * Dout + o] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int o = threadIdx.x + u * 256;
+            float x = 0.f;
+#pragma unroll
+            for (int kc = 0; kc < 32; ++kc) x += pv[u][kc];
+            if (o < Dout) {
+                y[o] = x;
+                if (o < DC) ss += x * x;
+            }
+        }
+    } else {
+        for (int o = threadIdx.x; o < Dout; o += 256) {
+            float x = 0.f;
+            for (int kc = 0; kc < kc_count; ++kc) x += part[((size_t)kc * T + t) * Dout + o];
+            y[o] = x;
+            if (o < DC) ss += x * x;
+        }
     }
     ss = block_sum(ss, red);                      // also publishes y[]
     const float inv = 1.0f / sqrtf(ss / (float)DC + eps);
@@ -100,11 +135,18 @@ __global__ __launch_bounds__(256) void append_finalize(
             v = y[o] * inv * load_act<ADT>(gamma, o);
         } else {
             const int k = (o - DC) >> 1;
+            // The angle needs double precision (at position 2^17 an fp32 angle
+            // is off by up to 1/64 rad): form it in double, reduce it modulo
+            // 2 pi with one fma against the double nearest 2 pi (error below
+            // 1e-11 rad for positions under 2^20), then take fp32 sin / cos of
+            // the reduced angle.
             const double ang = (double)pos * pow((double)rope_base, -2.0 * k / (double)DR);
-            double sn, cs;
-            sincos(ang, &sn, &cs);
-            const double x0 = y[DC + 2 * k], x1 = y[DC + 2 * k + 1];
-            v = (float)(((o - DC) & 1) ? x0 * sn + x1 * cs : x0 * cs - x1 * sn);
+            const double turns = rint(ang * 0.15915494309189535);
+            const float red = (float)fma(-turns, 6.283185307179586, ang);
+            float sn, cs;
+            sincosf(red, &sn, &cs);
+            const float x0 = y[DC + 2 * k], x1 = y[DC + 2 * k + 1];
+            v = ((o - DC) & 1) ? x0 * sn + x1 * cs : x0 * cs - x1 * sn;
         }
         yo[cnt] = v;
     }

@@ -106,6 +106,17 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
                 (unsigned long long)v[2] | ((unsigned long long)v[3] << 32);
         }
     }
+    // this wave's q_nope fragments (B operands), loaded together with W_UK
+    bf16x8 qv[8][2];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int r = rb * 64 + nb * 32 + l32;
+            qv[ks][nb] = r < R ? *reinterpret_cast<const bf16x8*>(
+                                     q_nope + ((size_t)r * H + h) * 128 + ks * 16 + hf * 8)
+                               : bf16x8{};
+        }
     // q_pe rides along in the workgroups of column block 0
     if (cb == 0) {
         for (int i = tid; i < 64 * 8; i += 256) {       // 64 rows x 8 chunks of 8
@@ -128,13 +139,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
         for (int j = 0; j < 8; ++j) au[j] = wt[(ks * 16 + hf * 8 + j) * WT_STRIDE + cl];
         a = __builtin_bit_cast(bf16x8, au);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int r = rb * 64 + nb * 32 + l32;
-            bf16x8 bv = {};
-            if (r < R)
-                bv = *reinterpret_cast<const bf16x8*>(q_nope + ((size_t)r * H + h) * 128 + ks * 16 + hf * 8);
-            acc[nb] = mfma32(a, bv, acc[nb]);
-        }
+        for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a, qv[ks][nb], acc[nb]);
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -530,53 +535,103 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
 // ---------------------------------------------------------------------------
 
 // grid: H * ceil(R / 32) workgroups (h fastest, so one head's row blocks share
-// an XCD and its W_UV slice in L2).  Wave w combines rows 8w .. 8w+7 of the
-// block into LDS, then computes out^T[32w .. +32][rows] = W_UV[h] o_lat^T.
+// an XCD and its W_UV slice in L2).  Workgroup (h, rb) handles rows rb*32 ..
+// +32 of head h; wave w combines rows 8w .. 8w+7, then computes
+// out^T[32w .. +32][rows] = W_UV[h] o_lat^T.  Every phase issues its global
+// loads together (partition weights, then all partitions of 8 rows, then the
+// whole W_UV slice) so each costs about one memory round trip.
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, int R, int num_splits,
     const unsigned short* __restrict__ w_uv,    // [H][128][512]
     unsigned short* __restrict__ out,           // [R][H][128] bf16
     float* __restrict__ lse_out) {              // [R][H] or null
     __shared__ __attribute__((aligned(16))) unsigned char ol[2][32 * 1024];   // hi, lo bf16
+    __shared__ float wts[32][kMaxSplits];       // normalised partition weights per local row
     const int h = blockIdx.x % H;
     const int rb = blockIdx.x / H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in an SGPR
     const int l32 = lane & 31, hf = lane >> 5;
+    const int S = num_splits;
 
-    for (int rr = 0; rr < 8; ++rr) {
-        const int rl = w * 8 + rr;                     // local row
-        const int r = rb * 32 + rl;
-        float acc[8] = {};
-        float tot = 0.f, mx = kNegInf;
-        if (r < R) {
-            const float* lrow = part_lse + (size_t)r * num_splits * H + h;
-            for (int s = lane; s < num_splits; s += 64) mx = fmaxf(mx, lrow[(size_t)s * H]);
-            mx = wave_max(mx);
-            if (mx != kNegInf) {
-                for (int s = 0; s < num_splits; ++s) {
-                    const float ls = lrow[(size_t)s * H];
-                    if (ls == kNegInf) continue;
-                    const float wt = __expf(ls - mx);
-                    tot += wt;
-                    const float* src = part_o + (((size_t)r * num_splits + s) * H + h) * DC + lane * 8;
-                    const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
-                    const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+    // ---- partition weights exp(lse_s - max) / sum and the merged lse; lanes
+    // run over partitions (S <= 256 = 4 x 64)
+    {
+        float lv[8][4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        acc[j] += wt * v0[j];
-                        acc[4 + j] += wt * v1[j];
-                    }
-                }
+        for (int rr = 0; rr < 8; ++rr) {
+            const int r = rb * 32 + w * 8 + rr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sp = lane + 64 * j;
+                lv[rr][j] = (r < R && sp < S) ? part_lse[((size_t)r * S + sp) * H + h] : kNegInf;
             }
-            if (lse_out != nullptr && lane == 0)
+        }
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const int rl = w * 8 + rr, r = rb * 32 + rl;
+            const float mx = wave_max(fmaxf(fmaxf(lv[rr][0], lv[rr][1]), fmaxf(lv[rr][2], lv[rr][3])));
+            float e[4], tot = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                e[j] = lv[rr][j] == kNegInf ? 0.f : __expf(lv[rr][j] - mx);
+                tot += e[j];
+            }
+            tot = wave_sum(tot);
+            const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (lane + 64 * j < S) wts[rl][lane + 64 * j] = e[j] * inv;
+            if (lse_out != nullptr && lane == 0 && r < R)
                 lse_out[(size_t)r * H + h] = (mx == kNegInf) ? kNegInf : mx + __logf(tot);
         }
-        const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+    }
+    // (each wave reads back only its own rows' weights: LDS operations of one
+    // wave complete in order)
+
+    // ---- o_lat of rows 8w .. 8w+7: lane holds columns 8 lane .. 8 lane + 7.
+    // A partition with no visible token has weight 0 and an unwritten partial:
+    // select, never multiply, so whatever that memory holds cannot leak in.
+    float acc[8][8];
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[rr][j] = 0.f;
+    const float* pbase = part_o + (size_t)h * DC + lane * 8;
+#pragma unroll 2
+    for (int sp = 0; sp < S; ++sp) {
+        f32x4 v[8][2];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const int r = min(rb * 32 + w * 8 + rr, R - 1);      // rows past R: weight 0
+            const float* src = pbase + ((size_t)r * S + sp) * H * DC;
+            v[rr][0] = *reinterpret_cast<const f32x4*>(src);
+            v[rr][1] = *reinterpret_cast<const f32x4*>(src + 4);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const float wt = wts[w * 8 + rr][sp];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = v[rr][j >> 2][j & 3];
+                acc[rr][j] += wt != 0.f ? wt * x : 0.f;
+            }
+        }
+    }
+    // W_UV slice of this wave's 32 output rows: all 32 fragments at once
+    bf16x8 wa[32];
+    {
+        const unsigned short* wrow = w_uv + ((size_t)h * 128 + w * 32 + l32) * DC + hf * 8;
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) wa[ks] = *reinterpret_cast<const bf16x8*>(wrow + ks * 16);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+        const int rl = w * 8 + rr;
         u16x8 hi, lo;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float v = acc[j] * inv;
+            const float v = acc[rr][j];
             hi[j] = f32_to_bf16_bits(v);
             lo[j] = f32_to_bf16_bits(v - bf16_bits_to_f32(hi[j]));
         }
@@ -586,17 +641,15 @@ __global__ __launch_bounds__(256) void combine_kernel(
     }
     __syncthreads();
 
-    f32x16 acc = {};
-    const unsigned short* wrow = w_uv + ((size_t)h * 128 + w * 32 + l32) * DC + hf * 8;
-#pragma unroll 4
+    f32x16 oacc = {};
+#pragma unroll
     for (int ks = 0; ks < 32; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow + ks * 16);
         const int ch = 2 * ks + hf;
         const int off = l32 * 1024 + ((ch ^ (l32 & 7)) << 4);
         const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&ol[0][off]);
         const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&ol[1][off]);
-        acc = mfma32(a, bh, acc);
-        acc = mfma32(a, bl, acc);
+        oacc = mfma32(wa[ks], bh, oacc);
+        oacc = mfma32(wa[ks], bl, oacc);
     }
     const int r = rb * 32 + l32;
     if (r < R) {
@@ -604,10 +657,10 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const unsigned long long pk =
-                (unsigned long long)f32_to_bf16_bits(acc[4 * g + 0]) |
-                ((unsigned long long)f32_to_bf16_bits(acc[4 * g + 1]) << 16) |
-                ((unsigned long long)f32_to_bf16_bits(acc[4 * g + 2]) << 32) |
-                ((unsigned long long)f32_to_bf16_bits(acc[4 * g + 3]) << 48);
+                (unsigned long long)f32_to_bf16_bits(oacc[4 * g + 0]) |
+                ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 1]) << 16) |
+                ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 2]) << 32) |
+                ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 3]) << 48);
             *reinterpret_cast<unsigned long long*>(dst + 8 * g) = pk;
         }
     }

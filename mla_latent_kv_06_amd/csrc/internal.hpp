@@ -13,6 +13,7 @@ namespace mla {
 // MI355X compute units; the default split count aims to give every CU work.
 constexpr int kNumCUs = 256;
 constexpr int kMaxSplits = 256;
+constexpr int kAppendChunk = 256;     // d_model columns per split-K chunk of the MFMA projection
 
 struct DecodeLaunch {
     // shape
