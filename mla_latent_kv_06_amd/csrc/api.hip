@@ -86,7 +86,9 @@ DecodeWs decode_ws(const mla_dims& d, int batch, int q_len, int splits) {
     w.qbuf = 0;
     size_t qb = R * H * (d.kv_lora_rank + d.qk_rope_dim) * (mfma ? 2 : 4);
     w.part_o = align_up(qb, 256);
-    w.part_lse = w.part_o + align_up(R * splits * H * d.kv_lora_rank * sizeof(float), 256);
+    // partial o_lat: fp16 on the MFMA path (normalised convex combinations of
+    // latent rows, stored with 2^-11 relative precision), fp32 otherwise
+    w.part_lse = w.part_o + align_up(R * splits * H * d.kv_lora_rank * (mfma ? 2 : 4), 256);
     w.total = w.part_lse + align_up(R * splits * H * sizeof(float), 256);
     return w;
 }
@@ -163,7 +165,7 @@ mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const
     a.lse = lse;
     char* base = static_cast<char*>(workspace);
     a.qbuf = base + ws.qbuf;
-    a.part_o = reinterpret_cast<float*>(base + ws.part_o);
+    a.part_o = base + ws.part_o;
     a.part_lse = reinterpret_cast<float*>(base + ws.part_lse);
     a.stream = static_cast<hipStream_t>(stream);
     const hipError_t e = mfma ? mla::launch_decode_mfma(a, stages) : mla::launch_decode_generic(a, stages);

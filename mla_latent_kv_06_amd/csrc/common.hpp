@@ -16,6 +16,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(8 * sizeof(unsigned short)))) unsigned short u16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned int)))) unsigned int u32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned short)))) unsigned short u16x4;
 
 #define MLA_LDS __attribute__((address_space(3)))
 
@@ -31,6 +32,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
 }
 
 // float -> bfloat16 bits, round to nearest even (NaN kept quiet).
+// IEEE binary16 bit patterns (the conversion rounds to nearest even)
+__device__ __forceinline__ unsigned short f32_to_f16_bits(float f) {
+    return __builtin_bit_cast(unsigned short, (_Float16)f);
+}
+__device__ __forceinline__ float f16_bits_to_f32(unsigned short b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
 __device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
     __bf16 h = static_cast<__bf16>(f);   // v_cvt_pk_bf16_f32 on gfx950: RNE
     return __builtin_bit_cast(unsigned short, h);

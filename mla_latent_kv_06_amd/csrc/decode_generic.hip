@@ -172,11 +172,12 @@ hipError_t run(const DecodeLaunch& a, unsigned stages) {
     if (stages & MLA_STAGE_SPLIT_KV) {
         g_split<CDT><<<R * a.num_splits * a.H, NT, 0, a.stream>>>(
             qbuf, a.pool, a.pool_scale, a.block_table, a.max_blocks, a.seq_lens, a.q_len,
-            a.num_splits, a.H, a.DC, a.DR, a.BS, a.scale, a.part_o, a.part_lse);
+            a.num_splits, a.H, a.DC, a.DR, a.BS, a.scale, static_cast<float*>(a.part_o), a.part_lse);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     if (stages & MLA_STAGE_COMBINE) {
-        g_combine<ADT><<<R * a.H, NT, 0, a.stream>>>(a.part_o, a.part_lse, a.num_splits, a.H, a.DC,
+        g_combine<ADT><<<R * a.H, NT, 0, a.stream>>>(static_cast<const float*>(a.part_o), a.part_lse,
+                                                    a.num_splits, a.H, a.DC,
                                                      a.V, a.w_uv, a.out, a.lse);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }

@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const float* __restrict__ pool_scale,         // [blocks][64] (fp8)
     const int* __restrict__ block_table, int max_blocks,
     const int* __restrict__ seq_lens, int q_len, int num_splits, float scale_log2,
-    float* __restrict__ part_o,                   // [R][S][H][512]
+    unsigned short* __restrict__ part_o,          // [R][S][H][512] fp16
     float* __restrict__ part_lse) {               // [R][S][H]
     // bf16: two tiles + the rotary queries of all heads (16 KB) = 160 KiB;
     // fp8: one bf16 tile + two fp8 staging tiles with scales (rotary queries in VGPRs)
@@ -498,34 +498,35 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         break;
     }
 
-    // ---- epilogue: normalised partial o_lat and log-sum-exp ------------------------
-    // A lane holds 16-byte pieces of 32 different head rows, so stores straight
-    // from the accumulators would scatter 32-byte pieces over 2 KB strides.
-    // Instead each wave transposes through its own LDS region (the tiles are
-    // free after the vote barrier), 256 columns at a time, and writes every
-    // head row as 1 KB contiguous stores.  Row stride 260 floats: the 16-byte
-    // writes of 16 consecutive lanes (16 head rows) fall on distinct banks.
-    constexpr int OSTR = 260;
+    // ---- epilogue: normalised partial o_lat (fp16) and log-sum-exp ---------------
+    // The partial is a convex combination of latent rows: fp16 keeps it to
+    // 2^-11 relative and halves the bytes every workgroup writes at the same
+    // moment (and the combine reads).  A lane holds 16-byte pieces of 32
+    // different head rows, so each wave transposes through its own LDS region
+    // (the tiles are free after the vote barrier) and writes every head row as
+    // one 1 KB store.  Row stride 520 halves: the 8-byte writes of 16
+    // consecutive lanes (16 head rows) fall on distinct banks.  Waves start
+    // at different rows so that concurrent stores spread over memory channels.
+    constexpr int OSTR = 520;
     const float inv_l = 1.0f / l_run;
-    MLA_LDS float* ost = reinterpret_cast<MLA_LDS float*>(smem + w * (32 * OSTR * 4));
-    float* po = part_o + (((size_t)row * num_splits + split) * H + w * 32) * DC + lane * 4;
+    MLA_LDS unsigned short* ost = reinterpret_cast<MLA_LDS unsigned short*>(smem + w * (32 * OSTR * 2));
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int cm = 0; cm < 16; ++cm)
 #pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8)
+        for (int g = 0; g < 4; ++g) {
+            u16x4 hv;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int cm = half * 8 + c8;
-                const f32x4 v = {o[cm][4 * g] * inv_l, o[cm][4 * g + 1] * inv_l,
-                                 o[cm][4 * g + 2] * inv_l, o[cm][4 * g + 3] * inv_l};
-                *reinterpret_cast<MLA_LDS f32x4*>(ost + l32 * OSTR + c8 * 32 + g * 8 + 4 * hf) = v;
-            }
-        // LDS operations of one wave complete in order: the reads see the writes
-#pragma unroll
-        for (int hh = 0; hh < 32; ++hh) {
-            const f32x4 v = *reinterpret_cast<const MLA_LDS f32x4*>(ost + hh * OSTR + lane * 4);
-            *reinterpret_cast<f32x4*>(po + hh * DC + half * 256) = v;
+            for (int j = 0; j < 4; ++j) hv[j] = f32_to_f16_bits(o[cm][4 * g + j] * inv_l);
+            *reinterpret_cast<MLA_LDS u16x4*>(ost + l32 * OSTR + cm * 32 + g * 8 + 4 * hf) = hv;
         }
+    // LDS operations of one wave complete in order: the reads see the writes
+    unsigned short* po = part_o + (((size_t)row * num_splits + split) * H + w * 32) * DC + lane * 8;
+    const int rot = (blockIdx.x * 4 + w) & 31;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int hh = (i + rot) & 31;
+        const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(ost + hh * OSTR + lane * 8);
+        *reinterpret_cast<u32x4*>(po + hh * DC) = v;
     }
     if (hf == 0) lse_dst[head] = (m_ref + __builtin_log2f(l_run)) * kLn2;
 }
@@ -541,7 +542,8 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
 // loads together (partition weights, then all partitions of 8 rows, then the
 // whole W_UV slice) so each costs about one memory round trip.
 __global__ __launch_bounds__(256) void combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse, int R, int num_splits,
+    const unsigned short* __restrict__ part_o,  // [R][S][H][512] fp16
+    const float* __restrict__ part_lse, int R, int num_splits,
     const unsigned short* __restrict__ w_uv,    // [H][128][512]
     unsigned short* __restrict__ out,           // [R][H][128] bf16
     float* __restrict__ lse_out) {              // [R][H] or null
@@ -597,23 +599,21 @@ __global__ __launch_bounds__(256) void combine_kernel(
     for (int rr = 0; rr < 8; ++rr)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[rr][j] = 0.f;
-    const float* pbase = part_o + (size_t)h * DC + lane * 8;
+    const unsigned short* pbase = part_o + (size_t)h * DC + lane * 8;
 #pragma unroll 2
     for (int sp = 0; sp < S; ++sp) {
-        f32x4 v[8][2];
+        u32x4 v[8];
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
             const int r = min(rb * 32 + w * 8 + rr, R - 1);      // rows past R: weight 0
-            const float* src = pbase + ((size_t)r * S + sp) * H * DC;
-            v[rr][0] = *reinterpret_cast<const f32x4*>(src);
-            v[rr][1] = *reinterpret_cast<const f32x4*>(src + 4);
+            v[rr] = *reinterpret_cast<const u32x4*>(pbase + ((size_t)r * S + sp) * H * DC);
         }
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
             const float wt = wts[w * 8 + rr][sp];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float x = v[rr][j >> 2][j & 3];
+                const float x = f16_bits_to_f32((unsigned short)(v[rr][j >> 1] >> (16 * (j & 1))));
                 acc[rr][j] += wt != 0.f ? wt * x : 0.f;
             }
         }
@@ -692,18 +692,21 @@ hipError_t launch_decode_mfma(const DecodeLaunch& a, unsigned stages) {
         if (a.cache_dtype == MLA_FP8_E4M3) {
             split_kv_kernel<true><<<grid, 256, 0, a.stream>>>(
                 qbuf, static_cast<const unsigned char*>(a.pool), a.pool_scale, a.block_table,
-                a.max_blocks, a.seq_lens, a.q_len, a.num_splits, scale_log2, a.part_o, a.part_lse);
+                a.max_blocks, a.seq_lens, a.q_len, a.num_splits, scale_log2,
+                static_cast<unsigned short*>(a.part_o), a.part_lse);
         } else {
             split_kv_kernel<false><<<grid, 256, 0, a.stream>>>(
                 qbuf, static_cast<const unsigned char*>(a.pool), nullptr, a.block_table,
-                a.max_blocks, a.seq_lens, a.q_len, a.num_splits, scale_log2, a.part_o, a.part_lse);
+                a.max_blocks, a.seq_lens, a.q_len, a.num_splits, scale_log2,
+                static_cast<unsigned short*>(a.part_o), a.part_lse);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (stages & MLA_STAGE_COMBINE) {
         const int grid = H * ((R + 31) / 32);
-        combine_kernel<<<grid, 256, 0, a.stream>>>(a.part_o, a.part_lse, R, a.num_splits,
+        combine_kernel<<<grid, 256, 0, a.stream>>>(static_cast<const unsigned short*>(a.part_o),
+                                                   a.part_lse, R, a.num_splits,
                                                    static_cast<const unsigned short*>(a.w_uv),
                                                    static_cast<unsigned short*>(a.out), a.lse);
         hipError_t e = hipGetLastError();

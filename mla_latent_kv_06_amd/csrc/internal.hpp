@@ -35,7 +35,7 @@ struct DecodeLaunch {
     float* lse;
     // workspace carve-up
     void* qbuf;                  // [R][H][DC+DR]: bf16 (MFMA path) or f32 (portable)
-    float* part_o;               // [R][S][H][DC]
+    void* part_o;                // [R][S][H][DC]: fp16 on the MFMA path, fp32 otherwise
     float* part_lse;             // [R][S][H]
     hipStream_t stream;
 };
