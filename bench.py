@@ -1,12 +1,13 @@
 """Benchmark: absorbed-MLA decode tokens/s + latent-cache HBM GB/s on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--layers NL] [--splits S] [--no-cpu-baseline] [--report FILE]
+                    [--layers NL] [--splits S] [--no-cpu-baseline] [--cpu-tokens N]
+                    [--report FILE]
 
 One step = the whole hot path for one layer over one batch: the cache append
-of one new token per sequence (wkv_a projection, RMSNorm, RoPE, paged write)
-followed by the absorbed decode (q absorption, split-KV attention over the
-paged latent cache, log-sum-exp combine, W_UV).  Steps rotate over NL
+of the new tokens (wkv_a projection, RMSNorm, RoPE, paged write; workloads
+that define one) followed by the absorbed decode (q absorption, split-KV
+attention over the paged latent cache, log-sum-exp combine, W_UV).  Steps rotate over NL
 independent layer copies (own pool, weights, queries) so the working set is
 far larger than the 256 MB last-level cache; inputs are resident in HBM before
 timing starts.  Prints ONE JSON line on stdout; details go to stderr.
@@ -71,9 +72,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="v3_b64_ctx8k_paged_bf16")
     p.add_argument("--layers", type=int, default=8)
-    p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--splits", type=int, default=None,
+                   help="split-KV partitions per query row (default: the workload's own; "
+                        "0 = the library's balanced schedule)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seqs", type=int, default=32)
+    p.add_argument("--cpu-tokens", type=int, default=262144,
+                   help="CPU-baseline sample: first sequences of layer 0 up to this many cached tokens")
     p.add_argument("--report", default=None)
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="instead: copy a buffer of this many bytes 5 times (calibrates "
@@ -107,17 +111,24 @@ class Layer:
         self.block_table = torch.from_numpy(table).to(dev)
         self.seq_lens = torch.from_numpy(seq_lens).to(dev)
         self.start_pos = torch.from_numpy(cached.astype(np.int32)).to(dev)
-        # cache rows: N(0,1) bf16 drawn on the device (unit RMS in expectation);
-        # decode time does not depend on the values
+        # cache rows: N(0,1) drawn on the device (unit RMS in expectation);
+        # decode time does not depend on the values.  fp8: e4m3 codes of the
+        # draw times 64 (inside the +-448 range) with a per-token scale of 1/64.
         g = torch.Generator(device=dev)
         g.manual_seed(seed)
-        self.pool = torch.empty((nblk, wl.block_size, wl.row_width), dtype=bf, device=dev)
+        fp8 = wl.cache_dtype == "fp8"
+        self.pool = torch.empty((nblk, wl.block_size, wl.row_width),
+                                dtype=torch.uint8 if fp8 else bf, device=dev)
         flat = self.pool.view(-1, wl.row_width)
         step = 1 << 16
         for i in range(0, flat.shape[0], step):
-            flat[i:i + step] = torch.randn(flat[i:i + step].shape, generator=g, device=dev,
-                                           dtype=torch.float32).to(bf)
-        self.scale = None
+            x = torch.randn(flat[i:i + step].shape, generator=g, device=dev, dtype=torch.float32)
+            if fp8:
+                flat[i:i + step] = (x * 64.0).to(torch.float8_e4m3fn).view(torch.uint8)
+            else:
+                flat[i:i + step] = x.to(bf)
+        self.scale = (torch.full((nblk, wl.block_size), 1.0 / 64.0, dtype=torch.float32, device=dev)
+                      if fp8 else None)
         self.out = torch.empty((B, wl.q_len, H, wl.v_head_dim), dtype=bf, device=dev)
         self.lse = torch.empty((B, wl.q_len, H), dtype=torch.float32, device=dev)
 
@@ -144,11 +155,11 @@ def main():
         log(f"copied {n} bytes 5 times")
         return
     wl = synth.WORKLOADS[args.workload]
-    if wl.cache_dtype != "bf16" or wl.act_dtype != "bf16":
-        raise SystemExit("bench.py times bf16 workloads")
+    if wl.act_dtype != "bf16" or wl.cache_dtype not in ("bf16", "fp8"):
+        raise SystemExit("bench.py times the bf16-activation workloads (bf16 or fp8 cache)")
     dims = b.Dims.from_workload(wl)
     B, Sq, H = wl.batch, wl.q_len, wl.n_heads
-    splits = args.splits or b.default_splits(dims, B, Sq)
+    splits = wl.num_splits if args.splits is None else args.splits
 
     t_setup = time.time()
     layers = [Layer(wl, li, dims, dev, torch, synth, b) for li in range(args.layers)]
@@ -157,14 +168,17 @@ def main():
                          dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s: {args.layers} layers, "
-        f"pool {layers[0].pool.numel() * 2 / 1e6:.1f} MB each, splits {splits}")
+        f"pool {layers[0].pool.numel() * layers[0].pool.element_size() / 1e6:.1f} MB each, "
+        f"splits {splits if splits else 'balanced'}")
 
     stream = torch.cuda.current_stream(dev)
 
     def step(L, ev=None):
-        b.append(dims, L.h, L.w_kv_a, L.gamma, L.block_table, L.start_pos, L.pool, None,
-                 rms_eps=1e-6, rope_base=10000.0, workspace=ws_app)
-        common = (dims, L.q_nope, L.q_pe, L.w_uk, L.w_uv, L.pool, None, L.block_table, L.seq_lens)
+        if wl.append:
+            b.append(dims, L.h, L.w_kv_a, L.gamma, L.block_table, L.start_pos, L.pool, L.scale,
+                     rms_eps=1e-6, rope_base=10000.0, workspace=ws_app)
+        common = (dims, L.q_nope, L.q_pe, L.w_uk, L.w_uv, L.pool, L.scale, L.block_table,
+                  L.seq_lens)
         b.decode(*common, num_splits=splits, out=L.out, lse=L.lse, workspace=ws_dec,
                  stages=b.STAGE_ABSORB_Q)
         if ev is not None:
@@ -200,12 +214,16 @@ def main():
 
     tokens_per_step = B * Sq
     value = tokens_per_step / (ms_step / 1e3)
-    # algorithmic work of the split-KV kernel: every visible cache token's
-    # 576-element row is read once; 2*H*(576+512) flops per token and query row
+    # algorithmic work of the split-KV kernel: every cache token's 576-element
+    # row (plus its fp8 scale) is read once; 2*H*(576+512) flops per visible
+    # token and query row
     seq_lens = layers[0].seq_lens_host.astype(np.int64)
-    cache_bytes = int(seq_lens.sum()) * wl.row_width * 2
+    row_bytes = wl.row_width * (1 if wl.cache_dtype == "fp8" else 2) + (4 if wl.cache_dtype == "fp8" else 0)
+    cache_bytes = int(seq_lens.sum()) * row_bytes
     flops = sum(int(L - Sq + s + 1) for L in seq_lens for s in range(Sq)) * 2 * H * (wl.row_width + wl.kv_lora_rank)
     achieved = cache_bytes / k_avg_s / 1e9
+    tflops = flops / k_avg_s / 1e12
+    mfma_bound = flops / cache_bytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     step_gbs = cache_bytes / (ms_step / 1e3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us  ({value:.4g} tok/s)  split-KV kernel {k_avg_s * 1e6:.1f} us "
         f"(p10 {np.percentile(k_ms, 10) * 1e3:.1f} / p90 {np.percentile(k_ms, 90) * 1e3:.1f})")
@@ -229,15 +247,22 @@ def main():
         "config": {
             "workload": wl.name, "batch": B, "ctx": int(seq_lens.max()), "q_len": Sq,
             "heads": H, "kv_lora_rank": wl.kv_lora_rank, "rope_dim": wl.qk_rope_dim,
-            "block_size": wl.block_size, "paged": wl.paged, "num_splits": splits,
+            "block_size": wl.block_size, "paged": wl.paged,
+            "num_splits": splits if splits else "balanced",
             "layers_rotated": args.layers,
-            "step": "cache append of 1 token/seq + absorbed decode, one layer",
+            "cache_dtype": wl.cache_dtype,
+            "step": ("cache append of %d token(s)/seq + absorbed decode, one layer" % Sq
+                     if wl.append else "absorbed decode, one layer"),
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
-            "bound": "hbm", "kernel": "split_kv_kernel<bf16>",
-            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "bound": "mfma" if mfma_bound else "hbm",
+            "kernel": "split_kv_kernel<%s>" % wl.cache_dtype,
+            "achieved": round(tflops if mfma_bound else achieved, 1),
+            "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round(tflops / BF16_PEAK_TFLOPS if mfma_bound else achieved / HBM_PEAK_GBS, 4),
+            "hbm_gbs": round(achieved, 1),
             "traffic": profiled_traffic(wl.name), "traffic_unit": "bytes per launch",
             "algorithmic_bytes": cache_bytes,
             "avg_launch_us": round(k_avg_s * 1e6, 2),
@@ -258,7 +283,7 @@ def main():
 
 def cpu_baseline(args, wl, L, torch):
     """The CPU oracle (naive float64 decode) on a bounded sample of the same
-    workload: the first --cpu-seqs sequences of layer 0, all heads, read back
+    workload: the first sequences of layer 0 up to --cpu-tokens cached tokens, all heads, read back
     from the device.  Also checks the GPU output for those sequences."""
     import oracle
     try:
@@ -266,16 +291,31 @@ def cpu_baseline(args, wl, L, torch):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    n = min(args.cpu_seqs, wl.batch)
+    n, tot = 0, 0
+    while n < wl.batch and (n == 0 or tot + int(L.seq_lens_host[n]) <= args.cpu_tokens):
+        tot += int(L.seq_lens_host[n])
+        n += 1
     D = wl.row_width
     torch.cuda.synchronize()
 
     def f64(t):
         return t.float().cpu().numpy().astype(np.float64)
 
-    pool_rows = f64(L.pool.view(-1, D))
-    rows = [oracle.gather_sequence(pool_rows, L.table_host[i], int(L.seq_lens_host[i]), wl.block_size)
-            for i in range(n)]
+    def seq_rows(i):
+        # this sequence's blocks only (gathered on the device), then the
+        # oracle's own gather over a compact table
+        nb = (int(L.seq_lens_host[i]) + wl.block_size - 1) // wl.block_size
+        ids = torch.from_numpy(L.table_host[i, :nb].astype(np.int64)).to(L.pool.device)
+        blocks = L.pool.index_select(0, ids).view(-1, D)
+        if wl.cache_dtype == "fp8":
+            codes = blocks.cpu().numpy()
+            sc = L.scale.index_select(0, ids).reshape(-1).cpu().numpy()
+            rows64 = oracle.dequantize_rows_fp8(codes, sc)
+        else:
+            rows64 = f64(blocks)
+        return oracle.gather_sequence(rows64, np.arange(nb), int(L.seq_lens_host[i]), wl.block_size)
+
+    rows = [seq_rows(i) for i in range(n)]
     qn, qp = f64(L.q_nope[:n]), f64(L.q_pe[:n])
     wuk, wuv = f64(L.w_uk), f64(L.w_uv)
     t = time.time()
@@ -286,8 +326,8 @@ def cpu_baseline(args, wl, L, torch):
     log(f"cpu oracle: {n} sequences in {dt:.1f}s on {threads} threads; GPU vs oracle max-abs {err:.2e}")
     return {"value": round(n * wl.q_len / dt, 4), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n} of {wl.batch} sequences (ctx {int(L.seq_lens_host[0])}, all "
-                      f"{wl.n_heads} heads), naive float64 decode, {dt:.1f}s",
+            "sample": f"{n} of {wl.batch} sequences ({tot} cached tokens, {wl.q_len} query "
+                      f"row(s) each, all {wl.n_heads} heads), naive float64 decode, {dt:.1f}s",
             "gpu_vs_oracle_max_abs": err}
 
 

@@ -145,11 +145,14 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t n_new,
                             float* cache_scale, void* workspace,
                             size_t workspace_bytes, void* stream);
 
-/* Split-KV partitions mla_decode_absorbed uses when num_splits == 0: a
- * function of batch and q_len only (the host never reads sequence lengths). */
+/* Split-KV partitions per query row that mla_decode_absorbed uses when
+ * num_splits == 0 on shapes served by the portable kernels: a function of batch
+ * and q_len only (the host never reads sequence lengths).  The DeepSeek-V3
+ * shape (MFMA kernels) uses the balanced schedule for num_splits == 0 instead
+ * (see mla_decode_absorbed). */
 int32_t mla_decode_default_splits(const mla_dims* dims, int32_t batch, int32_t q_len);
 
-/* Workspace bytes mla_decode_absorbed needs.  num_splits 0 = the default. */
+/* Workspace bytes mla_decode_absorbed needs for this num_splits (0 included). */
 mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch,
                                      int32_t q_len, int32_t num_splits,
                                      size_t* bytes);
@@ -174,10 +177,18 @@ enum {
  *  block_table  [batch][max_blocks_per_seq] int32, device
  *  seq_lens     [batch] int32, device: tokens of sequence b, the q_len new
  *               ones included
- *  num_splits   split-KV partitions per (sequence, query row), 0 = default,
- *               at most 256.  Partition k of a row that sees n tokens covers
- *               tokens [k*P, (k+1)*P) with P = ceil(n / (num_splits *
- *               block_size)) * block_size; empty partitions are skipped.
+ *  num_splits   split-KV partitions per (sequence, query row), at most 256.
+ *               Partition k of a row that sees n tokens covers tokens
+ *               [k*P, (k+1)*P) with P = ceil(n / (num_splits * block_size))
+ *               * block_size; empty partitions are skipped.
+ *               0 on the DeepSeek-V3 shape: balanced schedule.  The visible
+ *               64-token tiles of all rows, concatenated in row order, are
+ *               divided into equal contiguous ranges, one per workgroup
+ *               (as many workgroups as compute units, fewer when there are
+ *               fewer tiles); a range may cover parts of several rows, each
+ *               giving one partition.  Ragged batches then keep every compute
+ *               unit equally busy.  0 on other shapes: the default split count
+ *               (mla_decode_default_splits).
  *  out          [batch][q_len][n_heads][v_head_dim] act_dtype
  *  lse          [batch][q_len][n_heads] float or NULL: natural-log
  *               log-sum-exp of the scaled scores (-inf for a row with no token)

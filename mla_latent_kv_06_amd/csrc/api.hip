@@ -79,17 +79,28 @@ struct DecodeWs {
     size_t qbuf, part_o, part_lse, total;
 };
 
-DecodeWs decode_ws(const mla_dims& d, int batch, int q_len, int splits) {
+// Partial slots of the split-KV pass: R * splits with a fixed split count;
+// with balanced scheduling (MFMA shapes, num_splits == 0) one per (workgroup,
+// row) piece, at most kNumCUs + R.
+size_t partial_slots(const mla_dims& d, int batch, int q_len, int num_splits) {
+    const size_t R = (size_t)batch * q_len;
+    if (num_splits > 0) return R * num_splits;
+    if (mla::is_v3_shape(d)) return mla::kNumCUs + R;
+    return R * default_splits(batch, q_len);
+}
+
+DecodeWs decode_ws(const mla_dims& d, int batch, int q_len, int num_splits) {
     const bool mfma = mla::is_v3_shape(d);
     const size_t R = (size_t)batch * q_len, H = d.n_heads;
+    const size_t slots = partial_slots(d, batch, q_len, num_splits);
     DecodeWs w;
     w.qbuf = 0;
     size_t qb = R * H * (d.kv_lora_rank + d.qk_rope_dim) * (mfma ? 2 : 4);
     w.part_o = align_up(qb, 256);
     // partial o_lat: fp16 on the MFMA path (normalised convex combinations of
     // latent rows, stored with 2^-11 relative precision), fp32 otherwise
-    w.part_lse = w.part_o + align_up(R * splits * H * d.kv_lora_rank * (mfma ? 2 : 4), 256);
-    w.total = w.part_lse + align_up(R * splits * H * sizeof(float), 256);
+    w.part_lse = w.part_o + align_up(slots * H * d.kv_lora_rank * (mfma ? 2 : 4), 256);
+    w.total = w.part_lse + align_up(slots * H * sizeof(float), 256);
     return w;
 }
 
@@ -116,7 +127,9 @@ mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const
         return fail(MLA_ERR_BAD_SHAPE, "stages=0x%x: use MLA_STAGE_* bits", stages);
     if (batch == 0) return ok();
     if (max_blocks_per_seq < 1) return fail(MLA_ERR_BAD_SHAPE, "max_blocks_per_seq must be >= 1");
-    const int splits = num_splits == 0 ? default_splits(batch, q_len) : num_splits;
+    // 0: balanced scheduling on the MFMA path, the default split count otherwise
+    const int splits = (num_splits == 0 && !mla::is_v3_shape(d)) ? default_splits(batch, q_len)
+                                                                  : num_splits;
     if ((stages & MLA_STAGE_ABSORB_Q) && (!q_nope || !q_pe || !w_uk))
         return fail(MLA_ERR_NULL_POINTER, "q_nope, q_pe and w_uk are required");
     if ((stages & MLA_STAGE_SPLIT_KV) && (!cache_pool || !block_table || !seq_lens))
@@ -126,7 +139,7 @@ mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const
     if ((stages & MLA_STAGE_COMBINE) && (!w_uv || !out))
         return fail(MLA_ERR_NULL_POINTER, "w_uv and out are required");
     if (!workspace) return fail(MLA_ERR_NULL_POINTER, "workspace is NULL");
-    const DecodeWs ws = decode_ws(d, batch, q_len, splits);
+    const DecodeWs ws = decode_ws(d, batch, q_len, num_splits);
     if (workspace_bytes < ws.total)
         return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu", workspace_bytes, ws.total);
     const bool mfma = mla::is_v3_shape(d);
@@ -282,8 +295,7 @@ mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_
         return fail(MLA_ERR_BAD_SHAPE, "batch=%d q_len=%d", batch, q_len);
     if (num_splits < 0 || num_splits > mla::kMaxSplits)
         return fail(MLA_ERR_BAD_SHAPE, "num_splits=%d outside [0, %d]", num_splits, mla::kMaxSplits);
-    const int splits = num_splits == 0 ? default_splits(batch, q_len) : num_splits;
-    *bytes = decode_ws(*dims, batch, q_len, splits).total;
+    *bytes = decode_ws(*dims, batch, q_len, num_splits).total;
     return ok();
 }
 

@@ -245,6 +245,63 @@ __device__ __forceinline__ void convert_tile_fp8(const lds_u8* lstage, lds_u8* l
     }
 }
 
+// ---------------------------------------------------------------------------
+// work partition of the split-KV pass
+// ---------------------------------------------------------------------------
+//
+// Query row r = b * q_len + s (token s of sequence b) sees the first
+// seq_lens[b] - q_len + s + 1 cache tokens, i.e. tiles(r) 64-token tiles.
+//  - num_splits > 0: row r is cut into num_splits equal ranges of whole tiles,
+//    one workgroup each; partial slot r * num_splits + split.
+//  - num_splits == 0 (balanced): the rows' tiles, concatenated in row order,
+//    are cut into G equal ranges [i T / G, (i+1) T / G), one per workgroup
+//    (T = total tiles, G = min(grid, T), so no range is empty; workgroups
+//    past G have nothing to do).  A range may span several rows; each
+//    (workgroup i, row r) piece writes partial slot i + r.  Slots are unique:
+//    for i < i' the rows of i end no later than the rows of i' begin, so
+//    i + r < i' + r'.  Row r's pieces occupy slots first(r) + r .. last(r) + r,
+//    first / last being the workgroups holding its first / last tile.
+
+__device__ __forceinline__ int row_tiles(const int* __restrict__ seq_lens, int q_len, int r) {
+    const int b = r / q_len;
+    const int n_vis = seq_lens[b] - q_len + (r - b * q_len) + 1;
+    return n_vis > 0 ? (n_vis + BS - 1) / BS : 0;
+}
+
+// Workgroup holding tile t of the concatenated tiles (T tiles over G groups).
+__device__ __forceinline__ int group_of_tile(long long t, long long T, long long G) {
+    return (int)(((t + 1) * G + T - 1) / T - 1);
+}
+
+// Block-wide scan of row tile counts: thread tid owns rows [tid*per, tid*per+per)
+// (per = ceil(R / 256)).  Returns T; *excl / *mine receive the tiles before this
+// thread's rows and in them.  sc: 260 ints of LDS scratch.
+template <typename LdsInt>
+__device__ __forceinline__ int scan_row_tiles(const int* __restrict__ seq_lens, int q_len, int R,
+                                              LdsInt sc, int* excl, int* mine) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int per = (R + 255) / 256;
+    int local = 0;
+    for (int k = 0; k < per; ++k) {
+        const int r = tid * per + k;
+        if (r < R) local += row_tiles(seq_lens, q_len, r);
+    }
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) sc[256 + w] = incl;
+    __syncthreads();
+    int off = 0;
+    for (int k = 0; k < w; ++k) off += sc[256 + k];
+    const int T = sc[256] + sc[257] + sc[258] + sc[259];
+    *excl = off + incl - local;
+    *mine = local;
+    return T;
+}
+
 // Workgroup (row, split): row = b * q_len + s handles query token s of
 // sequence b for all 128 heads over cache tiles [t0, t1) of its visible range.
 // Wave w owns heads 32w .. 32w+31 for the whole tile loop; each 64-token tile
@@ -259,9 +316,9 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const unsigned char* __restrict__ pool,       // [blocks][64][576] bf16 | fp8
     const float* __restrict__ pool_scale,         // [blocks][64] (fp8)
     const int* __restrict__ block_table, int max_blocks,
-    const int* __restrict__ seq_lens, int q_len, int num_splits, float scale_log2,
-    unsigned short* __restrict__ part_o,          // [R][S][H][512] fp16
-    float* __restrict__ part_lse) {               // [R][S][H]
+    const int* __restrict__ seq_lens, int R, int q_len, int num_splits, float scale_log2,
+    unsigned short* __restrict__ part_o,          // [slots][H][512] fp16
+    float* __restrict__ part_lse) {               // [slots][H]
     // bf16: two tiles + the rotary queries of all heads (16 KB) = 160 KiB;
     // fp8: one bf16 tile + two fp8 staging tiles with scales (rotary queries in VGPRs)
     constexpr bool QPE_LDS = !FP8;
@@ -275,260 +332,321 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in an SGPR
     const int l32 = lane & 31, hf = lane >> 5;
-    const int row = blockIdx.x / num_splits;
-    const int split = blockIdx.x - row * num_splits;
-    const int b = row / q_len, s = row - b * q_len;
-    const int n_vis = seq_lens[b] - q_len + s + 1;
-    const int n_tiles = n_vis > 0 ? (n_vis + BS - 1) / BS : 0;
-    const int tps = (n_tiles + num_splits - 1) / num_splits;
-    const int t0 = split * tps;
-    const int t1 = min(n_tiles, t0 + tps);
-    float* lse_dst = part_lse + ((size_t)row * num_splits + split) * H;
-    if (t0 >= t1) {
-        if (tid < H) lse_dst[tid] = kNegInf;
-        return;
-    }
-    const int* btab = block_table + (size_t)b * max_blocks;
     const int head = w * 32 + l32;
 
-    // bf16: tiles at 0 and TILE, rotary queries at 2 TILE.
-    // fp8: the bf16 tile at 0, staging buffers at TILE and TILE + STAGE.
-    lds_u8* qpe = smem + 2 * TILE;
-
-    // this wave's 32 query rows, as MFMA B fragments: lane (hf, l32) holds
-    // channels 16 ks + 8 hf .. +8 of head 32 w + l32
-    bf16x8 qf[NQ];
-    {
-        const unsigned short* qrow = qbuf + ((size_t)row * H + head) * D + hf * 8;
-#pragma unroll
-        for (int ks = 0; ks < NQ; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
-    }
-    if constexpr (QPE_LDS) {
-        // q_pe of all heads: head h's chunk c (8 channels) at h*128 + ((c ^ g(h)) << 4)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = k * 256 + tid;               // 1024 chunks
-            const int h = i >> 3, c = i & 7;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(qbuf + ((size_t)row * H + h) * D + DC + c * 8);
-            *reinterpret_cast<MLA_LDS u32x4*>(qpe + h * 128 + ((c ^ fswz(h & 15)) << 4)) = v;
+    // ---- this workgroup's pieces (row, tiles [t0, t1), partial slot) ---------------
+    int cur_row = 0, cur_rs = 0, rng_a = 0, rng_b = 0;   // balanced: walk state
+    bool fixed_pending = num_splits > 0;
+    if (num_splits == 0) {
+        MLA_LDS int* sc = reinterpret_cast<MLA_LDS int*>(smem);
+        int excl, mine;
+        const int T = scan_row_tiles(seq_lens, q_len, R, sc, &excl, &mine);
+        const long long G = min((long long)gridDim.x, (long long)T);
+        if ((long long)blockIdx.x >= G) return;      // uniform: the whole workgroup leaves
+        rng_a = (int)((long long)blockIdx.x * T / G);
+        rng_b = (int)((long long)(blockIdx.x + 1) * T / G);
+        if (rng_a < rng_b && excl <= rng_a && rng_a < excl + mine) {
+            const int per = (R + 255) / 256;
+            int rs = excl;
+            for (int k = 0; k < per; ++k) {
+                const int r = tid * per + k;
+                const int nt = r < R ? row_tiles(seq_lens, q_len, r) : 0;
+                if (rng_a < rs + nt) {
+                    sc[260] = r;
+                    sc[261] = rs;
+                    break;
+                }
+                rs += nt;
+            }
         }
-    }
-    const lds_u8* qpe_lane = qpe + head * 128;
-    const int qpe_g = fswz(head & 15);
-
-    auto valid_of = [&](int t) { return min(BS, n_vis - t * BS); };
-    // asynchronous load of tile t into `dst` (a bf16 tile, or fp8 staging)
-    auto issue = [&](int t, lds_u8* dst) {
-        const size_t blk = (size_t)btab[t];
-        if constexpr (FP8) {
-            issue_tile_fp8(pool + blk * F8TILE, pool_scale + blk * BS, dst, w, lane);
-        } else {
-            issue_tile_bf16(pool + blk * GTILE, dst, w, lane);
+        __syncthreads();
+        if (rng_a < rng_b) {
+            cur_row = sc[260];
+            cur_rs = sc[261];
         }
+        __syncthreads();                 // scratch read before the tiles reuse it
+    }
+    auto next_piece = [&](int& row, int& t0, int& t1, int& slot) -> bool {
+        if (num_splits > 0) {
+            if (!fixed_pending) return false;
+            fixed_pending = false;
+            row = blockIdx.x / num_splits;
+            const int split = blockIdx.x - row * num_splits;
+            const int n_tiles = row_tiles(seq_lens, q_len, row);
+            const int tps = (n_tiles + num_splits - 1) / num_splits;
+            t0 = split * tps;
+            t1 = min(n_tiles, t0 + tps);
+            slot = blockIdx.x;
+            if (t0 >= t1) {              // nothing visible in this range
+                if (tid < H) part_lse[(size_t)slot * H + tid] = kNegInf;
+                return false;
+            }
+            return true;
+        }
+        while (cur_rs < rng_b && cur_row < R) {
+            const int r = cur_row, rs = cur_rs;
+            const int nt = row_tiles(seq_lens, q_len, r);
+            cur_row += 1;
+            cur_rs += nt;
+            const int lo = max(rng_a, rs) - rs, hi = min(rng_b, rs + nt) - rs;
+            if (hi > lo) {
+                row = r;
+                t0 = lo;
+                t1 = hi;
+                slot = blockIdx.x + r;
+                return true;
+            }
+        }
+        return false;
     };
 
-    // Per-lane LDS byte offsets.  Score operand (chunk 2 ks + hf of row
-    // 32 hb + l32): by ks % 4.  Transposed value reads (in a 16-lane group,
-    // lane 4r + b reads row 4 hf + r (+8), channels 4b .. 4b+3 of a 16-channel
-    // block): by cm % 2 and by the +8 row offset.
-    int qk_off[4], tr_off[2][2];
+    int row, t0, t1, slot;
+    for (int piece = 0; next_piece(row, t0, t1, slot); ++piece) {
+        if (piece > 0) __syncthreads();      // the previous piece's epilogue is done with LDS
+        const int b = row / q_len, s = row - b * q_len;
+        const int n_vis = seq_lens[b] - q_len + s + 1;
+        float* lse_dst = part_lse + (size_t)slot * H;
+        const int* btab = block_table + (size_t)b * max_blocks;
+
+        // bf16: tiles at 0 and TILE, rotary queries at 2 TILE.
+        // fp8: the bf16 tile at 0, staging buffers at TILE and TILE + STAGE.
+        lds_u8* qpe = smem + 2 * TILE;
+
+        // this wave's 32 query rows, as MFMA B fragments: lane (hf, l32) holds
+        // channels 16 ks + 8 hf .. +8 of head 32 w + l32
+        bf16x8 qf[NQ];
+        {
+            const unsigned short* qrow = qbuf + ((size_t)row * H + head) * D + hf * 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qk_off[j] = (l32 * 8 + ((2 * j + hf) ^ fswz(l32 & 15))) * 16;
-    {
-        const int r = (lane & 15) >> 2, g1 = (lane >> 4) & 1, b1 = (lane >> 1) & 1;
+            for (int ks = 0; ks < NQ; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+        }
+        if constexpr (QPE_LDS) {
+            // q_pe of all heads: head h's chunk c (8 channels) at h*128 + ((c ^ g(h)) << 4)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int t = 8 * e + 4 * hf + r;      // row within a 16-row group
-                tr_off[j][e] = (t * 8 + ((4 * j + 2 * g1 + b1) ^ fswz(t))) * 16 + (lane & 1) * 8;
+            for (int k = 0; k < 4; ++k) {
+                const int i = k * 256 + tid;               // 1024 chunks
+                const int h = i >> 3, c = i & 7;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(qbuf + ((size_t)row * H + h) * D + DC + c * 8);
+                *reinterpret_cast<MLA_LDS u32x4*>(qpe + h * 128 + ((c ^ fswz(h & 15)) << 4)) = v;
             }
-    }
+        }
+        const lds_u8* qpe_lane = qpe + head * 128;
+        const int qpe_g = fswz(head & 15);
 
-    // Softmax without rescaling the accumulators: every weight of a pass is
-    // exp2(s - m_ref) for one reference m_ref per head.  The first pass takes
-    // m_ref from the first half-tile; if a later half-tile's maximum exceeds it
-    // by more than kMaxLead (weights stay below 2^64, far from fp32 overflow)
-    // the pass's result is discarded, one scan computes the exact maximum and
-    // a last pass runs with it.  (Scaling O inside the loop would force the
-    // 256 accumulators out of AGPRs.)  The waves vote after the loop, in LDS.
-    constexpr float kMaxLead = 64.0f;
-    f32x16 o[16];
-    float m_ref = kNegInf, l_run = 0.f;
-    bool overflow = false;
-    int mode = 0;                        // 0: first-tile reference, 1: max scan, 2: exact reference
+        auto valid_of = [&](int t) { return min(BS, n_vis - t * BS); };
+        // asynchronous load of tile t into `dst` (a bf16 tile, or fp8 staging)
+        auto issue = [&](int t, lds_u8* dst) {
+            const size_t blk = (size_t)btab[t];
+            if constexpr (FP8) {
+                issue_tile_fp8(pool + blk * F8TILE, pool_scale + blk * BS, dst, w, lane);
+            } else {
+                issue_tile_bf16(pool + blk * GTILE, dst, w, lane);
+            }
+        };
 
-    // One tile: start the load of the next tile into `nxt` (when there is
-    // one), then attend over the 64 cache rows in `tile`.  The two buffers
-    // never overlap; saying so (restrict) lets the compiler keep the
-    // transposed value reads from waiting on the load in flight.
-    auto run_tile = [&](int t, const lds_u8* __restrict__ tile, lds_u8* __restrict__ nxt,
-                        bool has_next) __attribute__((always_inline)) {
-        const int valid = valid_of(t);
-        if (has_next) issue(t + 1, nxt);
+        // Per-lane LDS byte offsets.  Score operand (chunk 2 ks + hf of row
+        // 32 hb + l32): by ks % 4.  Transposed value reads (in a 16-lane group,
+        // lane 4r + b reads row 4 hf + r (+8), channels 4b .. 4b+3 of a 16-channel
+        // block): by cm % 2 and by the +8 row offset.
+        int qk_off[4], tr_off[2][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qk_off[j] = (l32 * 8 + ((2 * j + hf) ^ fswz(l32 & 15))) * 16;
+        {
+            const int r = (lane & 15) >> 2, g1 = (lane >> 4) & 1, b1 = (lane >> 1) & 1;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int t = 8 * e + 4 * hf + r;      // row within a 16-row group
+                    tr_off[j][e] = (t * 8 + ((4 * j + 2 * g1 + b1) ^ fswz(t))) * 16 + (lane & 1) * 8;
+                }
+        }
+
+        // Softmax without rescaling the accumulators: every weight of a pass is
+        // exp2(s - m_ref) for one reference m_ref per head.  The first pass takes
+        // m_ref from the first half-tile; if a later half-tile's maximum exceeds it
+        // by more than kMaxLead (weights stay below 2^64, far from fp32 overflow)
+        // the pass's result is discarded, one scan computes the exact maximum and
+        // a last pass runs with it.  (Scaling O inside the loop would force the
+        // 256 accumulators out of AGPRs.)  The waves vote after the loop, in LDS.
+        constexpr float kMaxLead = 64.0f;
+        f32x16 o[16];
+        float m_ref = kNegInf, l_run = 0.f;
+        bool overflow = false;
+        int mode = 0;                        // 0: first-tile reference, 1: max scan, 2: exact reference
+
+        // One tile: start the load of the next tile into `nxt` (when there is
+        // one), then attend over the 64 cache rows in `tile`.  The two buffers
+        // never overlap; saying so (restrict) lets the compiler keep the
+        // transposed value reads from waiting on the load in flight.
+        auto run_tile = [&](int t, const lds_u8* __restrict__ tile, lds_u8* __restrict__ nxt,
+                            bool has_next) __attribute__((always_inline)) {
+            const int valid = valid_of(t);
+            if (has_next) issue(t + 1, nxt);
 #pragma unroll 1
-        for (int hb = 0; hb < 2; ++hb) {
-            if (hb * 32 >= valid) break;
-            // ---- S^T = K . Q^T: rows 32 hb + l32 -----------------------------------
-            const lds_u8* kbase = tile + hb * 32 * 128;
-            auto ka = [&](int ks) {
-                return *reinterpret_cast<const MLA_LDS bf16x8*>(kbase + qk_off[ks & 3] + (ks >> 2) * 8192);
-            };
-            auto qb = [&](int ks) -> bf16x8 {
-                if (ks < NQ) return qf[ks];
-                const int c = 2 * (ks - 32) + hf;
-                return *reinterpret_cast<const MLA_LDS bf16x8*>(qpe_lane + ((c ^ qpe_g) << 4));
-            };
-            f32x16 sacc = {};
-            bf16x8 a0 = ka(0), a1 = ka(1), a2;
+            for (int hb = 0; hb < 2; ++hb) {
+                if (hb * 32 >= valid) break;
+                // ---- S^T = K . Q^T: rows 32 hb + l32 -----------------------------------
+                const lds_u8* kbase = tile + hb * 32 * 128;
+                auto ka = [&](int ks) {
+                    return *reinterpret_cast<const MLA_LDS bf16x8*>(kbase + qk_off[ks & 3] + (ks >> 2) * 8192);
+                };
+                auto qb = [&](int ks) -> bf16x8 {
+                    if (ks < NQ) return qf[ks];
+                    const int c = 2 * (ks - 32) + hf;
+                    return *reinterpret_cast<const MLA_LDS bf16x8*>(qpe_lane + ((c ^ qpe_g) << 4));
+                };
+                f32x16 sacc = {};
+                bf16x8 a0 = ka(0), a1 = ka(1), a2;
 #pragma unroll
-            for (int ks = 0; ks < 36; ++ks) {
-                if (ks + 2 < 36) a2 = ka(ks + 2);
-                sacc = mfma32(a0, qb(ks), sacc);
-                a0 = a1;
-                a1 = a2;
-            }
-            // lane holds head `head`, tokens 32 hb + 8 (i/4) + 4 hf + (i%4)
-            float sv[16];
+                for (int ks = 0; ks < 36; ++ks) {
+                    if (ks + 2 < 36) a2 = ka(ks + 2);
+                    sacc = mfma32(a0, qb(ks), sacc);
+                    a0 = a1;
+                    a1 = a2;
+                }
+                // lane holds head `head`, tokens 32 hb + 8 (i/4) + 4 hf + (i%4)
+                float sv[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sv[i] = sacc[i] * scale_log2;
-            if (valid < BS) {
+                for (int i = 0; i < 16; ++i) sv[i] = sacc[i] * scale_log2;
+                if (valid < BS) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int tok = hb * 32 + (i >> 2) * 8 + 4 * hf + (i & 3);
-                    if (tok >= valid) sv[i] = kNegInf;
+                    for (int i = 0; i < 16; ++i) {
+                        const int tok = hb * 32 + (i >> 2) * 8 + 4 * hf + (i & 3);
+                        if (tok >= valid) sv[i] = kNegInf;
+                    }
+                }
+                float hmax = sv[0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) hmax = fmaxf(hmax, sv[i]);
+                hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
+                if (mode == 1) {
+                    m_ref = fmaxf(m_ref, hmax);
+                    continue;
+                }
+                if (mode == 0 && t == t0 && hb == 0) m_ref = hmax;
+                // (cannot hold in the exact-reference pass: the scan saw the same
+                // maxima, so at most three passes run)
+                overflow |= hmax > m_ref + kMaxLead;
+
+                float psum = 0.f;
+                bf16x8 pf[2];
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    u16x8 pu;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float pv = __builtin_amdgcn_exp2f(sv[k2 * 8 + j] - m_ref);
+                        psum += pv;
+                        pu[j] = f32_to_bf16_bits(pv);
+                    }
+                    pf[k2] = __builtin_bit_cast(bf16x8, pu);
+                }
+                psum += __shfl_xor(psum, 32, 64);
+                l_run += psum;
+
+                // ---- O^T += V^T . P^T (latent columns of the same rows) -----------------
+                // K-step k2 covers tokens 32 hb + 16 k2 + {0..3, 8..11} (lanes 0-31)
+                // and {4..7, 12..15} (lanes 32-63), matching P's layout.  Fragments
+                // are read one step ahead; k2 runs outermost so that consecutive
+                // MFMAs update different accumulators.
+                auto va = [&](int k2, int cm) {
+                    const lds_u8* vb = tile + (cm >> 1) * 8192 + (hb * 32 + k2 * 16) * 128;
+                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (MLA_LDS bf16x4*)(vb + tr_off[cm & 1][0]));
+                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (MLA_LDS bf16x4*)(vb + tr_off[cm & 1][1]));     // rows +8 are in the offset
+                    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                };
+                bf16x8 v0 = va(0, 0), v1;
+#pragma unroll
+                for (int st = 0; st < 32; ++st) {
+                    const int k2 = st >> 4, cm = st & 15;
+                    if (st + 1 < 32) v1 = va((st + 1) >> 4, (st + 1) & 15);
+                    o[cm] = mfma32(v0, pf[k2], o[cm]);
+                    v0 = v1;
                 }
             }
-            float hmax = sv[0];
+        };
+
+        for (;;) {
 #pragma unroll
-            for (int i = 1; i < 16; ++i) hmax = fmaxf(hmax, sv[i]);
-            hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
-            if (mode == 1) {
-                m_ref = fmaxf(m_ref, hmax);
+            for (int i = 0; i < 16; ++i) o[i] = f32x16{};
+            l_run = 0.f;
+            overflow = false;
+            issue(t0, FP8 ? smem + TILE : smem);
+            for (int t = t0; t < t1; ++t) {
+                const int cur = (t - t0) & 1;
+                wait_vmem_all();
+                __syncthreads();             // tile t landed; previous tile fully consumed
+                const bool has_next = t + 1 < t1;
+                if constexpr (FP8) {
+                    lds_u8* st_cur = smem + TILE + cur * STAGE;
+                    lds_u8* st_nxt = smem + TILE + (cur ^ 1) * STAGE;
+                    convert_tile_fp8(st_cur, smem, tid, valid_of(t));
+                    __syncthreads();
+                    run_tile(t, smem, st_nxt, has_next);
+                } else {
+                    lds_u8* cur_tile = smem + cur * TILE;
+                    lds_u8* nxt_tile = smem + (cur ^ 1) * TILE;
+                    if (valid_of(t) < BS) {  // last, partial tile of the sequence
+                        zero_rows(cur_tile, valid_of(t), tid);
+                        __syncthreads();
+                    }
+                    run_tile(t, cur_tile, nxt_tile, has_next);
+                }
+            }
+            // ---- vote: did any wave's weights run past the reference? ------------------
+            __syncthreads();                 // all waves are done with the tiles
+            MLA_LDS int* votes = reinterpret_cast<MLA_LDS int*>(smem);
+            if (lane == 0) votes[w] = __builtin_amdgcn_ballot_w64(overflow) != 0;
+            __syncthreads();
+            const bool redo = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+            __syncthreads();                 // votes read before the next pass reuses the tiles
+            if (redo) {
+                mode = 1;
+                m_ref = kNegInf;
                 continue;
             }
-            if (mode == 0 && t == t0 && hb == 0) m_ref = hmax;
-            // (cannot hold in the exact-reference pass: the scan saw the same
-            // maxima, so at most three passes run)
-            overflow |= hmax > m_ref + kMaxLead;
-
-            float psum = 0.f;
-            bf16x8 pf[2];
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                u16x8 pu;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float pv = __builtin_amdgcn_exp2f(sv[k2 * 8 + j] - m_ref);
-                    psum += pv;
-                    pu[j] = f32_to_bf16_bits(pv);
-                }
-                pf[k2] = __builtin_bit_cast(bf16x8, pu);
+            if (mode == 1) {
+                mode = 2;
+                continue;
             }
-            psum += __shfl_xor(psum, 32, 64);
-            l_run += psum;
+            break;
+        }
 
-            // ---- O^T += V^T . P^T (latent columns of the same rows) -----------------
-            // K-step k2 covers tokens 32 hb + 16 k2 + {0..3, 8..11} (lanes 0-31)
-            // and {4..7, 12..15} (lanes 32-63), matching P's layout.  Fragments
-            // are read one step ahead; k2 runs outermost so that consecutive
-            // MFMAs update different accumulators.
-            auto va = [&](int k2, int cm) {
-                const lds_u8* vb = tile + (cm >> 1) * 8192 + (hb * 32 + k2 * 16) * 128;
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (MLA_LDS bf16x4*)(vb + tr_off[cm & 1][0]));
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (MLA_LDS bf16x4*)(vb + tr_off[cm & 1][1]));     // rows +8 are in the offset
-                return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            };
-            bf16x8 v0 = va(0, 0), v1;
+        // ---- epilogue: normalised partial o_lat (fp16) and log-sum-exp ---------------
+        // The partial is a convex combination of latent rows: fp16 keeps it to
+        // 2^-11 relative and halves the bytes every workgroup writes at the same
+        // moment (and the combine reads).  A lane holds 16-byte pieces of 32
+        // different head rows, so each wave transposes through its own LDS region
+        // (the tiles are free after the vote barrier) and writes every head row as
+        // one 1 KB store.  Row stride 520 halves: the 8-byte writes of 16
+        // consecutive lanes (16 head rows) fall on distinct banks.  Waves start
+        // at different rows so that concurrent stores spread over memory channels.
+        constexpr int OSTR = 520;
+        const float inv_l = 1.0f / l_run;
+        MLA_LDS unsigned short* ost = reinterpret_cast<MLA_LDS unsigned short*>(smem + w * (32 * OSTR * 2));
 #pragma unroll
-            for (int st = 0; st < 32; ++st) {
-                const int k2 = st >> 4, cm = st & 15;
-                if (st + 1 < 32) v1 = va((st + 1) >> 4, (st + 1) & 15);
-                o[cm] = mfma32(v0, pf[k2], o[cm]);
-                v0 = v1;
-            }
-        }
-    };
-
-    for (;;) {
+        for (int cm = 0; cm < 16; ++cm)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[i] = f32x16{};
-        l_run = 0.f;
-        overflow = false;
-        issue(t0, FP8 ? smem + TILE : smem);
-        for (int t = t0; t < t1; ++t) {
-            const int cur = (t - t0) & 1;
-            wait_vmem_all();
-            __syncthreads();             // tile t landed; previous tile fully consumed
-            const bool has_next = t + 1 < t1;
-            if constexpr (FP8) {
-                lds_u8* st_cur = smem + TILE + cur * STAGE;
-                lds_u8* st_nxt = smem + TILE + (cur ^ 1) * STAGE;
-                convert_tile_fp8(st_cur, smem, tid, valid_of(t));
-                __syncthreads();
-                run_tile(t, smem, st_nxt, has_next);
-            } else {
-                lds_u8* cur_tile = smem + cur * TILE;
-                lds_u8* nxt_tile = smem + (cur ^ 1) * TILE;
-                if (valid_of(t) < BS) {  // last, partial tile of the sequence
-                    zero_rows(cur_tile, valid_of(t), tid);
-                    __syncthreads();
-                }
-                run_tile(t, cur_tile, nxt_tile, has_next);
+            for (int g = 0; g < 4; ++g) {
+                u16x4 hv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) hv[j] = f32_to_f16_bits(o[cm][4 * g + j] * inv_l);
+                *reinterpret_cast<MLA_LDS u16x4*>(ost + l32 * OSTR + cm * 32 + g * 8 + 4 * hf) = hv;
             }
+        // LDS operations of one wave complete in order: the reads see the writes
+        unsigned short* po = part_o + ((size_t)slot * H + w * 32) * DC + lane * 8;
+        const int rot = (blockIdx.x * 4 + w) & 31;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int hh = (i + rot) & 31;
+            const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(ost + hh * OSTR + lane * 8);
+            *reinterpret_cast<u32x4*>(po + hh * DC) = v;
         }
-        // ---- vote: did any wave's weights run past the reference? ------------------
-        __syncthreads();                 // all waves are done with the tiles
-        MLA_LDS int* votes = reinterpret_cast<MLA_LDS int*>(smem);
-        if (lane == 0) votes[w] = __builtin_amdgcn_ballot_w64(overflow) != 0;
-        __syncthreads();
-        const bool redo = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
-        __syncthreads();                 // votes read before the next pass reuses the tiles
-        if (redo) {
-            mode = 1;
-            m_ref = kNegInf;
-            continue;
-        }
-        if (mode == 1) {
-            mode = 2;
-            continue;
-        }
-        break;
+        if (hf == 0) lse_dst[head] = (m_ref + __builtin_log2f(l_run)) * kLn2;
     }
-
-    // ---- epilogue: normalised partial o_lat (fp16) and log-sum-exp ---------------
-    // The partial is a convex combination of latent rows: fp16 keeps it to
-    // 2^-11 relative and halves the bytes every workgroup writes at the same
-    // moment (and the combine reads).  A lane holds 16-byte pieces of 32
-    // different head rows, so each wave transposes through its own LDS region
-    // (the tiles are free after the vote barrier) and writes every head row as
-    // one 1 KB store.  Row stride 520 halves: the 8-byte writes of 16
-    // consecutive lanes (16 head rows) fall on distinct banks.  Waves start
-    // at different rows so that concurrent stores spread over memory channels.
-    constexpr int OSTR = 520;
-    const float inv_l = 1.0f / l_run;
-    MLA_LDS unsigned short* ost = reinterpret_cast<MLA_LDS unsigned short*>(smem + w * (32 * OSTR * 2));
-#pragma unroll
-    for (int cm = 0; cm < 16; ++cm)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            u16x4 hv;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) hv[j] = f32_to_f16_bits(o[cm][4 * g + j] * inv_l);
-            *reinterpret_cast<MLA_LDS u16x4*>(ost + l32 * OSTR + cm * 32 + g * 8 + 4 * hf) = hv;
-        }
-    // LDS operations of one wave complete in order: the reads see the writes
-    unsigned short* po = part_o + (((size_t)row * num_splits + split) * H + w * 32) * DC + lane * 8;
-    const int rot = (blockIdx.x * 4 + w) & 31;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const int hh = (i + rot) & 31;
-        const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(ost + hh * OSTR + lane * 8);
-        *reinterpret_cast<u32x4*>(po + hh * DC) = v;
-    }
-    if (hf == 0) lse_dst[head] = (m_ref + __builtin_log2f(l_run)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -542,8 +660,9 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
 // loads together (partition weights, then all partitions of 8 rows, then the
 // whole W_UV slice) so each costs about one memory round trip.
 __global__ __launch_bounds__(256) void combine_kernel(
-    const unsigned short* __restrict__ part_o,  // [R][S][H][512] fp16
-    const float* __restrict__ part_lse, int R, int num_splits,
+    const unsigned short* __restrict__ part_o,  // [slots][H][512] fp16
+    const float* __restrict__ part_lse,         // [slots][H]
+    const int* __restrict__ seq_lens, int q_len, int R, int num_splits, int groups,
     const unsigned short* __restrict__ w_uv,    // [H][128][512]
     unsigned short* __restrict__ out,           // [R][H][128] bf16
     float* __restrict__ lse_out) {              // [R][H] or null
@@ -554,19 +673,54 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in an SGPR
     const int l32 = lane & 31, hf = lane >> 5;
-    const int S = num_splits;
+    __shared__ int pbase[32], pcnt[32];         // partial slots of each local row
+
+    // ---- where each row's partials are (see the split-KV work partition)
+    if (num_splits > 0) {
+        if (tid < 32) {
+            const bool in = rb * 32 + tid < R;
+            pbase[tid] = in ? (rb * 32 + tid) * num_splits : 0;
+            pcnt[tid] = in ? num_splits : 0;
+        }
+    } else {
+        int* sc = reinterpret_cast<int*>(&wts[0][0]);
+        int excl, mine;
+        const int T = scan_row_tiles(seq_lens, q_len, R, sc, &excl, &mine);
+        const int per = (R + 255) / 256;
+        int rs = excl;
+        for (int k = 0; k < per; ++k) {
+            const int r = tid * per + k;
+            if (r >= R) break;
+            const int nt = row_tiles(seq_lens, q_len, r);
+            if (r >= rb * 32 && r < rb * 32 + 32) {
+                const int G = min(groups, T);
+                const int f = nt > 0 ? group_of_tile(rs, T, G) : 0;
+                const int l = nt > 0 ? group_of_tile(rs + nt - 1, T, G) : -1;
+                pbase[r - rb * 32] = f + r;
+                pcnt[r - rb * 32] = l - f + 1;
+            }
+            rs += nt;
+        }
+        if (tid < 32 && rb * 32 + tid >= R) {
+            pbase[tid] = 0;
+            pcnt[tid] = 0;
+        }
+    }
+    __syncthreads();
 
     // ---- partition weights exp(lse_s - max) / sum and the merged lse; lanes
-    // run over partitions (S <= 256 = 4 x 64)
+    // run over partitions (at most 256 = 4 x 64)
+    int S = 0;                                  // most partials of this wave's rows
     {
         float lv[8][4];
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
-            const int r = rb * 32 + w * 8 + rr;
+            const int base = pbase[w * 8 + rr], cnt = pcnt[w * 8 + rr];
+            S = max(S, cnt);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int sp = lane + 64 * j;
-                lv[rr][j] = (r < R && sp < S) ? part_lse[((size_t)r * S + sp) * H + h] : kNegInf;
+                lv[rr][j] = sp < cnt ? part_lse[((size_t)base + sp) * H + h] : kNegInf;
             }
         }
 #pragma unroll
@@ -583,7 +737,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
             const float inv = tot > 0.f ? 1.0f / tot : 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (lane + 64 * j < S) wts[rl][lane + 64 * j] = e[j] * inv;
+                if (lane + 64 * j < kMaxSplits) wts[rl][lane + 64 * j] = e[j] * inv;
             if (lse_out != nullptr && lane == 0 && r < R)
                 lse_out[(size_t)r * H + h] = (mx == kNegInf) ? kNegInf : mx + __logf(tot);
         }
@@ -599,14 +753,15 @@ __global__ __launch_bounds__(256) void combine_kernel(
     for (int rr = 0; rr < 8; ++rr)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[rr][j] = 0.f;
-    const unsigned short* pbase = part_o + (size_t)h * DC + lane * 8;
+    const unsigned short* pcol = part_o + (size_t)h * DC + lane * 8;
 #pragma unroll 2
     for (int sp = 0; sp < S; ++sp) {
         u32x4 v[8];
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
-            const int r = min(rb * 32 + w * 8 + rr, R - 1);      // rows past R: weight 0
-            v[rr] = *reinterpret_cast<const u32x4*>(pbase + ((size_t)r * S + sp) * H * DC);
+            // past a row's last partial the weight is 0: read its first one
+            const int sl = pbase[w * 8 + rr] + (sp < pcnt[w * 8 + rr] ? sp : 0);
+            v[rr] = *reinterpret_cast<const u32x4*>(pcol + (size_t)sl * H * DC);
         }
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
@@ -687,17 +842,18 @@ hipError_t launch_decode_mfma(const DecodeLaunch& a, unsigned stages) {
         if (e != hipSuccess) return e;
     }
     if (stages & MLA_STAGE_SPLIT_KV) {
-        const int grid = R * a.num_splits;
+        // balanced scheduling: one workgroup per compute unit
+        const int grid = a.num_splits > 0 ? R * a.num_splits : kNumCUs;
         const float scale_log2 = a.scale * kLog2e;
         if (a.cache_dtype == MLA_FP8_E4M3) {
             split_kv_kernel<true><<<grid, 256, 0, a.stream>>>(
                 qbuf, static_cast<const unsigned char*>(a.pool), a.pool_scale, a.block_table,
-                a.max_blocks, a.seq_lens, a.q_len, a.num_splits, scale_log2,
+                a.max_blocks, a.seq_lens, R, a.q_len, a.num_splits, scale_log2,
                 static_cast<unsigned short*>(a.part_o), a.part_lse);
         } else {
             split_kv_kernel<false><<<grid, 256, 0, a.stream>>>(
                 qbuf, static_cast<const unsigned char*>(a.pool), nullptr, a.block_table,
-                a.max_blocks, a.seq_lens, a.q_len, a.num_splits, scale_log2,
+                a.max_blocks, a.seq_lens, R, a.q_len, a.num_splits, scale_log2,
                 static_cast<unsigned short*>(a.part_o), a.part_lse);
         }
         hipError_t e = hipGetLastError();
@@ -706,7 +862,8 @@ hipError_t launch_decode_mfma(const DecodeLaunch& a, unsigned stages) {
     if (stages & MLA_STAGE_COMBINE) {
         const int grid = H * ((R + 31) / 32);
         combine_kernel<<<grid, 256, 0, a.stream>>>(static_cast<const unsigned short*>(a.part_o),
-                                                   a.part_lse, R, a.num_splits,
+                                                   a.part_lse, a.seq_lens, a.q_len, R, a.num_splits,
+                                                   kNumCUs,
                                                    static_cast<const unsigned short*>(a.w_uv),
                                                    static_cast<unsigned short*>(a.out), a.lse);
         hipError_t e = hipGetLastError();

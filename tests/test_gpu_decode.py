@@ -141,19 +141,38 @@ def test_mid_bf16_two_queries():
     check(out, ref, "bf16", lse, ref_lse, "v3_mid_q2")
 
 
+@pytest.mark.parametrize("splits", [4, 0])
 @pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 128, 129])
-def test_edge_lengths(L):
+def test_edge_lengths(L, splits):
     """Single-token caches, exact block multiples and one-token tails; with
-    q_len 2, L = 1 gives a first row that sees no token (zeros, lse -inf)."""
+    q_len 2, L = 1 gives a first row that sees no token (zeros, lse -inf).
+    splits 0 is the balanced schedule (here fewer tiles than workgroups)."""
     for q_len in (1, 2):
         wl = MID.replace(name="v3_edge", batch=2, q_len=q_len)
-        announce("v3_edge", "L", L, "q_len", q_len)
+        announce("v3_edge", "L", L, "q_len", q_len, "splits", splits)
         case = build_case(wl, seq_lens_override=[L, L + 3])
-        _, out, lse = run(case, num_splits=4)
+        _, out, lse = run(case, num_splits=splits)
         ref, ref_lse = case.oracle_decode()
         vis = np.isfinite(ref_lse)
         check(out[vis], ref[vis], "bf16", lse[vis], ref_lse[vis], f"edge L={L} q={q_len}")
         assert np.all(out[~vis] == 0) and np.all(np.isneginf(lse[~vis]))
+
+
+@pytest.mark.parametrize("q_len,lo,hi,batch", [(1, 64, 700, 100), (2, 1, 300, 40)])
+def test_balanced_schedule_ragged(q_len, lo, hi, batch):
+    """Balanced scheduling (num_splits 0): the concatenated tiles of all rows
+    are cut into equal ranges, so workgroups cover several short rows or
+    pieces of rows.  Every row is checked against the oracle on 8 heads."""
+    wl = MID.replace(name="v3_balanced", batch=batch, q_len=q_len, ctx_lo=lo, ctx_hi=hi)
+    announce("v3_balanced", "q_len", q_len, "batch", batch, "ctx", lo, hi)
+    case = build_case(wl)
+    _, out, lse = run(case, num_splits=0)
+    heads = np.arange(5, 128, 16)
+    ref, ref_lse = case.oracle_decode(heads=heads)
+    got, got_lse = out[:, :, heads], lse[:, :, heads]
+    vis = np.isfinite(ref_lse)
+    check(got[vis], ref[vis], "bf16", got_lse[vis], ref_lse[vis], f"v3_balanced q_len={q_len}")
+    assert np.all(got[~vis] == 0) and np.all(np.isneginf(got_lse[~vis]))
 
 
 def test_softmax_reference_restart():
@@ -194,16 +213,18 @@ def test_permuted_and_contiguous_tables_bitwise_equal():
 def test_deterministic_and_split_invariant():
     wl = W["v3_b4_ctx128k_split32_bf16"].replace(name="v3_long", batch=2, ctx_lo=20000,
                                                  ctx_hi=20000)
-    announce("v3_long", "splits 1 / 8 / 32")
+    announce("v3_long", "splits 1 / 8 / 32 / balanced")
     case = build_case(wl)
     dc = G().DeviceCase(case)
     res = {}
-    for s in (1, 8, 32):
+    for s in (1, 8, 32, 0):
         o, l = dc.decode(num_splits=s)
         res[s] = (G().to_np(o), G().to_np(l))
     o2, l2 = dc.decode(num_splits=32)
     assert np.array_equal(G().to_np(o2), res[32][0])
-    for s in (1, 8):
+    o0, _ = dc.decode(num_splits=0)
+    assert np.array_equal(G().to_np(o0), res[0][0])
+    for s in (1, 8, 0):
         d = np.max(np.abs(res[s][0] - res[32][0]))
         assert d <= 2e-3, (s, d)
     ref, ref_lse = case.oracle_decode(heads=np.arange(0, 128, 37))
