@@ -79,92 +79,119 @@ __global__ __launch_bounds__(256) void append_gemm_generic(const void* __restric
     part[i] = acc;
 }
 
-// grid: T tokens, 256 threads.
+// grid: T tokens, 256 threads.  Dout = DC + DR <= 1280 (dims are validated).
+//
+// Everything that does not depend on the projection is started first so that
+// its latency overlaps the partial loads: the token's position and cache
+// slot, gamma, and the rotary sine / cosine.  RoPE turns pairs (x[2k],
+// x[2k+1]) by pos * base^(-2k/R); the angle needs double precision (at
+// position 2^17 an fp32 angle is off by up to 1/64 rad), so it is formed in
+// double, reduced modulo 2 pi with one fma against the double nearest 2 pi
+// (error below 1e-11 rad for positions under 2^20), and its fp32 sin / cos
+// taken.  The split-K partials are summed chunk by chunk in increasing order.
 template <int ADT, int CDT>
 __global__ __launch_bounds__(256) void append_finalize(
     const float* __restrict__ part, int kc_count, int T, int DC, int DR,
     const void* __restrict__ gamma, float eps, float rope_base,
     const int* __restrict__ block_table, int max_blocks, const int* __restrict__ start_pos,
     int n_new, int BSZ, void* __restrict__ pool, float* __restrict__ pool_scale) {
-    __shared__ float y[2048];
+    __shared__ float y[1280];
+    __shared__ float rsn[128], rcs[128];
     __shared__ float red[16];
-    const int t = blockIdx.x;
+    const int t = blockIdx.x, tid = threadIdx.x;
     const int Dout = DC + DR;
-    float ss = 0.f;
-    // Sum of the split-K partials, chunk by chunk in increasing order.  Common
-    // shapes (Dout <= 768, kc_count <= 32) issue every load of the thread
-    // before the first add, so the sum costs one memory round trip.
+    const int b = t / n_new;
+    const int pos = start_pos[b] + (t - b * n_new);
+    const size_t phys = (size_t)block_table[(size_t)b * max_blocks + pos / BSZ] * BSZ + pos % BSZ;
+
+    // Loads below are unconditional, at clamped (valid) addresses, with the
+    // unused values selected away afterwards: a load under a branch would be
+    // waited for inside that branch, one round trip each.
+    constexpr int U = 5;                        // outputs per thread: o = tid + 256 u
+    float gm[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int o = tid + 256 * u;
+        gm[u] = load_act<ADT>(gamma, min(o, DC - 1)) * (o < DC ? 1.f : 0.f);
+    }
+    float x[U];
     if (Dout <= 3 * 256 && kc_count <= 32) {
+        // common shapes: every partial load of the thread is in flight at once
         float pv[3][32];
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
-            const int o = threadIdx.x + u * 256;
+            const int o = tid + 256 * u;
+            // (clamped reads are finite partial sums: a 0 / 1 factor drops them)
+            const float keep_o = o < Dout ? 1.f : 0.f;
 #pragma unroll
-            for (int kc = 0; kc < 32; ++kc)
-                pv[u][kc] = (o < Dout && kc < kc_count) ? part[((size_t)kc * T + t) * Dout + o] : 0.f;
+            for (int kc = 0; kc < 32; ++kc) {
+                const float v = part[((size_t)min(kc, kc_count - 1) * T + t) * Dout + min(o, Dout - 1)];
+                pv[u][kc] = v * (kc < kc_count ? keep_o : 0.f);
+            }
         }
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
-            const int o = threadIdx.x + u * 256;
-            float x = 0.f;
+            x[u] = 0.f;
 #pragma unroll
-            for (int kc = 0; kc < 32; ++kc) x += pv[u][kc];
-            if (o < Dout) {
-                y[o] = x;
-                if (o < DC) ss += x * x;
-            }
+            for (int kc = 0; kc < 32; ++kc) x[u] += pv[u][kc];
         }
+        x[3] = x[4] = 0.f;
     } else {
-        for (int o = threadIdx.x; o < Dout; o += 256) {
-            float x = 0.f;
-            for (int kc = 0; kc < kc_count; ++kc) x += part[((size_t)kc * T + t) * Dout + o];
-            y[o] = x;
-            if (o < DC) ss += x * x;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int o = tid + 256 * u;
+            x[u] = 0.f;
+            if (o < Dout)
+                for (int kc = 0; kc < kc_count; ++kc) x[u] += part[((size_t)kc * T + t) * Dout + o];
         }
     }
-    ss = block_sum(ss, red);                      // also publishes y[]
+    if (tid < DR / 2) {
+        const double ang = (double)pos * pow((double)rope_base, -2.0 * tid / (double)DR);
+        const double turns = rint(ang * 0.15915494309189535);
+        sincosf((float)fma(-turns, 6.283185307179586, ang), &rsn[tid], &rcs[tid]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int o = tid + 256 * u;
+        if (o < Dout) y[o] = x[u];
+        if (o < DC) ss += x[u] * x[u];
+    }
+    ss = block_sum(ss, red);                    // also publishes y[], rsn[], rcs[]
     const float inv = 1.0f / sqrtf(ss / (float)DC + eps);
-    const int b = t / n_new;
-    const int pos = start_pos[b] + (t - b * n_new);
-    // RoPE pairs (x[2k], x[2k+1]); angle pos * base^(-2k/R) in double
-    float yo[8];
-    int cnt = 0;
-    for (int o = threadIdx.x; o < Dout; o += 256, ++cnt) {
-        float v;
+    float yo[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int o = tid + 256 * u;
         if (o < DC) {
-            v = y[o] * inv * load_act<ADT>(gamma, o);
-        } else {
+            yo[u] = x[u] * inv * gm[u];
+        } else if (o < Dout) {
             const int k = (o - DC) >> 1;
-            // The angle needs double precision (at position 2^17 an fp32 angle
-            // is off by up to 1/64 rad): form it in double, reduce it modulo
-            // 2 pi with one fma against the double nearest 2 pi (error below
-            // 1e-11 rad for positions under 2^20), then take fp32 sin / cos of
-            // the reduced angle.
-            const double ang = (double)pos * pow((double)rope_base, -2.0 * k / (double)DR);
-            const double turns = rint(ang * 0.15915494309189535);
-            const float red = (float)fma(-turns, 6.283185307179586, ang);
-            float sn, cs;
-            sincosf(red, &sn, &cs);
             const float x0 = y[DC + 2 * k], x1 = y[DC + 2 * k + 1];
-            v = ((o - DC) & 1) ? x0 * sn + x1 * cs : x0 * cs - x1 * sn;
+            yo[u] = ((o - DC) & 1) ? x0 * rsn[k] + x1 * rcs[k] : x0 * rcs[k] - x1 * rsn[k];
+        } else {
+            yo[u] = 0.f;
         }
-        yo[cnt] = v;
     }
-    const size_t phys = (size_t)block_table[(size_t)b * max_blocks + pos / BSZ] * BSZ + pos % BSZ;
     if constexpr (CDT == MLA_FP8_E4M3) {
         float amax = 0.f;
-        cnt = 0;
-        for (int o = threadIdx.x; o < Dout; o += 256, ++cnt) amax = fmaxf(amax, fabsf(yo[cnt]));
+#pragma unroll
+        for (int u = 0; u < U; ++u) amax = fmaxf(amax, fabsf(yo[u]));
         amax = block_max(amax, red);
         const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
         unsigned char* dst = static_cast<unsigned char*>(pool) + phys * Dout;
-        cnt = 0;
-        for (int o = threadIdx.x; o < Dout; o += 256, ++cnt)
-            dst[o] = static_cast<unsigned char>(f32_to_e4m3_rne_sat(yo[cnt] / sc));
-        if (threadIdx.x == 0) pool_scale[phys] = sc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int o = tid + 256 * u;
+            if (o < Dout) dst[o] = static_cast<unsigned char>(f32_to_e4m3_rne_sat(yo[u] / sc));
+        }
+        if (tid == 0) pool_scale[phys] = sc;
     } else {
-        cnt = 0;
-        for (int o = threadIdx.x; o < Dout; o += 256, ++cnt) store_act<CDT>(pool, phys * Dout + o, yo[cnt]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int o = tid + 256 * u;
+            if (o < Dout) store_act<CDT>(pool, phys * Dout + o, yo[u]);
+        }
     }
 }
 

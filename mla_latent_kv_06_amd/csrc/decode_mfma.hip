@@ -74,9 +74,12 @@ __device__ __forceinline__ void wait_vmem_all() {
 
 // grid: H * 4 * ceil(R / 64) workgroups of 256 threads.  Workgroup (h, cb, rb)
 // produces q_lat[rb*64 .. +64][h][cb*128 .. +128]: q_lat^T = W_UK[h]^T q_nope^T
-// with W_UK[h][:, cb*128 .. +128] staged in LDS (row stride padded to 264 B so
-// the transposed reads of two half-waves fall in different banks).
-constexpr int WT_STRIDE = 132;  // ushorts per staged W_UK row
+// with W_UK[h][:, cb*128 .. +128] staged in LDS as [n][col] rows of 288 bytes
+// (256 + 32 of padding).  The MFMA A operand (32 latent columns x 16 n) is
+// read with the transposing ds_read_b64_tr_b16: a 16-lane group reads 4 rows
+// x 16 columns and each lane receives one column's 4 values; the padding puts
+// the 4 rows of a group on disjoint banks.
+constexpr int WT_ROWB = 288;    // bytes per staged W_UK row
 
 __global__ __launch_bounds__(256) void absorb_q_kernel(
     const unsigned short* __restrict__ q_nope,  // [R][H][128]
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
     const unsigned short* __restrict__ w_uk,    // [H][128][512]
     unsigned short* __restrict__ qbuf,          // [R][H][576]
     int R) {
-    __shared__ __attribute__((aligned(16))) unsigned short wt[128 * WT_STRIDE];
+    __shared__ __attribute__((aligned(16))) unsigned char wt[128 * WT_ROWB];
     const int bid = blockIdx.x;
     const int h = bid % H;
     const int cb = (bid / H) & 3;
@@ -93,18 +96,12 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in an SGPR
     const int l32 = lane & 31, hf = lane >> 5;
 
-    {   // stage W_UK[h][n][cb*128 .. +128]: thread -> (n = tid/2, 64 columns)
-        const int n = tid >> 1, half = tid & 1;
-        const unsigned short* src = w_uk + ((size_t)h * 128 + n) * DC + cb * 128 + half * 64;
-        unsigned short* dst = wt + n * WT_STRIDE + half * 64;
+    // W_UK[h][n][cb*128 .. +128]: 128 rows x 16 chunks of 16 B, 8 per thread
+    u32x4 wv[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            u32x4 v = *reinterpret_cast<const u32x4*>(src + k * 8);
-            *reinterpret_cast<unsigned long long*>(dst + k * 8) =
-                (unsigned long long)v[0] | ((unsigned long long)v[1] << 32);
-            *reinterpret_cast<unsigned long long*>(dst + k * 8 + 4) =
-                (unsigned long long)v[2] | ((unsigned long long)v[3] << 32);
-        }
+    for (int k = 0; k < 8; ++k) {
+        const int i = k * 256 + tid, n = i >> 4, c = i & 15;
+        wv[k] = *reinterpret_cast<const u32x4*>(w_uk + ((size_t)h * 128 + n) * DC + cb * 128 + c * 8);
     }
     // this wave's q_nope fragments (B operands), loaded together with W_UK
     bf16x8 qv[8][2];
@@ -127,34 +124,54 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
             }
         }
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int i = k * 256 + tid, n = i >> 4, c = i & 15;
+        *reinterpret_cast<u32x4*>(wt + n * WT_ROWB + c * 16) = wv[k];
+    }
     __syncthreads();
 
+    // A fragment of K-step ks: lane (hf, l32) needs column w*32 + l32 at
+    // n = 16 ks + 8 hf .. +8.  16-lane group g = lane / 16 covers columns
+    // 16 (g & 1) .. +16 of this wave's 32 and n offset 8 (g >> 1); lane
+    // 4 r + b of a group points at row r, columns 4 b .. 4 b + 3.
+    const int g = lane >> 4, r4 = (lane & 15) >> 2, b4 = lane & 3;
+    const int a_off = (8 * (g >> 1) + r4) * WT_ROWB + (w * 32 + 16 * (g & 1) + 4 * b4) * 2;
     f32x16 acc[2] = {};
-    const int cl = w * 32 + l32;                       // local latent column (M)
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {                   // K = n, 16 per step
-        bf16x8 a;
-        u16x8 au;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) au[j] = wt[(ks * 16 + hf * 8 + j) * WT_STRIDE + cl];
-        a = __builtin_bit_cast(bf16x8, au);
+        const unsigned char* base = wt + ks * 16 * WT_ROWB + a_off;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(base));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(base + 4 * WT_ROWB));
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a, qv[ks][nb], acc[nb]);
     }
+    // The output tile (64 query rows x 128 latent columns) goes through LDS so
+    // that each row's 256-byte segment is written by one contiguous store:
+    // from the accumulators a lane holds 8-byte pieces of 32 different rows.
+    constexpr int OROWB = 272;                  // bytes per staged output row
+    __syncthreads();                            // every wave is done reading W_UK
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int r = rb * 64 + nb * 32 + l32;
-        if (r >= R) continue;
-        unsigned short* dst = qbuf + ((size_t)r * H + h) * D + cb * 128 + w * 32 + 4 * hf;
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int gg = 0; gg < 4; ++gg) {
             const unsigned long long pk =
-                (unsigned long long)f32_to_bf16_bits(acc[nb][4 * g + 0]) |
-                ((unsigned long long)f32_to_bf16_bits(acc[nb][4 * g + 1]) << 16) |
-                ((unsigned long long)f32_to_bf16_bits(acc[nb][4 * g + 2]) << 32) |
-                ((unsigned long long)f32_to_bf16_bits(acc[nb][4 * g + 3]) << 48);
-            *reinterpret_cast<unsigned long long*>(dst + 8 * g) = pk;
+                (unsigned long long)f32_to_bf16_bits(acc[nb][4 * gg + 0]) |
+                ((unsigned long long)f32_to_bf16_bits(acc[nb][4 * gg + 1]) << 16) |
+                ((unsigned long long)f32_to_bf16_bits(acc[nb][4 * gg + 2]) << 32) |
+                ((unsigned long long)f32_to_bf16_bits(acc[nb][4 * gg + 3]) << 48);
+            *reinterpret_cast<unsigned long long*>(
+                wt + (nb * 32 + l32) * OROWB + (w * 32 + 8 * gg + 4 * hf) * 2) = pk;
         }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {               // 64 rows x 16 chunks, 4 per thread
+        const int i = k * 256 + tid, rl = i >> 4, c = i & 15;
+        const int r = rb * 64 + rl;
+        if (r < R)
+            *reinterpret_cast<u32x4*>(qbuf + ((size_t)r * H + h) * D + cb * 128 + c * 8) =
+                *reinterpret_cast<const u32x4*>(wt + rl * OROWB + c * 16);
     }
 }
 
@@ -806,18 +823,28 @@ __global__ __launch_bounds__(256) void combine_kernel(
         oacc = mfma32(wa[ks], bh, oacc);
         oacc = mfma32(wa[ks], bl, oacc);
     }
-    const int r = rb * 32 + l32;
-    if (r < R) {
-        unsigned short* dst = out + ((size_t)r * H + h) * 128 + w * 32 + 4 * hf;
+    // out rows (32 rows x 128 values of head h) through LDS, so that each
+    // row's 256-byte segment is one contiguous store (a lane holds 8-byte
+    // pieces of 32 different rows)
+    constexpr int OROWB = 272;                  // bytes per staged output row
+    __syncthreads();                            // every wave is done reading o_lat
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const unsigned long long pk =
-                (unsigned long long)f32_to_bf16_bits(oacc[4 * g + 0]) |
-                ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 1]) << 16) |
-                ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 2]) << 32) |
-                ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 3]) << 48);
-            *reinterpret_cast<unsigned long long*>(dst + 8 * g) = pk;
-        }
+    for (int g = 0; g < 4; ++g) {
+        const unsigned long long pk =
+            (unsigned long long)f32_to_bf16_bits(oacc[4 * g + 0]) |
+            ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 1]) << 16) |
+            ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 2]) << 32) |
+            ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 3]) << 48);
+        *reinterpret_cast<unsigned long long*>(&ol[0][l32 * OROWB + (w * 32 + 8 * g + 4 * hf) * 2]) = pk;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {               // 32 rows x 16 chunks, 2 per thread
+        const int i = k * 256 + tid, rl = i >> 4, c = i & 15;
+        const int r = rb * 32 + rl;
+        if (r < R)
+            *reinterpret_cast<u32x4*>(out + ((size_t)r * H + h) * 128 + c * 8) =
+                *reinterpret_cast<const u32x4*>(&ol[0][rl * OROWB + c * 16]);
     }
 }
 
