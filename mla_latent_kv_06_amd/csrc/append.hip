@@ -19,9 +19,10 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // One wave per (32 outputs, 32 tokens, K chunk of at most kAppendChunk):
 //   part[kc][t][o] = sum_{d in chunk} W[o][d] h[t][d]
-// as x^T = W . h^T with both operands streamed straight from global memory;
+// as x = h . W^T with both operands streamed straight from global memory;
 // all of a chunk's fragments are loaded before the first MFMA, so a wave
-// waits for memory once.
+// waits for memory once.  The result's lanes run along outputs, so each
+// store instruction writes two full 128-byte rows of part.
 __global__ __launch_bounds__(256) void append_gemm_mfma(const unsigned short* __restrict__ h,
                                                         const unsigned short* __restrict__ w,
                                                         int T, int d, int Dout, int kc_count,
@@ -54,14 +55,12 @@ __global__ __launch_bounds__(256) void append_gemm_mfma(const unsigned short* __
     }
     f32x16 acc = {};
 #pragma unroll
-    for (int i = 0; i < NK; ++i) acc = mfma32(av[i], bv[i], acc);
-    if (tok_ok) {
-        float* dst = part + ((size_t)kc * T + t) * Dout + mb * 32 + 4 * hf;
+    for (int i = 0; i < NK; ++i) acc = mfma32(bv[i], av[i], acc);
+    // acc[i] of lane (hf, l32): token nb*32 + 8 (i/4) + 4 hf + i%4, output o
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            f32x4 v = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-            *reinterpret_cast<f32x4*>(dst + 8 * g) = v;
-        }
+    for (int i = 0; i < 16; ++i) {
+        const int tt = nb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+        if (tt < T) part[((size_t)kc * T + tt) * Dout + o] = acc[i];
     }
 }
 
