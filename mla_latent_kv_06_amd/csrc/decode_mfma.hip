@@ -7,12 +7,14 @@
 //  1. absorb_q:  q_lat[r,h,:] = W_UK[h]^T q_nope[r,h,:]  (the query-side weight
 //     absorption of "DeepSeek-V2: MLA Explained", "Optimization Note"), packed
 //     with q_pe into one 576-wide bf16 query row per (row, head).
-//  2. split_kv:  one workgroup per (sequence, query row, partition).  All 128
-//     heads share every 64-token cache tile ("Latent Attention.", "Compress,
+//  2. split_kv:  each workgroup walks a range of (query row, cache tile) work
+//     -- a fixed partition of one row, or an equal share of all rows' tiles
+//     on the balanced schedule -- writing one piece per row it touches.  All
+//     128 heads share every 64-token cache tile ("Latent Attention.", "Compress,
 //     then rebuild": one latent serves every head), so heads form the dense
 //     MFMA dimension: S^T = K_tile . Q^T, online softmax, O^T += V^T . P^T
-//     with the latent columns of the same tile as values.  Writes the
-//     partition's normalised o_lat and log-sum-exp.
+//     with the latent columns of the same tile as values.  Writes each
+//     piece's normalised o_lat (fp16) and log-sum-exp.
 //  3. combine:   merges partitions by log-sum-exp weights into o_lat, then
 //     out[r,h,:] = W_UV[h] o_lat (the value-side absorption).
 //
@@ -319,8 +321,10 @@ __device__ __forceinline__ int scan_row_tiles(const int* __restrict__ seq_lens, 
     return T;
 }
 
-// Workgroup (row, split): row = b * q_len + s handles query token s of
-// sequence b for all 128 heads over cache tiles [t0, t1) of its visible range.
+// A piece (row, tiles [t0, t1)): row = b * q_len + s is query token s of
+// sequence b; the piece covers all 128 heads over those tiles of the row's
+// visible range.  A workgroup handles one piece (fixed partitions) or the
+// consecutive pieces its balanced share of the tile sequence spans.
 // Wave w owns heads 32w .. 32w+31 for the whole tile loop; each 64-token tile
 // is processed as two halves of 32 tokens:
 //   S^T (32 tokens x 32 heads) = K_half (32 x 576) . Q_w^T   [36 MFMA]
