@@ -205,6 +205,18 @@ __device__ __forceinline__ void issue_tile_bf16(const unsigned char* __restrict_
     }
 }
 
+// Copy instruction k (0..17) of wave w of the bf16 tile copy above.
+__device__ __forceinline__ void issue_tile_bf16_part(__amdgpu_buffer_rsrc_t rsrc, lds_u8* ltile,
+                                                     int w, int lane, int k) {
+    const unsigned off0 = (lane >> 3) * ROWB + (((lane & 7) ^ fswz(lane >> 3)) << 4);
+    const int i = w * 18 + k;
+    const int cg = i >> 3, q = i & 7;
+    // rows 8q + 8 .. +7 (q odd) have g = f(l/8) ^ 2: chunk slot bit 1 flips
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(ltile + i * 1024), 16,
+                                             (q & 1) ? (off0 ^ 32u) : off0, q * 8 * ROWB + cg * 128,
+                                             0, 0);
+}
+
 // Zero rows valid .. 63 of an LDS tile (their cache slots hold no token).
 __device__ __forceinline__ void zero_rows(lds_u8* ltile, int valid, int tid) {
     for (int p = valid * NCH + tid; p < BS * NCH; p += 256) {
@@ -433,6 +445,21 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         // fp8: the bf16 tile at 0, staging buffers at TILE and TILE + STAGE.
         lds_u8* qpe = smem + 2 * TILE;
 
+        auto valid_of = [&](int t) { return min(BS, n_vis - t * BS); };
+        // asynchronous load of tile t into `dst` (a bf16 tile, or fp8 staging)
+        auto issue = [&](int t, lds_u8* dst) {
+            const size_t blk = (size_t)btab[t];
+            if constexpr (FP8) {
+                issue_tile_fp8(pool + blk * F8TILE, pool_scale + blk * BS, dst, w, lane);
+            } else {
+                issue_tile_bf16(pool + blk * GTILE, dst, w, lane);
+            }
+        };
+        // The first tile's copy goes out before the query loads, so that the two
+        // memory round trips of a piece's start overlap.
+        issue(t0, FP8 ? smem + TILE : smem);
+        bool t0_in_flight = true;
+
         // this wave's 32 query rows, as MFMA B fragments: lane (hf, l32) holds
         // channels 16 ks + 8 hf .. +8 of head 32 w + l32
         bf16x8 qf[NQ];
@@ -454,16 +481,6 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         const lds_u8* qpe_lane = qpe + head * 128;
         const int qpe_g = fswz(head & 15);
 
-        auto valid_of = [&](int t) { return min(BS, n_vis - t * BS); };
-        // asynchronous load of tile t into `dst` (a bf16 tile, or fp8 staging)
-        auto issue = [&](int t, lds_u8* dst) {
-            const size_t blk = (size_t)btab[t];
-            if constexpr (FP8) {
-                issue_tile_fp8(pool + blk * F8TILE, pool_scale + blk * BS, dst, w, lane);
-            } else {
-                issue_tile_bf16(pool + blk * GTILE, dst, w, lane);
-            }
-        };
 
         // Per-lane LDS byte offsets.  Score operand (chunk 2 ks + hf of row
         // 32 hb + l32): by ks % 4.  Transposed value reads (in a 16-lane group,
@@ -503,7 +520,17 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         auto run_tile = [&](int t, const lds_u8* __restrict__ tile, lds_u8* __restrict__ nxt,
                             bool has_next) __attribute__((always_inline)) {
             const int valid = valid_of(t);
-            if (has_next) issue(t + 1, nxt);
+            // bf16: the next tile's 18 copy instructions of this wave are spread
+            // over the two score chains (one every 4 MFMAs); issued as one burst
+            // they hold the wave at issue while the address unit works through
+            // the workgroup's 72 copies.  Without a next tile the resource has no
+            // records and the copies read nothing.
+            [[maybe_unused]] __amdgpu_buffer_rsrc_t nrs;
+            if constexpr (FP8) {
+                if (has_next) issue(t + 1, nxt);
+            } else {
+                nrs = make_rsrc(pool + (size_t)btab[has_next ? t + 1 : t] * GTILE, has_next ? GTILE : 0);
+            }
 #pragma unroll 1
             for (int hb = 0; hb < 2; ++hb) {
                 if (hb * 32 >= valid) break;
@@ -523,6 +550,9 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                 for (int ks = 0; ks < 36; ++ks) {
                     if (ks + 2 < 36) a2 = ka(ks + 2);
                     sacc = mfma32(a0, qb(ks), sacc);
+                    if constexpr (!FP8) {
+                        if ((ks & 3) == 0) issue_tile_bf16_part(nrs, nxt, w, lane, hb * 9 + (ks >> 2));
+                    }
                     a0 = a1;
                     a1 = a2;
                 }
@@ -595,7 +625,8 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
             for (int i = 0; i < 16; ++i) o[i] = f32x16{};
             l_run = 0.f;
             overflow = false;
-            issue(t0, FP8 ? smem + TILE : smem);
+            if (!t0_in_flight) issue(t0, FP8 ? smem + TILE : smem);   // a later pass
+            t0_in_flight = false;
             for (int t = t0; t < t1; ++t) {
                 const int cur = (t - t0) & 1;
                 wait_vmem_all();
@@ -618,6 +649,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                 }
             }
             // ---- vote: did any wave's weights run past the reference? ------------------
+            wait_vmem_all();                 // (record-less copies of the last tile included)
             __syncthreads();                 // all waves are done with the tiles
             MLA_LDS int* votes = reinterpret_cast<MLA_LDS int*>(smem);
             if (lane == 0) votes[w] = __builtin_amdgcn_ballot_w64(overflow) != 0;
