@@ -23,18 +23,23 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // all of a chunk's fragments are loaded before the first MFMA, so a wave
 // waits for memory once.  The result's lanes run along outputs, so each
 // store instruction writes two full 128-byte rows of part.
+//
+// Work placement: the token blocks of one (output block, chunk) are
+// neighbouring waves of one workgroup, so each W slice leaves HBM once and its
+// second read hits the compute unit's caches.
+// grid: P * kc_count workgroups, P = ceil(n_mb * n_nb / 4) per chunk.
 __global__ __launch_bounds__(256) void append_gemm_mfma(const unsigned short* __restrict__ h,
                                                         const unsigned short* __restrict__ w,
                                                         int T, int d, int Dout, int kc_count,
                                                         int kchunk, float* __restrict__ part) {
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, hf = lane >> 5;
-    const int job = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int n_mb = Dout / 32, n_nb = (T + 31) / 32;
-    if (job >= n_mb * n_nb * kc_count) return;
-    const int mb = job % n_mb;
-    const int nb = (job / n_mb) % n_nb;
-    const int kc = job / (n_mb * n_nb);
+    const int P = (n_mb * n_nb + 3) / 4;
+    const int kc = blockIdx.x / P;
+    const int lj = (blockIdx.x - kc * P) * 4 + (threadIdx.x >> 6);
+    const int nb = lj % n_nb, mb = lj / n_nb;
+    if (kc >= kc_count || mb >= n_mb) return;
     const int o = mb * 32 + l32;
     const int t = nb * 32 + l32;
     const int k_lo = kc * kchunk, k_hi = min(d, k_lo + kchunk);
@@ -210,8 +215,8 @@ hipError_t launch_append(const AppendLaunch& a, bool mfma_gemm) {
     if (T == 0) return hipSuccess;
     const int Dout = a.DC + a.DR;
     if (mfma_gemm) {
-        const int jobs = (Dout / 32) * ((T + 31) / 32) * a.kc;
-        append_gemm_mfma<<<(jobs + 3) / 4, 256, 0, a.stream>>>(
+        const int P = ((Dout / 32) * ((T + 31) / 32) + 3) / 4;
+        append_gemm_mfma<<<P * a.kc, 256, 0, a.stream>>>(
             static_cast<const unsigned short*>(a.h), static_cast<const unsigned short*>(a.w_kv_a), T,
             a.d_model, Dout, a.kc, a.kchunk, a.part);
     } else {
