@@ -286,8 +286,8 @@ __device__ __forceinline__ void convert_tile_fp8(const lds_u8* lstage, lds_u8* l
 //    one workgroup each; partial slot r * num_splits + split.
 //  - num_splits == 0 (balanced): the rows' tiles, concatenated in row order,
 //    are cut into G equal ranges [i T / G, (i+1) T / G), one per workgroup
-//    (T = total tiles, G = min(grid, T), so no range is empty; workgroups
-//    past G have nothing to do).  A range may span several rows; each
+//    (T = total tiles, G = min(grid, ceil(T / 4)) <= T, so no range is empty;
+//    workgroups past G have nothing to do).  A range may span several rows; each
 //    (workgroup i, row r) piece writes partial slot i + r.  Slots are unique:
 //    for i < i' the rows of i end no later than the rows of i' begin, so
 //    i + r < i' + r'.  Row r's pieces occupy slots first(r) + r .. last(r) + r,
@@ -297,6 +297,15 @@ __device__ __forceinline__ int row_tiles(const int* __restrict__ seq_lens, int q
     const int b = r / q_len;
     const int n_vis = seq_lens[b] - q_len + (r - b * q_len) + 1;
     return n_vis > 0 ? (n_vis + BS - 1) / BS : 0;
+}
+
+// Workgroups of the balanced schedule for T tiles: at most one per compute
+// unit (the grid), and at least kMinGroupTiles tiles each, so that a small
+// batch does not pay a workgroup's fixed costs (query load, partial write,
+// one more partial to merge) for a single tile.
+constexpr int kMinGroupTiles = 4;
+__device__ __forceinline__ long long balanced_groups(long long grid, long long T) {
+    return min(grid, (T + kMinGroupTiles - 1) / kMinGroupTiles);
 }
 
 // Workgroup holding tile t of the concatenated tiles (T tiles over G groups).
@@ -374,7 +383,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         MLA_LDS int* sc = reinterpret_cast<MLA_LDS int*>(smem);
         int excl, mine;
         const int T = scan_row_tiles(seq_lens, q_len, R, sc, &excl, &mine);
-        const long long G = min((long long)gridDim.x, (long long)T);
+        const long long G = balanced_groups(gridDim.x, T);
         if ((long long)blockIdx.x >= G) return;      // uniform: the whole workgroup leaves
         rng_a = (int)((long long)blockIdx.x * T / G);
         rng_b = (int)((long long)(blockIdx.x + 1) * T / G);
@@ -746,7 +755,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
             if (r >= R) break;
             const int nt = row_tiles(seq_lens, q_len, r);
             if (r >= rb * 32 && r < rb * 32 + 32) {
-                const int G = min(groups, T);
+                const int G = (int)balanced_groups(groups, T);
                 const int f = nt > 0 ? group_of_tile(rs, T, G) : 0;
                 const int l = nt > 0 ? group_of_tile(rs + nt - 1, T, G) : -1;
                 pbase[r - rb * 32] = f + r;

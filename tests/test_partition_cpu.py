@@ -1,8 +1,8 @@
 """The balanced split-KV work partition (num_splits == 0 on the MFMA shapes),
 checked as arithmetic on the CPU: the scheme the kernels implement is
 
-  T tiles of all query rows, concatenated in row order, G = min(grid, T)
-  workgroups; workgroup i takes tiles [i T / G, (i+1) T / G); the piece of
+  T tiles of all query rows, concatenated in row order, G = min(grid, ceil(T / 4))
+  workgroups (at least 4 tiles each, at most one per compute unit); workgroup i takes tiles [i T / G, (i+1) T / G); the piece of
   row r inside it writes partial slot i + r; row r's partials are the slots
   g(first tile of r) + r .. g(last tile of r) + r with
   g(t) = ceil((t + 1) G / T) - 1 the workgroup holding tile t.
@@ -20,7 +20,7 @@ import random
 
 def pieces(tiles, grid):
     T = sum(tiles)
-    G = min(grid, T)
+    G = min(grid, (T + 3) // 4)
     rs = [0]
     for t in tiles:
         rs.append(rs[-1] + t)
