@@ -13,11 +13,17 @@ Parity status of each public function (what pins it is listed in
 ``tests/test_oracle_pins.py``):
 
 * ``decode_naive``           pinned (associativity, brute force, special cases)
+* ``decode_fp8_queries``     pinned (equals ``decode_naive`` when the queries are
+                             exact e4m3 values; log-sum-exp within the bound
+                             the query rounding allows)
+* ``round_to_bf16``          pinned (vs torch.bfloat16 on binary32 inputs, ties)
 * ``append_rows``            pinned (brute force, RMSNorm / RoPE invariants)
 * ``rmsnorm``, ``rope``      pinned (closed-form invariants, complex form)
 * ``slot_index``, ``gather_sequence``  pinned (brute force, permutation)
 * ``e4m3fn_decode`` / ``e4m3fn_encode`` / ``quantize_rows_fp8``
                              pinned (format definition vs torch.float8_e4m3fn)
+* ``quantize_vector_fp8_pow2`` pinned (minimal exponent by brute force, exact
+                             quotient, error bound)
 * ``bf16_bits_to_f64``       pinned (vs torch.bfloat16)
 * ``sizes.*``                pinned (figures printed on the pages)
 """
@@ -30,7 +36,9 @@ from .mla_ref import (  # noqa: F401
     slot_index,
     gather_sequence,
     decode_naive,
+    decode_fp8_queries,
     default_softmax_scale,
+    round_to_bf16,
 )
 from .fp8 import (  # noqa: F401
     E4M3FN_MAX,
@@ -38,5 +46,6 @@ from .fp8 import (  # noqa: F401
     e4m3fn_encode,
     quantize_rows_fp8,
     dequantize_rows_fp8,
+    quantize_vector_fp8_pow2,
 )
 from . import sizes  # noqa: F401

@@ -11,10 +11,17 @@ value 448.  One float32 scale per token covers all of its latent and rotary
 channels: scale = amax / 448, codes = round-to-nearest-even(x / scale),
 saturating at +-448.
 
+For query vectors (the fp8 score product) the scale is a power of two
+instead: the pages give no fp8 query arithmetic; this reading follows the
+power-of-two (e8m0) block scales of the OCP microscaling formats, which keep
+the division exact.
+
 The decoder is written from that bit layout, not from any library table.
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -75,3 +82,21 @@ def quantize_rows_fp8(rows: np.ndarray):
 def dequantize_rows_fp8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     """float(code) * scale, in float64."""
     return e4m3fn_decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def quantize_vector_fp8_pow2(v: np.ndarray):
+    """e4m3 rounding of one vector with a power-of-two scale -> (codes uint8,
+    sigma float).  sigma = 2^e with e the smallest integer such that
+    max|v| <= 448 * 2^e (sigma = 1 for an all-zero vector), so v / sigma is
+    exact and codes = round-to-nearest-even(v / sigma) never saturate."""
+    v = np.asarray(v, dtype=np.float64)
+    amax = float(np.max(np.abs(v)))
+    if amax == 0.0:
+        return e4m3fn_encode(v), 1.0
+    e = math.ceil(math.log2(amax / E4M3FN_MAX))
+    while amax > E4M3FN_MAX * 2.0 ** e:          # guard log2's rounding
+        e += 1
+    while amax <= E4M3FN_MAX * 2.0 ** (e - 1):
+        e -= 1
+    sigma = 2.0 ** e
+    return e4m3fn_encode(v / sigma), sigma

@@ -35,6 +35,8 @@ import math
 
 import numpy as np
 
+from .fp8 import e4m3fn_decode, quantize_vector_fp8_pow2
+
 
 def default_softmax_scale(qk_nope_dim: int, qk_rope_dim: int) -> float:
     """1 / sqrt(d_h + d_h^R): the score divisor of "DeepSeek-V2: MLA
@@ -50,6 +52,17 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     bits = np.asarray(bits, dtype=np.uint16)
     with np.errstate(invalid="ignore"):
         return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (ties to even), as
+    float64.  bfloat16 keeps 8 significant bits and binary32's exponent range;
+    below 2^-126 the spacing stays 2^-133 (subnormals).  Overflow is not
+    handled (the values rounded here are far below 2^127)."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                       # x = m 2^e, 0.5 <= |m| < 1
+    q = np.maximum(e, -125) - 8              # exponent of the last kept bit
+    return np.ldexp(np.rint(np.ldexp(x, -q)), q)   # rint: ties to even
 
 
 def rmsnorm(x: np.ndarray, gamma: np.ndarray | None = None, eps: float = 0.0) -> np.ndarray:
@@ -171,5 +184,60 @@ def decode_naive(q_nope, q_pe, w_uk, w_uv, seq_rows, q_len, softmax_scale=None):
                 e = np.exp(sc - m)
                 tot = e.sum()
                 out[b, s, i] = (e / tot) @ v_full[:n_vis]
+                lse[b, s, i] = m + math.log(tot)
+    return out, lse
+
+
+def decode_fp8_queries(q_nope, q_pe, w_uk, w_uv, seq_rows, q_len, softmax_scale=None):
+    """Decode whose score product takes the queries in fp8 (absorbed form).
+
+    The attention is that of ``decode_naive`` with the content key folded into
+    the query, the absorption of "DeepSeek-V2: MLA Explained", "Optimization
+    Note" (W_UK moves onto the query side, so the score reads the cached
+    latent as it is).  The pages give no fp8 arithmetic for the score; the
+    reading here:
+    for every sequence b, query row s and head i
+
+      q_lat  = bf16(W_UK[i]^T q^C_i)      the absorbed query, held at bfloat16
+                                          like the queries themselves
+      q~     = [q_lat ; q^R_i]            576 values
+      q^     = e4m3 rounding of q~ / sigma, sigma the smallest power of two
+               with amax|q~| <= 448 sigma (``quantize_vector_fp8_pow2``),
+               dequantised: code * sigma
+      s_j    = q^ . [c_j ; k^R_j] * scale
+      o_i    = W_UV[i] sum_j softmax_j(s) c_j
+
+    over the tokens row s may see.  Arguments and results as ``decode_naive``.
+    """
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    q_pe = np.asarray(q_pe, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    B, Sq, H, N = q_nope.shape
+    R = q_pe.shape[-1]
+    V = w_uv.shape[1]
+    if Sq != q_len:
+        raise ValueError("q_len does not match q_nope")
+    scale = default_softmax_scale(N, R) if softmax_scale is None else float(softmax_scale)
+    out = np.zeros((B, Sq, H, V))
+    lse = np.full((B, Sq, H), -np.inf)
+    for b in range(B):
+        rows = np.asarray(seq_rows[b], dtype=np.float64)
+        L = rows.shape[0]
+        for i in range(H):
+            for s in range(Sq):
+                n_vis = L - Sq + s + 1
+                if n_vis <= 0:
+                    continue
+                q_lat = round_to_bf16(w_uk[i].T @ q_nope[b, s, i])
+                q_t = np.concatenate([q_lat, q_pe[b, s, i]])
+                codes, sigma = quantize_vector_fp8_pow2(q_t)
+                q_hat = e4m3fn_decode(codes) * sigma
+                sc = (rows[:n_vis] @ q_hat) * scale
+                m = sc.max()
+                e = np.exp(sc - m)
+                tot = e.sum()
+                o_lat = (e / tot) @ rows[:n_vis, : w_uk.shape[-1]]
+                out[b, s, i] = w_uv[i] @ o_lat
                 lse[b, s, i] = m + math.log(tot)
     return out, lse

@@ -464,3 +464,107 @@ def test_bf16_decode_matches_torch():
     assert np.array_equal(np.isnan(got), np.isnan(ref))
     ok = ~np.isnan(ref)
     np.testing.assert_array_equal(got[ok], ref[ok])
+
+
+def test_round_to_bf16_matches_torch():
+    rng = np.random.default_rng(20)
+    x = rng.standard_normal(60000) * np.exp(rng.uniform(-30, 30, 60000))
+    x = np.concatenate([x, rng.standard_normal(2000) * 1e-39])      # binary32 subnormals
+    x = x.astype(np.float32).astype(np.float64)
+    # midpoints between neighbouring bfloat16 values: ties go to the even one
+    b = oracle.bf16_bits_to_f64(rng.integers(0x0080, 0x7F00, 5000).astype(np.uint16))
+    nxt = oracle.bf16_bits_to_f64((np.frombuffer(b.astype(np.float32).tobytes(), np.uint32) >> 16)
+                                  .astype(np.uint16) + 1)
+    x = np.concatenate([x, (b + nxt) / 2, -(b + nxt) / 2])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_to_bf16(x), ref)
+
+
+def test_fp8_pow2_vector_quantisation():
+    rng = np.random.default_rng(23)
+    vecs = [rng.standard_normal(576) * 10.0 ** rng.uniform(-4, 4) for _ in range(200)]
+    for k in (-7, 0, 3):                       # amax exactly 448 * 2^k, and just above
+        v = rng.uniform(-1, 1, 64) * 448 * 2.0 ** k
+        v[5] = 448 * 2.0 ** k
+        vecs += [v, v * (1 + 2.0 ** -30)]
+    for v in vecs:
+        codes, sigma = oracle.quantize_vector_fp8_pow2(v)
+        e = math.log2(sigma)
+        assert e == int(e)
+        amax = np.abs(v).max()
+        assert amax <= 448 * sigma and amax > 224 * sigma      # the smallest such power
+        np.testing.assert_array_equal(codes, oracle.e4m3fn_encode(v / sigma))
+        back = oracle.e4m3fn_decode(codes) * sigma
+        err = np.abs(back - v)
+        assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(v), 2.0 ** -10 * sigma) * (1 + 1e-12))
+    assert math.log2(oracle.quantize_vector_fp8_pow2(vecs[-6])[1]) == -7
+    assert math.log2(oracle.quantize_vector_fp8_pow2(vecs[-5])[1]) == -6
+    codes, sigma = oracle.quantize_vector_fp8_pow2(np.zeros(8))
+    assert sigma == 1.0 and not codes.any()
+
+
+# --------------------------------------------------------------------------
+# decode with e4m3 queries in the score product
+# --------------------------------------------------------------------------
+
+def _e4m3_grid_queries(rng, shape, exps):
+    """Values of the e4m3 grid times 2^e (e per head, last axis before the
+    channels), so that the per-vector quantisation is exact."""
+    codes = rng.integers(0, 0x7F, size=shape).astype(np.uint8)
+    codes |= (rng.integers(0, 2, size=shape) << 7).astype(np.uint8)
+    v = oracle.e4m3fn_decode(codes)
+    return v * np.ldexp(1.0, np.asarray(exps))[None, None, :, None]
+
+
+def test_fp8_queries_equal_naive_when_queries_are_e4m3_values():
+    rng = np.random.default_rng(21)
+    B, Sq, H, N, R, d_c, V = 2, 2, 3, 8, 4, 16, 5
+    exps = [-3, 0, 2]                       # a different scale per head
+    q_nope = _e4m3_grid_queries(rng, (B, Sq, H, N), exps)
+    q_pe = _e4m3_grid_queries(rng, (B, Sq, H, R), exps)
+    # the largest magnitude, 448 * 2^e, sits in the content part for some
+    # (row, head) and in the rotary part for others
+    for b in range(B):
+        for s in range(Sq):
+            for i in range(H):
+                tgt = q_nope if (b + s + i) % 2 == 0 else q_pe
+                tgt[b, s, i, (b + i) % tgt.shape[-1]] = -448.0 * 2.0 ** exps[i]
+    w_uk = np.zeros((H, N, d_c))
+    for i in range(H):
+        w_uk[i, :, :N] = np.eye(N)          # q_lat = [q^C ; 0], exact
+    w_uv = rng.standard_normal((H, V, d_c))
+    rows = [rng.standard_normal((7, d_c + R)), rng.standard_normal((3, d_c + R))]
+    out_n, lse_n = oracle.decode_naive(q_nope, q_pe, w_uk, w_uv, rows, Sq, 0.3)
+    out_f, lse_f = oracle.decode_fp8_queries(q_nope, q_pe, w_uk, w_uv, rows, Sq, 0.3)
+    np.testing.assert_allclose(out_f, out_n, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse_f, lse_n, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_queries_lse_within_query_rounding_bound():
+    """The log-sum-exp moves by at most the largest score change, and each
+    score change is bounded by the query rounding: bfloat16 (2^-9 relative)
+    then e4m3 (2^-4 relative, or 2^-10 sigma below the normal range)."""
+    rng = np.random.default_rng(22)
+    B, Sq, H, N, R, d_c, V = 2, 2, 4, 16, 8, 32, 6
+    q_nope = rng.standard_normal((B, Sq, H, N)) * 3
+    q_pe = rng.standard_normal((B, Sq, H, R)) * 3
+    w_uk = rng.standard_normal((H, N, d_c)) * 0.3
+    w_uv = rng.standard_normal((H, V, d_c))
+    rows = [rng.standard_normal((40, d_c + R)), rng.standard_normal((9, d_c + R))]
+    scale = 0.2
+    _, lse_n = oracle.decode_naive(q_nope, q_pe, w_uk, w_uv, rows, Sq, scale)
+    out_f, lse_f = oracle.decode_fp8_queries(q_nope, q_pe, w_uk, w_uv, rows, Sq, scale)
+    assert np.isfinite(out_f).all()
+    moved = 0
+    for b in range(B):
+        for s in range(Sq):
+            n_vis = rows[b].shape[0] - Sq + s + 1
+            for i in range(H):
+                q = np.concatenate([w_uk[i].T @ q_nope[b, s, i], q_pe[b, s, i]])
+                sigma = 2 * np.abs(q).max() / 448       # the power of two is below this
+                dq = (2.0 ** -9 + 2.0 ** -4 * (1 + 2.0 ** -9)) * np.abs(q) + 2.0 ** -10 * sigma
+                bound = scale * (np.abs(rows[b][:n_vis]) @ dq).max()
+                d = abs(lse_f[b, s, i] - lse_n[b, s, i])
+                assert d <= bound, (b, s, i, d, bound)
+                moved += d > 1e-9
+    assert moved >= B * Sq * H // 2         # the rounding does change the scores
