@@ -31,6 +31,7 @@ import numpy as np
 METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak) at bs64, ctx 8k"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("decode_mfma.hip", "common.hpp", "internal.hpp")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "split_kv_kernel_v3_b64_ctx8k_bf16_hbm_traffic.txt")
@@ -76,6 +77,8 @@ def parse():
                    help="split-KV partitions per query row (default: the workload's own; "
                         "0 = the library's balanced schedule)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fp8-scores", action="store_true",
+                   help="fp8 cache: score product on the fp8 matrix cores (MLA_FLAG_FP8_SCORES)")
     p.add_argument("--cpu-tokens", type=int, default=262144,
                    help="CPU-baseline sample: first sequences of layer 0 up to this many cached tokens")
     p.add_argument("--report", default=None)
@@ -157,7 +160,9 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     if wl.act_dtype != "bf16" or wl.cache_dtype not in ("bf16", "fp8"):
         raise SystemExit("bench.py times the bf16-activation workloads (bf16 or fp8 cache)")
-    dims = b.Dims.from_workload(wl)
+    if args.fp8_scores and wl.cache_dtype != "fp8":
+        raise SystemExit("--fp8-scores needs an fp8-cache workload")
+    dims = b.Dims.from_workload(wl, flags=b.FLAG_FP8_SCORES if args.fp8_scores else 0)
     B, Sq, H = wl.batch, wl.q_len, wl.n_heads
     splits = wl.num_splits if args.splits is None else args.splits
 
@@ -223,13 +228,20 @@ def main():
     flops = sum(int(L - Sq + s + 1) for L in seq_lens for s in range(Sq)) * 2 * H * (wl.row_width + wl.kv_lora_rank)
     achieved = cache_bytes / k_avg_s / 1e9
     tflops = flops / k_avg_s / 1e12
-    mfma_bound = flops / cache_bytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    # matrix-core peak: bf16 for both products, or with fp8 scores the score
+    # share (576 of the 576 + 512 columns) at the fp8 rate, time-weighted
+    if args.fp8_scores:
+        f_s = wl.row_width / (wl.row_width + wl.kv_lora_rank)
+        mfma_peak = 1.0 / (f_s / FP8_PEAK_TFLOPS + (1 - f_s) / BF16_PEAK_TFLOPS)
+    else:
+        mfma_peak = BF16_PEAK_TFLOPS
+    mfma_bound = flops / cache_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     step_gbs = cache_bytes / (ms_step / 1e3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us  ({value:.4g} tok/s)  split-KV kernel {k_avg_s * 1e6:.1f} us "
         f"(p10 {np.percentile(k_ms, 10) * 1e3:.1f} / p90 {np.percentile(k_ms, 90) * 1e3:.1f})")
     log(f"cache {cache_bytes / 1e6:.1f} MB: kernel {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s), "
         f"step {step_gbs:.0f} GB/s; kernel {flops / k_avg_s / 1e12:.0f} TFLOP/s "
-        f"({flops / k_avg_s / 1e12 / BF16_PEAK_TFLOPS:.1%} of bf16 MFMA peak)")
+        f"({flops / k_avg_s / 1e12 / mfma_peak:.1%} of the {mfma_peak:.0f} TFLOP/s MFMA peak)")
 
     result = {
         "metric": METRIC,
@@ -242,7 +254,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 scores, bf16 values" if args.fp8_scores else "bf16",
         "data": "synthetic",
         "config": {
             "workload": wl.name, "batch": B, "ctx": int(seq_lens.max()), "q_len": Sq,
@@ -251,23 +263,24 @@ def main():
             "num_splits": splits if splits else "balanced",
             "layers_rotated": args.layers,
             "cache_dtype": wl.cache_dtype,
+            "fp8_scores": bool(args.fp8_scores),
             "step": ("cache append of %d token(s)/seq + absorbed decode, one layer" % Sq
                      if wl.append else "absorbed decode, one layer"),
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
             "bound": "mfma" if mfma_bound else "hbm",
-            "kernel": "split_kv_kernel<%s>" % wl.cache_dtype,
+            "kernel": "split_kv_kernel<%s%s>" % (wl.cache_dtype, ", fp8 scores" if args.fp8_scores else ""),
             "achieved": round(tflops if mfma_bound else achieved, 1),
-            "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+            "peak": round(mfma_peak, 1) if mfma_bound else HBM_PEAK_GBS,
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
-            "frac": round(tflops / BF16_PEAK_TFLOPS if mfma_bound else achieved / HBM_PEAK_GBS, 4),
+            "frac": round(tflops / mfma_peak if mfma_bound else achieved / HBM_PEAK_GBS, 4),
             "hbm_gbs": round(achieved, 1),
             "traffic": profiled_traffic(wl.name), "traffic_unit": "bytes per launch",
             "algorithmic_bytes": cache_bytes,
             "avg_launch_us": round(k_avg_s * 1e6, 2),
             "mfma_tflops": round(flops / k_avg_s / 1e12, 1),
-            "mfma_frac": round(flops / k_avg_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "mfma_frac": round(flops / k_avg_s / 1e12 / mfma_peak, 4),
         },
         "cpu_baseline": None,
     }

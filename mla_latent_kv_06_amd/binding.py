@@ -29,6 +29,7 @@ STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_BAD_SHAPE",
                 5: "MLA_ERR_WORKSPACE_TOO_SMALL", 6: "MLA_ERR_HIP"}
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 STAGE_ABSORB_Q, STAGE_SPLIT_KV, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
+FLAG_FP8_SCORES = 1          # mla_dims.flags: fp8 score product (fp8 cache, MFMA shape)
 
 DTYPE_CODES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 _TORCH_OF = {MLA_F32: (torch.float32,), MLA_BF16: (torch.bfloat16,),
@@ -45,21 +46,21 @@ class Dims(ctypes.Structure):
                 ("qk_rope_dim", ctypes.c_int32), ("qk_nope_dim", ctypes.c_int32),
                 ("v_head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("cache_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("flags", ctypes.c_int32)]
 
     @classmethod
     def make(cls, n_heads, kv_lora_rank, qk_rope_dim, qk_nope_dim, v_head_dim, block_size,
-             cache_dtype="bf16", act_dtype="bf16", softmax_scale=0.0):
+             cache_dtype="bf16", act_dtype="bf16", softmax_scale=0.0, flags=0):
         cd = DTYPE_CODES[cache_dtype] if isinstance(cache_dtype, str) else cache_dtype
         ad = DTYPE_CODES[act_dtype] if isinstance(act_dtype, str) else act_dtype
         return cls(n_heads, kv_lora_rank, qk_rope_dim, qk_nope_dim, v_head_dim, block_size,
-                   cd, ad, softmax_scale)
+                   cd, ad, softmax_scale, flags)
 
     @classmethod
-    def from_workload(cls, wl, softmax_scale=0.0):
+    def from_workload(cls, wl, softmax_scale=0.0, flags=0):
         return cls.make(wl.n_heads, wl.kv_lora_rank, wl.qk_rope_dim, wl.qk_nope_dim,
                         wl.v_head_dim, wl.block_size, wl.cache_dtype, wl.act_dtype,
-                        softmax_scale)
+                        softmax_scale, flags)
 
 
 _P = ctypes.c_void_p

@@ -245,6 +245,64 @@ __device__ __forceinline__ void issue_tile_fp8(const unsigned char* __restrict__
     }
 }
 
+// fp8 scores: the staging tile keeps rows 37 chunks (592 bytes) apart, so the
+// score operand reads of 16 consecutive rows (one 16-byte chunk each, row
+// stride 148 dwords) fall on distinct banks.  Position p = 64 i + lane of copy
+// instruction i holds chunk p % 37 of row p / 37; the 37th chunk of a row is
+// padding (it repeats chunk 35).  37 instructions, spread over the 4 waves;
+// the 64 scales follow the codes.
+constexpr int F8ROW = 37;                       // 16-byte chunks per padded staging row
+constexpr int F8SCODES = BS * F8ROW * 16;       // 37888 bytes
+__device__ __forceinline__ void issue_tile_fp8_padded(const unsigned char* __restrict__ gtile,
+                                                      const float* __restrict__ gscale,
+                                                      lds_u8* lstage, int w, int lane) {
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(gtile, F8TILE);
+#pragma unroll 1
+    for (int i = w; i < BS * F8ROW / 64; i += 4) {
+        const int p = i * 64 + lane;
+        const int t = p / F8ROW, c = p - t * F8ROW;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(lstage + i * 1024), 16,
+                                                 t * D + min(c, F8CHUNKS - 1) * 16, 0, 0, 0);
+    }
+    if (w == 0) {
+        const __amdgpu_buffer_rsrc_t srs = make_rsrc(gscale, BS * 4);
+        if (lane < 16)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (MLA_LDS void*)(lstage + F8SCODES), 16,
+                                                     lane * 16, 0, 0, 0);
+    }
+}
+
+// Padded fp8 staging -> dequantised bf16 tile, latent channels only (the
+// scores read the codes themselves).  Rows at or beyond `valid` become zeros.
+__device__ __forceinline__ void convert_tile_fp8_latent(const lds_u8* lstage, lds_u8* ltile, int tid,
+                                                        int valid) {
+    const MLA_LDS float* lscale = reinterpret_cast<const MLA_LDS float*>(lstage + F8SCODES);
+#pragma unroll 1
+    for (int k = 0; k < 8; ++k) {
+        const int p = k * 256 + tid;                   // 64 rows x 32 latent chunks
+        const int t = p >> 5, c = p & 31;
+        u32x4 outw[2];
+        if (t < valid) {
+            const u32x4 raw = *reinterpret_cast<const MLA_LDS u32x4*>(lstage + (t * F8ROW + c) * 16);
+            const float sc = lscale[t];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[q], false);
+                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[q], true);
+                const unsigned int p0 = f32_to_bf16_bits(lo[0] * sc) | ((unsigned)f32_to_bf16_bits(lo[1] * sc) << 16);
+                const unsigned int p1 = f32_to_bf16_bits(hi[0] * sc) | ((unsigned)f32_to_bf16_bits(hi[1] * sc) << 16);
+                outw[q >> 1][(q & 1) * 2 + 0] = p0;
+                outw[q >> 1][(q & 1) * 2 + 1] = p1;
+            }
+        } else {
+            outw[0] = u32x4{0, 0, 0, 0};
+            outw[1] = u32x4{0, 0, 0, 0};
+        }
+        *reinterpret_cast<MLA_LDS u32x4*>(ltile + tpos(t, 2 * c) * 16) = outw[0];
+        *reinterpret_cast<MLA_LDS u32x4*>(ltile + tpos(t, 2 * c + 1) * 16) = outw[1];
+    }
+}
+
 // fp8 staging (+ scales) -> dequantised bf16 swizzled tile (value * token
 // scale, RNE).  Rows at or beyond `valid` become zeros.
 __device__ __forceinline__ void convert_tile_fp8(const lds_u8* lstage, lds_u8* ltile, int tid,
@@ -352,7 +410,10 @@ __device__ __forceinline__ int scan_row_tiles(const int* __restrict__ seq_lens, 
 //   O^T (512 cols x 32 heads) += V^T (512 x 32) . P^T         [32 MFMA]
 // so softmax statistics stay inside the wave.  Q_w stays in VGPRs (its rotary
 // part in LDS on the bf16 path) and O^T in AGPRs for the whole loop.
-template <bool FP8>
+// F8S (fp8 cache only): the score product runs on the fp8 matrix cores, with
+// the cache codes as they are and the queries quantised to e4m3 with one scale
+// per (row, head); the value product stays bf16.
+template <bool FP8, bool F8S = false>
 __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const unsigned short* __restrict__ qbuf,      // [R][H][576] bf16
     const unsigned char* __restrict__ pool,       // [blocks][64][576] bf16 | fp8
@@ -365,9 +426,10 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     // fp8: one bf16 tile + two fp8 staging tiles with scales (rotary queries in VGPRs)
     constexpr bool QPE_LDS = !FP8;
     constexpr int QPE_BYTES = H * DR * 2;
-    constexpr int STAGE = F8TILE + 256;           // fp8 staging buffer: codes + scales
+    static_assert(FP8 || !F8S, "fp8 scores need an fp8 cache");
+    constexpr int STAGE = (F8S ? F8SCODES : F8TILE) + 256;   // fp8 staging buffer: codes + scales
     constexpr int LDS_BYTES = FP8 ? (TILE + 2 * STAGE) : (2 * TILE + QPE_BYTES);
-    constexpr int NQ = QPE_LDS ? 32 : 36;          // query K-steps kept in VGPRs
+    constexpr int NQ = F8S ? 1 : (QPE_LDS ? 32 : 36);   // bf16 query K-steps kept in VGPRs
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[LDS_BYTES];
     lds_u8* smem = (lds_u8*)smem_raw;
 
@@ -458,7 +520,9 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         // asynchronous load of tile t into `dst` (a bf16 tile, or fp8 staging)
         auto issue = [&](int t, lds_u8* dst) {
             const size_t blk = (size_t)btab[t];
-            if constexpr (FP8) {
+            if constexpr (F8S) {
+                issue_tile_fp8_padded(pool + blk * F8TILE, pool_scale + blk * BS, dst, w, lane);
+            } else if constexpr (FP8) {
                 issue_tile_fp8(pool + blk * F8TILE, pool_scale + blk * BS, dst, w, lane);
             } else {
                 issue_tile_bf16(pool + blk * GTILE, dst, w, lane);
@@ -472,10 +536,61 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         // this wave's 32 query rows, as MFMA B fragments: lane (hf, l32) holds
         // channels 16 ks + 8 hf .. +8 of head 32 w + l32
         bf16x8 qf[NQ];
-        {
+        if constexpr (!F8S) {
             const unsigned short* qrow = qbuf + ((size_t)row * H + head) * D + hf * 8;
 #pragma unroll
             for (int ks = 0; ks < NQ; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+        }
+        // fp8 scores: the fp8 B fragments of K-step s (64 channels) hold channels
+        // 64 s + 32 hf .. +32 of head 32 w + l32, divided by the head's scale
+        // 2^e, the smallest power of two with amax <= 448 * 2^e, and rounded to
+        // nearest even.  The division is exact, so the rounding sees the exact
+        // quotient; |q| / 2^e <= 448 never saturates.
+        [[maybe_unused]] i32x8 qc[F8S ? 9 : 1];
+        [[maybe_unused]] float qscale = 1.f;
+        if constexpr (F8S) {
+            const unsigned short* qrow = qbuf + ((size_t)row * H + head) * D + hf * 32;
+            u32x4 raw[9][4];
+            float amax = 0.f;
+#pragma unroll
+            for (int s8 = 0; s8 < 9; ++s8)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) raw[s8][j] = *reinterpret_cast<const u32x4*>(qrow + 64 * s8 + 8 * j);
+#pragma unroll
+            for (int s8 = 0; s8 < 9; ++s8)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const unsigned u = raw[s8][j][e];
+                        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32((unsigned short)u)),
+                                                 fabsf(bf16_bits_to_f32((unsigned short)(u >> 16)))));
+                    }
+            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+            // amax = f 2^E, 0.5 <= f < 1, and 448 = 0.875 2^9
+            int ex = 0;
+            const float fm = frexpf(amax, &ex);
+            const int qe = amax > 0.f ? (fm <= 0.875f ? ex - 9 : ex - 8) : 0;
+            qscale = ldexpf(1.0f, qe);
+            const float inv = ldexpf(1.0f, -qe);
+#pragma unroll
+            for (int s8 = 0; s8 < 9; ++s8)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // 8 bf16 -> 8 e4m3 codes (2 dwords)
+                    const u32x4 u = raw[s8][j];
+                    int d0 = 0, d1 = 0;
+                    d0 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_bits_to_f32((unsigned short)u[0]) * inv,
+                                                         bf16_bits_to_f32((unsigned short)(u[0] >> 16)) * inv, d0, false);
+                    d0 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_bits_to_f32((unsigned short)u[1]) * inv,
+                                                         bf16_bits_to_f32((unsigned short)(u[1] >> 16)) * inv, d0, true);
+                    d1 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_bits_to_f32((unsigned short)u[2]) * inv,
+                                                         bf16_bits_to_f32((unsigned short)(u[2] >> 16)) * inv, d1, false);
+                    d1 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_bits_to_f32((unsigned short)u[3]) * inv,
+                                                         bf16_bits_to_f32((unsigned short)(u[3] >> 16)) * inv, d1, true);
+                    qc[s8][2 * j] = d0;
+                    qc[s8][2 * j + 1] = d1;
+                }
         }
         if constexpr (QPE_LDS) {
             // q_pe of all heads: head h's chunk c (8 channels) at h*128 + ((c ^ g(h)) << 4)
@@ -527,7 +642,8 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         // never overlap; saying so (restrict) lets the compiler keep the
         // transposed value reads from waiting on the load in flight.
         auto run_tile = [&](int t, const lds_u8* __restrict__ tile, lds_u8* __restrict__ nxt,
-                            bool has_next) __attribute__((always_inline)) {
+                            const lds_u8* __restrict__ stg, bool has_next) __attribute__((always_inline)) {
+            (void)stg;
             const int valid = valid_of(t);
             // bf16: the next tile's 18 copy instructions of this wave are spread
             // over the two score chains (one every 4 MFMAs); issued as one burst
@@ -554,21 +670,51 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                     return *reinterpret_cast<const MLA_LDS bf16x8*>(qpe_lane + ((c ^ qpe_g) << 4));
                 };
                 f32x16 sacc = {};
-                bf16x8 a0 = ka(0), a1 = ka(1), a2;
+                float sv[16];
+                if constexpr (F8S) {
+                    // codes of rows 32 hb + l32, channels 64 s + 32 hf .. +32: two
+                    // consecutive 16-byte chunks of the padded staging row
+                    const lds_u8* srow = stg + ((hb * 32 + l32) * F8ROW + 2 * hf) * 16;
+                    auto kc = [&](int s8) {
+                        const u32x4 lo = *reinterpret_cast<const MLA_LDS u32x4*>(srow + s8 * 64);
+                        const u32x4 hi = *reinterpret_cast<const MLA_LDS u32x4*>(srow + s8 * 64 + 16);
+                        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    };
+                    i32x8 a0 = kc(0), a1 = kc(1), a2;
 #pragma unroll
-                for (int ks = 0; ks < 36; ++ks) {
-                    if (ks + 2 < 36) a2 = ka(ks + 2);
-                    sacc = mfma32(a0, qb(ks), sacc);
-                    if constexpr (!FP8) {
-                        if ((ks & 3) == 0) issue_tile_bf16_part(nrs, nxt, w, lane, hb * 9 + (ks >> 2));
+                    for (int s8 = 0; s8 < 9; ++s8) {
+                        if (s8 + 2 < 9) a2 = kc(s8 + 2);
+                        // e4m3 x e4m3, unit block scales (e8m0 127 = 1.0)
+                        sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qc[s8], sacc, 0, 0, 0, 127, 0, 127);
+                        a0 = a1;
+                        a1 = a2;
                     }
-                    a0 = a1;
-                    a1 = a2;
+                    // token scales of the lane's rows 32 hb + 8 g + 4 hf .. +4
+                    const MLA_LDS float* lsc = reinterpret_cast<const MLA_LDS float*>(stg + F8SCODES);
+                    const float qs = qscale * scale_log2;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 ks4 = *reinterpret_cast<const MLA_LDS f32x4*>(lsc + hb * 32 + 8 * g + 4 * hf);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) sv[4 * g + j] = sacc[4 * g + j] * qs * ks4[j];
+                    }
+                } else {
+                    bf16x8 a0 = ka(0), a1 = ka(1), a2;
+#pragma unroll
+                    for (int ks = 0; ks < 36; ++ks) {
+                        if (ks + 2 < 36) a2 = ka(ks + 2);
+                        sacc = mfma32(a0, qb(ks), sacc);
+                        if constexpr (!FP8) {
+                            if ((ks & 3) == 0) issue_tile_bf16_part(nrs, nxt, w, lane, hb * 9 + (ks >> 2));
+                        }
+                        a0 = a1;
+                        a1 = a2;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sv[i] = sacc[i] * scale_log2;
                 }
                 // lane holds head `head`, tokens 32 hb + 8 (i/4) + 4 hf + (i%4)
-                float sv[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sv[i] = sacc[i] * scale_log2;
                 if (valid < BS) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
@@ -644,9 +790,13 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                 if constexpr (FP8) {
                     lds_u8* st_cur = smem + TILE + cur * STAGE;
                     lds_u8* st_nxt = smem + TILE + (cur ^ 1) * STAGE;
-                    convert_tile_fp8(st_cur, smem, tid, valid_of(t));
+                    if constexpr (F8S) {
+                        convert_tile_fp8_latent(st_cur, smem, tid, valid_of(t));
+                    } else {
+                        convert_tile_fp8(st_cur, smem, tid, valid_of(t));
+                    }
                     __syncthreads();
-                    run_tile(t, smem, st_nxt, has_next);
+                    run_tile(t, smem, st_nxt, st_cur, has_next);
                 } else {
                     lds_u8* cur_tile = smem + cur * TILE;
                     lds_u8* nxt_tile = smem + (cur ^ 1) * TILE;
@@ -654,7 +804,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                         zero_rows(cur_tile, valid_of(t), tid);
                         __syncthreads();
                     }
-                    run_tile(t, cur_tile, nxt_tile, has_next);
+                    run_tile(t, cur_tile, nxt_tile, nullptr, has_next);
                 }
             }
             // ---- vote: did any wave's weights run past the reference? ------------------
@@ -917,7 +1067,12 @@ hipError_t launch_decode_mfma(const DecodeLaunch& a, unsigned stages) {
         // balanced scheduling: one workgroup per compute unit
         const int grid = a.num_splits > 0 ? R * a.num_splits : kNumCUs;
         const float scale_log2 = a.scale * kLog2e;
-        if (a.cache_dtype == MLA_FP8_E4M3) {
+        if (a.cache_dtype == MLA_FP8_E4M3 && a.fp8_scores) {
+            split_kv_kernel<true, true><<<grid, 256, 0, a.stream>>>(
+                qbuf, static_cast<const unsigned char*>(a.pool), a.pool_scale, a.block_table,
+                a.max_blocks, a.seq_lens, R, a.q_len, a.num_splits, scale_log2,
+                static_cast<unsigned short*>(a.part_o), a.part_lse);
+        } else if (a.cache_dtype == MLA_FP8_E4M3) {
             split_kv_kernel<true><<<grid, 256, 0, a.stream>>>(
                 qbuf, static_cast<const unsigned char*>(a.pool), a.pool_scale, a.block_table,
                 a.max_blocks, a.seq_lens, R, a.q_len, a.num_splits, scale_log2,

@@ -112,6 +112,14 @@ def test_decode_validation_rejects_before_launch(b):
     assert _call_decode(b, bad) == 3                             # UNSUPPORTED act dtype
     assert "act_dtype" in b.lib().mla_last_error().decode()
     assert _call_decode(b, d, batch=0) == 0                      # nothing to do
+    # flags: unknown bits, and fp8 scores without an fp8 cache, are refused
+    bad = b.Dims.make(128, 512, 64, 128, 128, 64, flags=2)
+    assert _call_decode(b, bad) == 3
+    bad = b.Dims.make(128, 512, 64, 128, 128, 64, "bf16", "bf16", flags=b.FLAG_FP8_SCORES)
+    assert _call_decode(b, bad) == 3
+    assert "FP8_SCORES" in b.lib().mla_last_error().decode()
+    bad = b.Dims.make(64, 512, 64, 128, 128, 64, "fp8", "bf16", flags=b.FLAG_FP8_SCORES)
+    assert _call_decode(b, bad) == 3                             # not the MFMA shape
 
 
 def test_append_validation_rejects_before_launch(b):

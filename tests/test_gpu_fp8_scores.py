@@ -1,0 +1,101 @@
+"""GPU parity of the fp8 score product (mla_dims.flags = MLA_FLAG_FP8_SCORES,
+fp8 cache) against the CPU oracle.
+
+Parity: the option rounds every absorbed query vector to e4m3 with one scale
+per (row, head) and multiplies the stored cache codes directly; the oracle's
+``decode_fp8_queries`` is that definition in float64, so the kernel is held to
+the fp8-cache bar against it (max-abs <= 6e-2 and rel-L2 <= 5e-3 over the
+output, log-sum-exp within 1e-3).
+
+Accuracy cost: the same output against the exact oracle (``decode_naive``) is
+printed, with a loose sanity bound.  With few visible tokens the output moves
+with the logits' rounding error (up to ~0.1 on outputs of magnitude ~4 at two
+tokens); over long sequences the errors average out.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from mla_latent_kv_06_amd import synth
+from tests.casebuild import build_case, error_stats
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+MID = W["v3_b64_ctx1k8k_paged_bf16"].replace(name="v3_mid_fp8s", batch=3, ctx_lo=40,
+                                             ctx_hi=450, append=False, cache_dtype="fp8")
+
+
+def announce(*what):
+    print("[gpu-case]", *what, flush=True)
+
+
+def run_fp8s(case, num_splits):
+    from mla_latent_kv_06_amd import binding as b
+    from tests import gpu_util
+    dc = gpu_util.DeviceCase(case)
+    dc.dims = b.Dims.from_workload(case.wl, flags=b.FLAG_FP8_SCORES)
+    out, lse = dc.decode(num_splits=num_splits)
+    return gpu_util.to_np(out), gpu_util.to_np(lse)
+
+
+def check(got, ref, got_lse, ref_lse, tag):
+    max_abs, rel = error_stats(got, ref)
+    d_lse = float(np.max(np.abs(got_lse - ref_lse)))
+    print(f"{tag}: max-abs {max_abs:.3e} rel-L2 {rel:.3e} lse {d_lse:.3e}", flush=True)
+    assert np.isfinite(got).all(), tag
+    assert max_abs <= 6e-2, (tag, max_abs)
+    assert rel <= 5e-3, (tag, rel)
+    assert d_lse <= 1e-3, (tag, "lse", d_lse)
+
+
+def cost(got, ref, got_lse, ref_lse, tag):
+    """Against the exact oracle: printed; bounded loosely (a few percent of
+    the logits' rounding reaches the output)."""
+    max_abs, rel = error_stats(got, ref)
+    d_lse = float(np.max(np.abs(got_lse - ref_lse)))
+    print(f"{tag} vs exact: max-abs {max_abs:.3e} rel-L2 {rel:.3e} lse {d_lse:.3e}", flush=True)
+    assert rel <= 0.1 and d_lse <= 0.2, (tag, rel, d_lse)
+
+
+def judge(case, out, lse, tag, seqs=None, heads=None):
+    ref, ref_lse = case.oracle_decode(seqs=seqs, heads=heads, fp8_queries=True)
+    check(out, ref, lse, ref_lse, tag)
+    ref, ref_lse = case.oracle_decode(seqs=seqs, heads=heads)
+    cost(out, ref, lse, ref_lse, tag)
+
+
+@pytest.mark.parametrize("q_len,splits", [(1, 2), (2, 2), (1, 0), (2, 0)])
+def test_fp8_scores_mid(q_len, splits):
+    wl = MID.replace(q_len=q_len)
+    announce("v3_mid_fp8s", "q_len", q_len, "splits", splits)
+    case = build_case(wl)
+    out, lse = run_fp8s(case, splits)
+    judge(case, out, lse, f"fp8 scores mid q_len={q_len} splits={splits}")
+
+
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 129])
+@pytest.mark.parametrize("q_len", [1, 2])
+def test_fp8_scores_edge_lengths(L, q_len):
+    """Partial tiles: rows past the sequence end hold NaN-poisoned codes and
+    scales, which must not reach the output."""
+    wl = MID.replace(name="v3_edge_fp8s", batch=2, ctx_lo=L, ctx_hi=L, q_len=q_len)
+    announce("v3_edge_fp8s", "L", L, "q_len", q_len)
+    case = build_case(wl)
+    out, lse = run_fp8s(case, 0)
+    judge(case, out, lse, f"fp8 scores edge L={L} q={q_len}")
+
+
+def test_fp8_scores_full_size_sampled():
+    wl = W["v3_b128_ctx8k32k_fp8_q2"]
+    lens = synth.seq_lens(wl)
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), wl.batch // 2})
+    announce(wl.name, "fp8 scores", "sampled seqs", seqs)
+    case = build_case(wl, fill=seqs)
+    out, lse = run_fp8s(case, wl.num_splits)
+    rng = np.random.default_rng(0)
+    heads = np.sort(rng.choice(wl.n_heads, size=8, replace=False))
+    judge(case, out[seqs][:, :, heads], lse[seqs][:, :, heads], wl.name + " fp8 scores",
+          seqs=seqs, heads=heads)
