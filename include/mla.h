@@ -109,8 +109,8 @@ typedef struct {
  * even) after division by one power of two 2^e, the smallest with
  * amax |q| <= 448 * 2^e, i.e. up to 2^-4 relative error per query element.
  * The value product stays bf16.  This trades accuracy for speed: with the
- * default the scores use bf16 queries against the dequantised cache.  The
- * append ignores flags. */
+ * default the scores use bf16 queries against the codes' exact values, with
+ * the token scale applied in fp32.  The append ignores flags. */
 enum { MLA_FLAG_FP8_SCORES = 1 };
 
 /* Status name, e.g. "MLA_ERR_BAD_SHAPE". Never NULL. */

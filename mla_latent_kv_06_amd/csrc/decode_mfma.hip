@@ -272,11 +272,13 @@ __device__ __forceinline__ void issue_tile_fp8_padded(const unsigned char* __res
     }
 }
 
-// Padded fp8 staging -> dequantised bf16 tile, latent channels only (the
-// scores read the codes themselves).  Rows at or beyond `valid` become zeros.
-__device__ __forceinline__ void convert_tile_fp8_latent(const lds_u8* lstage, lds_u8* ltile, int tid,
+// Padded fp8 staging -> bf16 tile of the codes' values, latent channels only
+// (the scores read the codes themselves).  Rows at or beyond `valid` become
+// zeros, and so do their token scales.
+__device__ __forceinline__ void convert_tile_fp8_latent(lds_u8* lstage, lds_u8* ltile, int tid,
                                                         int valid) {
-    const MLA_LDS float* lscale = reinterpret_cast<const MLA_LDS float*>(lstage + F8SCODES);
+    MLA_LDS float* lscale = reinterpret_cast<MLA_LDS float*>(lstage + F8SCODES);
+    if (tid < BS && tid >= valid) lscale[tid] = 0.f;
 #pragma unroll 1
     for (int k = 0; k < 8; ++k) {
         const int p = k * 256 + tid;                   // 64 rows x 32 latent chunks
@@ -284,13 +286,12 @@ __device__ __forceinline__ void convert_tile_fp8_latent(const lds_u8* lstage, ld
         u32x4 outw[2];
         if (t < valid) {
             const u32x4 raw = *reinterpret_cast<const MLA_LDS u32x4*>(lstage + (t * F8ROW + c) * 16);
-            const float sc = lscale[t];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[q], false);
                 const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[q], true);
-                const unsigned int p0 = f32_to_bf16_bits(lo[0] * sc) | ((unsigned)f32_to_bf16_bits(lo[1] * sc) << 16);
-                const unsigned int p1 = f32_to_bf16_bits(hi[0] * sc) | ((unsigned)f32_to_bf16_bits(hi[1] * sc) << 16);
+                const unsigned int p0 = f32_to_bf16_bits(lo[0]) | ((unsigned)f32_to_bf16_bits(lo[1]) << 16);
+                const unsigned int p1 = f32_to_bf16_bits(hi[0]) | ((unsigned)f32_to_bf16_bits(hi[1]) << 16);
                 outw[q >> 1][(q & 1) * 2 + 0] = p0;
                 outw[q >> 1][(q & 1) * 2 + 1] = p1;
             }
@@ -303,11 +304,15 @@ __device__ __forceinline__ void convert_tile_fp8_latent(const lds_u8* lstage, ld
     }
 }
 
-// fp8 staging (+ scales) -> dequantised bf16 swizzled tile (value * token
-// scale, RNE).  Rows at or beyond `valid` become zeros.
-__device__ __forceinline__ void convert_tile_fp8(const lds_u8* lstage, lds_u8* ltile, int tid,
+// fp8 staging -> bf16 swizzled tile of the codes' values.  Every e4m3 value is
+// a bf16 value (3 of 7 mantissa bits, a narrower exponent range), so the copy
+// is exact; the token scale is applied to the scores and the weights instead.
+// Rows at or beyond `valid` become zeros, and so do their token scales (past a
+// sequence's end a block may hold anything).
+__device__ __forceinline__ void convert_tile_fp8(lds_u8* lstage, lds_u8* ltile, int tid,
                                                  int valid) {
-    const MLA_LDS float* lscale = reinterpret_cast<const MLA_LDS float*>(lstage + F8TILE);
+    MLA_LDS float* lscale = reinterpret_cast<MLA_LDS float*>(lstage + F8TILE);
+    if (tid < BS && tid >= valid) lscale[tid] = 0.f;
 #pragma unroll 1
     for (int k = 0; k < 9; ++k) {
         const int p = k * 256 + tid;                   // 2304 fp8 chunks
@@ -315,13 +320,12 @@ __device__ __forceinline__ void convert_tile_fp8(const lds_u8* lstage, lds_u8* l
         u32x4 outw[2];
         if (t < valid) {
             const u32x4 raw = *reinterpret_cast<const MLA_LDS u32x4*>(lstage + p * 16);
-            const float sc = lscale[t];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[q], false);
                 const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[q], true);
-                const unsigned int p0 = f32_to_bf16_bits(lo[0] * sc) | ((unsigned)f32_to_bf16_bits(lo[1] * sc) << 16);
-                const unsigned int p1 = f32_to_bf16_bits(hi[0] * sc) | ((unsigned)f32_to_bf16_bits(hi[1] * sc) << 16);
+                const unsigned int p0 = f32_to_bf16_bits(lo[0]) | ((unsigned)f32_to_bf16_bits(lo[1]) << 16);
+                const unsigned int p1 = f32_to_bf16_bits(hi[0]) | ((unsigned)f32_to_bf16_bits(hi[1]) << 16);
                 outw[q >> 1][(q & 1) * 2 + 0] = p0;
                 outw[q >> 1][(q & 1) * 2 + 1] = p1;
             }
@@ -671,6 +675,21 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                 };
                 f32x16 sacc = {};
                 float sv[16];
+                // fp8: token scales of the lane's rows 32 hb + 8 (i/4) + 4 hf + (i%4)
+                // (zero past the sequence end), applied to the scores and folded
+                // into the weights, so that keys and values enter the products as
+                // the codes' exact values
+                [[maybe_unused]] float tsc[16];
+                if constexpr (FP8) {
+                    const MLA_LDS float* lsc =
+                        reinterpret_cast<const MLA_LDS float*>(stg + (F8S ? F8SCODES : F8TILE));
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 ks4 = *reinterpret_cast<const MLA_LDS f32x4*>(lsc + hb * 32 + 8 * g + 4 * hf);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) tsc[4 * g + j] = ks4[j];
+                    }
+                }
                 if constexpr (F8S) {
                     // codes of rows 32 hb + l32, channels 64 s + 32 hf .. +32: two
                     // consecutive 16-byte chunks of the padded staging row
@@ -690,15 +709,8 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                         a0 = a1;
                         a1 = a2;
                     }
-                    // token scales of the lane's rows 32 hb + 8 g + 4 hf .. +4
-                    const MLA_LDS float* lsc = reinterpret_cast<const MLA_LDS float*>(stg + F8SCODES);
-                    const float qs = qscale * scale_log2;
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4 ks4 = *reinterpret_cast<const MLA_LDS f32x4*>(lsc + hb * 32 + 8 * g + 4 * hf);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) sv[4 * g + j] = sacc[4 * g + j] * qs * ks4[j];
-                    }
+                    for (int i = 0; i < 16; ++i) sv[i] = sacc[i] * qscale * tsc[i];
                 } else {
                     bf16x8 a0 = ka(0), a1 = ka(1), a2;
 #pragma unroll
@@ -712,7 +724,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                         a1 = a2;
                     }
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) sv[i] = sacc[i] * scale_log2;
+                    for (int i = 0; i < 16; ++i) sv[i] = FP8 ? sacc[i] * tsc[i] : sacc[i];
                 }
                 // lane holds head `head`, tokens 32 hb + 8 (i/4) + 4 hf + (i%4)
                 if (valid < BS) {
@@ -722,15 +734,19 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                         if (tok >= valid) sv[i] = kNegInf;
                     }
                 }
+                // sv holds unscaled scores; the log2-domain score is sv * scale_log2
+                // (scale_log2 > 0, so maxima commute with the scaling).  Maxima and
+                // sums stay per lane here; the two lanes of a head (hf = 0, 1) are
+                // combined once per pass, not per half-tile.
                 float hmax = sv[0];
 #pragma unroll
                 for (int i = 1; i < 16; ++i) hmax = fmaxf(hmax, sv[i]);
-                hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
+                hmax *= scale_log2;
                 if (mode == 1) {
                     m_ref = fmaxf(m_ref, hmax);
                     continue;
                 }
-                if (mode == 0 && t == t0 && hb == 0) m_ref = hmax;
+                if (mode == 0 && t == t0 && hb == 0) m_ref = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
                 // (cannot hold in the exact-reference pass: the scan saw the same
                 // maxima, so at most three passes run)
                 overflow |= hmax > m_ref + kMaxLead;
@@ -742,13 +758,12 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                     u16x8 pu;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        const float pv = __builtin_amdgcn_exp2f(sv[k2 * 8 + j] - m_ref);
+                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[k2 * 8 + j], scale_log2, -m_ref));
                         psum += pv;
-                        pu[j] = f32_to_bf16_bits(pv);
+                        pu[j] = f32_to_bf16_bits(FP8 ? pv * tsc[k2 * 8 + j] : pv);
                     }
                     pf[k2] = __builtin_bit_cast(bf16x8, pu);
                 }
-                psum += __shfl_xor(psum, 32, 64);
                 l_run += psum;
 
                 // ---- O^T += V^T . P^T (latent columns of the same rows) -----------------
@@ -820,12 +835,14 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                 m_ref = kNegInf;
                 continue;
             }
-            if (mode == 1) {
+            if (mode == 1) {             // the scan's maxima: both lanes of each head
+                m_ref = fmaxf(m_ref, __shfl_xor(m_ref, 32, 64));
                 mode = 2;
                 continue;
             }
             break;
         }
+        l_run += __shfl_xor(l_run, 32, 64);  // the head's two lanes hold disjoint tokens
 
         // ---- epilogue: normalised partial o_lat (fp16) and log-sum-exp ---------------
         // The partial is a convex combination of latent rows: fp16 keeps it to

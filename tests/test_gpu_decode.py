@@ -175,26 +175,57 @@ def test_balanced_schedule_ragged(q_len, lo, hi, batch):
     assert np.all(got[~vis] == 0) and np.all(np.isneginf(got_lse[~vis]))
 
 
-def test_softmax_reference_restart():
-    """Rotary keys of each sequence's last tokens scaled by 60: their scores
+def _restart_case(cache_dtype):
+    """Rotary keys of each sequence's last 40 tokens scaled by 60: their scores
     exceed the first tile's maximum by far more than the kernel's fixed
     reference allows, forcing its restart path (max scan + exact-reference
-    pass).  Values (latents) are untouched, so outputs stay O(1)."""
-    wl = MID.replace(name="v3_restart", batch=2, ctx_lo=300, ctx_hi=300)
+    pass).  Values (latents) are untouched, so outputs stay O(1).  An fp8 row
+    is requantised as a whole (its token scale covers all 576 channels)."""
+    wl = MID.replace(name="v3_restart", batch=2, ctx_lo=300, ctx_hi=300, cache_dtype=cache_dtype)
     case = build_case(wl)
     D, dc = wl.row_width, wl.kv_lora_rank
     flat = case.pool.reshape(-1, D)
+    sflat = None if case.scale is None else case.scale.reshape(-1)
     for b in range(wl.batch):
         L = int(case.seq_lens[b])
         for j in range(L - 40, L):
             p = casebuild.oracle.slot_index(case.block_table, b, j, wl.block_size)
-            kr = casebuild.oracle.bf16_bits_to_f64(flat[p, dc:])
-            flat[p, dc:] = casebuild.to_bf16_bits(kr * 60.0)
-    announce("v3_restart")
-    _, out, lse = run(case, num_splits=1)
+            if cache_dtype == "bf16":
+                kr = casebuild.oracle.bf16_bits_to_f64(flat[p, dc:])
+                flat[p, dc:] = casebuild.to_bf16_bits(kr * 60.0)
+            else:
+                row = casebuild.oracle.dequantize_rows_fp8(flat[p][None], sflat[p:p + 1])[0]
+                row[dc:] *= 60.0
+                codes, sc = casebuild.oracle.quantize_rows_fp8(row[None])
+                flat[p], sflat[p] = codes[0], sc[0]
+    return case
+
+
+@pytest.mark.parametrize("cache_dtype,splits", [("bf16", 1), ("bf16", 0), ("fp8", 0)])
+def test_softmax_reference_restart(cache_dtype, splits):
+    case = _restart_case(cache_dtype)
+    announce("v3_restart", cache_dtype, "splits", splits)
+    _, out, lse = run(case, num_splits=splits)
     ref, ref_lse = case.oracle_decode()
     assert ref_lse.max() > 40
-    check(out, ref, "bf16", lse, ref_lse, "v3_restart")
+    check(out, ref, cache_dtype, lse, ref_lse, f"v3_restart {cache_dtype} splits={splits}")
+
+
+def test_softmax_reference_restart_fp8_scores():
+    from mla_latent_kv_06_amd import binding as b
+    case = _restart_case("fp8")
+    announce("v3_restart", "fp8 scores")
+    dc = G().DeviceCase(case)
+    dc.dims = b.Dims.from_workload(case.wl, flags=b.FLAG_FP8_SCORES)
+    out, lse = dc.decode(num_splits=0)
+    out, lse = G().to_np(out), G().to_np(lse)
+    ref, ref_lse = case.oracle_decode(fp8_queries=True)
+    assert ref_lse.max() > 40
+    max_abs, rel = error_stats(out, ref)
+    d_lse = float(np.max(np.abs(lse - ref_lse)))
+    print(f"v3_restart fp8 scores: max-abs {max_abs:.3e} rel-L2 {rel:.3e} lse {d_lse:.3e}", flush=True)
+    assert np.isfinite(out).all()
+    assert max_abs <= 6e-2 and rel <= 5e-3 and d_lse <= 1e-2, (max_abs, rel, d_lse)
 
 
 # ---------------------------------------------------------------------------

@@ -5,7 +5,7 @@ Parity: the option rounds every absorbed query vector to e4m3 with one scale
 per (row, head) and multiplies the stored cache codes directly; the oracle's
 ``decode_fp8_queries`` is that definition in float64, so the kernel is held to
 the fp8-cache bar against it (max-abs <= 6e-2 and rel-L2 <= 5e-3 over the
-output, log-sum-exp within 1e-3).
+output, log-sum-exp within 1e-2 as for the default decode).
 
 Accuracy cost: the same output against the exact oracle (``decode_naive``) is
 printed, with a loose sanity bound.  With few visible tokens the output moves
@@ -48,7 +48,7 @@ def check(got, ref, got_lse, ref_lse, tag):
     assert np.isfinite(got).all(), tag
     assert max_abs <= 6e-2, (tag, max_abs)
     assert rel <= 5e-3, (tag, rel)
-    assert d_lse <= 1e-3, (tag, "lse", d_lse)
+    assert d_lse <= 1e-2, (tag, "lse", d_lse)
 
 
 def cost(got, ref, got_lse, ref_lse, tag):
