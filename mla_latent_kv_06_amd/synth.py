@@ -16,6 +16,9 @@ Value distributions (all draws standard normal, then scaled by a constant):
 * W_UK [H, N, d_c], W_UV [H, V, d_c]: N(0, 1) / sqrt(d_c)  (std 1/sqrt(fan_in),
   fan_in = d_c, the up-projections' input width).
 * W_kv,a [d_c + R, d]: N(0, 1) / sqrt(d).
+* query path: W_DQ [d_q, d]: N(0, 1) / sqrt(d); W_UQ [H N, f] and W_QR [H R, f]:
+  N(0, 1) / sqrt(f), f = d_q (or d for full-rank queries, d_q = 0); the query
+  norm's gamma [d_q]: 1 + 0.1 N(0, 1).
 * sequence lengths: uniform integers on the closed range.
 * block tables: ceil(L/bs) blocks per sequence taken in order from one random
   permutation of a shared pool (or the identity for contiguous caches); the
@@ -30,7 +33,10 @@ import math
 import numpy as np
 
 # stream tags
-_LENGTHS, _BLOCKS, _CACHE, _QNOPE, _QPE, _WUK, _WUV, _H, _WKVA = range(9)
+_LENGTHS, _BLOCKS, _CACHE, _QNOPE, _QPE, _WUK, _WUV, _H, _WKVA, _WDQ, _WUQ, _WQR, _QG = range(13)
+
+# query compression width of the DeepSeek-V3 shape (0 = full-rank queries)
+Q_LORA_RANK_V3 = 1536
 
 
 @dataclasses.dataclass(frozen=True)
@@ -172,3 +178,32 @@ def hidden(wl: Workload, n_new: int | None = None, seed: int = 0) -> np.ndarray:
 def w_kv_a(wl: Workload, seed: int = 0) -> np.ndarray:
     w = _normal(_rng(seed, _WKVA), (wl.row_width, wl.d_model))
     return w * np.float32(1.0 / math.sqrt(wl.d_model))
+
+
+def w_dq(wl: Workload, q_lora_rank: int, seed: int = 0) -> np.ndarray:
+    """Query down-projection [d_q, d]."""
+    w = _normal(_rng(seed, _WDQ), (q_lora_rank, wl.d_model))
+    return w * np.float32(1.0 / math.sqrt(wl.d_model))
+
+
+def _q_fan_in(wl: Workload, q_lora_rank: int) -> int:
+    return q_lora_rank if q_lora_rank > 0 else wl.d_model
+
+
+def w_uq(wl: Workload, q_lora_rank: int, seed: int = 0) -> np.ndarray:
+    """Query content up-projection [H * N, d_q] (or [H * N, d] at d_q = 0)."""
+    f = _q_fan_in(wl, q_lora_rank)
+    w = _normal(_rng(seed, _WUQ), (wl.n_heads * wl.qk_nope_dim, f))
+    return w * np.float32(1.0 / math.sqrt(f))
+
+
+def w_qr(wl: Workload, q_lora_rank: int, seed: int = 0) -> np.ndarray:
+    """Query rotary projection [H * R, d_q] (or [H * R, d] at d_q = 0)."""
+    f = _q_fan_in(wl, q_lora_rank)
+    w = _normal(_rng(seed, _WQR), (wl.n_heads * wl.qk_rope_dim, f))
+    return w * np.float32(1.0 / math.sqrt(f))
+
+
+def q_norm_gamma(q_lora_rank: int, seed: int = 0) -> np.ndarray:
+    """Query-latent norm weights [d_q]: 1 + 0.1 N(0, 1)."""
+    return np.float32(1.0) + np.float32(0.1) * _normal(_rng(seed, _QG), (q_lora_rank,))

@@ -18,6 +18,8 @@ Parity status of each public function (what pins it is listed in
                              the query rounding allows)
 * ``round_to_bf16``          pinned (vs torch.bfloat16 on binary32 inputs, ties)
 * ``append_rows``            pinned (brute force, RMSNorm / RoPE invariants)
+* ``query_rows``             pinned (head-block layout, query/key relative
+                             position, norm scale invariance, full rank)
 * ``rmsnorm``, ``rope``      pinned (closed-form invariants, complex form)
 * ``slot_index``, ``gather_sequence``  pinned (brute force, permutation)
 * ``e4m3fn_decode`` / ``e4m3fn_encode`` / ``quantize_rows_fp8``
@@ -33,6 +35,7 @@ from .mla_ref import (  # noqa: F401
     rmsnorm,
     rope,
     append_rows,
+    query_rows,
     slot_index,
     gather_sequence,
     decode_naive,

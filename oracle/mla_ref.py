@@ -119,6 +119,33 @@ def append_rows(h, w_kv_a, gamma, eps, positions, kv_lora_rank, rope_base=10000.
     return np.concatenate([lat, kr], axis=1)
 
 
+def query_rows(h, w_dq, q_gamma, eps, w_uq, w_qr, positions, n_heads, rope_base=10000.0):
+    """Query path of "DeepSeek-V2: MLA Explained", "MLA Full Formulas", step 1
+    (query compression), in float64:
+
+      c_Q   = W_DQ h                         (h itself when w_dq is None:
+                                              full-rank queries, q_lora_rank 0)
+      c_Q   = RMSNorm(c_Q) * gamma           when q_gamma is given (the V3
+                                              reading: "KV Compression --
+                                              DeepSeek-V3" notes RMSNorm after
+                                              the compressed latent vectors)
+      q^C   = W_UQ c_Q,  split into n_heads blocks [q^C_1; ...; q^C_H]
+      q^R   = RoPE(W_QR c_Q), per head block, at the token's position
+
+    h [T, d]; w_dq [d_q, d]; w_uq [H * N, d_q]; w_qr [H * R, d_q];
+    positions [T].  Returns (q_nope [T, H, N], q_pe [T, H, R])."""
+    h = np.asarray(h, dtype=np.float64)
+    c = h if w_dq is None else h @ np.asarray(w_dq, dtype=np.float64).T
+    if q_gamma is not None:
+        c = rmsnorm(c, q_gamma, eps)
+    T = c.shape[0]
+    q_nope = (c @ np.asarray(w_uq, dtype=np.float64).T).reshape(T, n_heads, -1)
+    qr = (c @ np.asarray(w_qr, dtype=np.float64).T).reshape(T, n_heads, -1)
+    pos = np.asarray(positions, dtype=np.float64)
+    q_pe = np.stack([rope(qr[:, i, :], pos, rope_base) for i in range(n_heads)], axis=1)
+    return q_nope, q_pe
+
+
 def slot_index(block_table: np.ndarray, b: int, pos: int, block_size: int) -> int:
     """Physical row (block * block_size + offset) that token ``pos`` of
     sequence ``b`` occupies in the paged pool."""

@@ -568,3 +568,85 @@ def test_fp8_queries_lse_within_query_rounding_bound():
                 assert d <= bound, (b, s, i, d, bound)
                 moved += d > 1e-9
     assert moved >= B * Sq * H // 2         # the rounding does change the scores
+
+
+# --------------------------------------------------------------------------
+# query path
+# --------------------------------------------------------------------------
+
+def test_query_rows_head_blocks_follow_the_concatenation():
+    """With W_UQ = identity (d_q = H N) the content query of head i is the
+    i-th block of c_Q: [q^C_1; ...; q^C_H] = q^C, blocks in head order."""
+    rng = np.random.default_rng(30)
+    H, N, R, T = 3, 4, 2, 5
+    c = rng.standard_normal((T, H * N))
+    w_qr = rng.standard_normal((H * R, H * N))
+    q_nope, q_pe = oracle.query_rows(c, None, None, 0.0, np.eye(H * N), w_qr, np.zeros(T), H)
+    for i in range(H):
+        np.testing.assert_array_equal(q_nope[:, i, :], c[:, i * N:(i + 1) * N])
+    # position 0 rotates nothing: the rotary block is W_QR c as it is
+    np.testing.assert_allclose(q_pe.reshape(T, -1), c @ w_qr.T, rtol=1e-13, atol=1e-13)
+
+
+def test_query_rows_rotary_dot_products_depend_on_relative_position():
+    """q^R (at position a, this path) against k^R (at position b, the append's
+    rotation) depends only on a - b: query and key rotate pairs alike."""
+    rng = np.random.default_rng(31)
+    H, N, R, d, dq = 2, 4, 8, 16, 12
+    h = rng.standard_normal((1, d))
+    w_dq = rng.standard_normal((dq, d))
+    w_uq = rng.standard_normal((H * N, dq))
+    w_qr = rng.standard_normal((H * R, dq))
+    key_pre = rng.standard_normal(R)
+    for a, b in [(5, 2), (1000, 997), (131075, 131072)]:
+        _, qa = oracle.query_rows(h, w_dq, None, 0.0, w_uq, w_qr, [a], H)
+        kb = oracle.rope(key_pre[None], [b])[0]
+        _, q0 = oracle.query_rows(h, w_dq, None, 0.0, w_uq, w_qr, [a - b], H)
+        k0 = oracle.rope(key_pre[None], [0])[0]
+        np.testing.assert_allclose(qa[0] @ kb, q0[0] @ k0, rtol=1e-8, atol=1e-8)
+
+
+def test_query_rows_norm_is_scale_invariant():
+    rng = np.random.default_rng(32)
+    H, N, R, d, dq, T = 2, 4, 4, 16, 8, 3
+    h = rng.standard_normal((T, d))
+    w_dq = rng.standard_normal((dq, d))
+    w_uq = rng.standard_normal((H * N, dq))
+    w_qr = rng.standard_normal((H * R, dq))
+    g = 1 + 0.1 * rng.standard_normal(dq)
+    pos = [0, 7, 100]
+    a = oracle.query_rows(h, w_dq, g, 0.0, w_uq, w_qr, pos, H)
+    b = oracle.query_rows(3.5 * h, w_dq, g, 0.0, w_uq, w_qr, pos, H)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-12)
+    # without the norm the queries scale with h
+    c = oracle.query_rows(h, w_dq, None, 0.0, w_uq, w_qr, pos, H)
+    e = oracle.query_rows(3.5 * h, w_dq, None, 0.0, w_uq, w_qr, pos, H)
+    for x, y in zip(c, e):
+        np.testing.assert_allclose(3.5 * x, y, rtol=1e-12, atol=1e-12)
+    # the normalised latent has RMS |gamma|-weighted 1: with gamma = 1 and an
+    # identity up-projection, the content queries have unit mean square
+    qn, _ = oracle.query_rows(h, w_dq, np.ones(dq), 0.0, np.eye(dq), w_qr[:, :dq], pos, dq // 4)
+    np.testing.assert_allclose(np.mean(qn.reshape(T, -1) ** 2, axis=1), 1.0, rtol=1e-12)
+    # gamma weights the normalised latent channel by channel
+    qg, _ = oracle.query_rows(h, w_dq, g, 0.0, np.eye(dq), w_qr[:, :dq], pos, dq // 4)
+    np.testing.assert_allclose(qg.reshape(T, -1), qn.reshape(T, -1) * g, rtol=1e-12, atol=1e-12)
+
+
+def test_query_rows_full_rank_is_the_direct_projection():
+    """q_lora_rank 0: no down-projection and no norm, q^C = W_UQ h."""
+    rng = np.random.default_rng(33)
+    H, N, R, d, T = 2, 3, 4, 6, 2
+    h = rng.standard_normal((T, d))
+    w_uq = rng.standard_normal((H * N, d))
+    w_qr = rng.standard_normal((H * R, d))
+    q_nope, q_pe = oracle.query_rows(h, None, None, 0.0, w_uq, w_qr, [3, 9], H)
+    for t in range(T):
+        for i in range(H):
+            for n in range(N):
+                want = sum(w_uq[i * N + n, k] * h[t, k] for k in range(d))
+                assert abs(q_nope[t, i, n] - want) < 1e-12
+    # rotation keeps each pair's length
+    pre = (h @ w_qr.T).reshape(T, H, R // 2, 2)
+    np.testing.assert_allclose(np.linalg.norm(q_pe.reshape(T, H, R // 2, 2), axis=-1),
+                               np.linalg.norm(pre, axis=-1), rtol=1e-12)
