@@ -79,6 +79,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--fp8-scores", action="store_true",
                    help="fp8 cache: score product on the fp8 matrix cores (MLA_FLAG_FP8_SCORES)")
+    p.add_argument("--query-path", action="store_true",
+                   help="add the query path (W_DQ, norm, W_UQ / W_QR, RoPE) to each step")
     p.add_argument("--cpu-tokens", type=int, default=262144,
                    help="CPU-baseline sample: first sequences of layer 0 up to this many cached tokens")
     p.add_argument("--report", default=None)
@@ -91,7 +93,7 @@ def parse():
 class Layer:
     """One layer's device tensors."""
 
-    def __init__(self, wl, li, dims, dev, torch, synth, b):
+    def __init__(self, wl, li, dims, dev, torch, synth, b, query_path=False):
         seed = 1000 + li
         B, H = wl.batch, wl.n_heads
         bf = torch.bfloat16
@@ -106,6 +108,12 @@ class Layer:
         self.w_kv_a = up(synth.w_kv_a(wl, seed))
         self.gamma = torch.ones(wl.kv_lora_rank, dtype=bf, device=dev)
         self.h = up(synth.hidden(wl, seed=seed))
+        if query_path:                   # query compression weights (d_q = 1536)
+            ql = synth.Q_LORA_RANK_V3
+            self.w_dq = up(synth.w_dq(wl, ql, seed))
+            self.q_gamma = up(synth.q_norm_gamma(ql, seed))
+            self.w_uq = up(synth.w_uq(wl, ql, seed))
+            self.w_qr = up(synth.w_qr(wl, ql, seed))
         cached = synth.cached_lengths(wl, seed)
         seq_lens = (cached + wl.q_len).astype(np.int32)
         table, nblk = synth.block_tables(seq_lens, wl.block_size, wl.paged, seed)
@@ -167,7 +175,10 @@ def main():
     splits = wl.num_splits if args.splits is None else args.splits
 
     t_setup = time.time()
-    layers = [Layer(wl, li, dims, dev, torch, synth, b) for li in range(args.layers)]
+    layers = [Layer(wl, li, dims, dev, torch, synth, b, args.query_path) for li in range(args.layers)]
+    ql = synth.Q_LORA_RANK_V3 if args.query_path else 0
+    ws_q = (torch.empty(max(1, b.query_workspace_size(dims, B, Sq, wl.d_model, ql)), dtype=torch.uint8,
+                        device=dev) if args.query_path else None)
     ws_dec = torch.empty(b.decode_workspace_size(dims, B, Sq, splits), dtype=torch.uint8, device=dev)
     ws_app = torch.empty(max(1, b.append_workspace_size(dims, B, Sq, wl.d_model)),
                          dtype=torch.uint8, device=dev)
@@ -178,10 +189,18 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    def step(L, ev=None):
+    def step(L, ev=None, qev=None):
         if wl.append:
             b.append(dims, L.h, L.w_kv_a, L.gamma, L.block_table, L.start_pos, L.pool, L.scale,
                      rms_eps=1e-6, rope_base=10000.0, workspace=ws_app)
+        if args.query_path:              # the decode's queries from the layer input
+            if qev is not None:
+                qev[0].record(stream)
+            b.query_project(dims, L.h, L.w_dq, L.q_gamma, L.w_uq, L.w_qr, L.start_pos,
+                            rms_eps=1e-6, rope_base=10000.0, q_nope=L.q_nope, q_pe=L.q_pe,
+                            workspace=ws_q)
+            if qev is not None:
+                qev[1].record(stream)
         common = (dims, L.q_nope, L.q_pe, L.w_uk, L.w_uv, L.pool, L.scale, L.block_table,
                   L.seq_lens)
         b.decode(*common, num_splits=splits, out=L.out, lse=L.lse, workspace=ws_dec,
@@ -200,6 +219,8 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    qevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
     t0 = torch.cuda.Event(enable_timing=True)
@@ -209,12 +230,13 @@ def main():
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(K):
-        step(layers[i % len(layers)], evs[i])
+        step(layers[i % len(layers)], evs[i], qevs[i] if args.query_path else None)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / K
     k_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    q_ms = np.array([e0.elapsed_time(e1) for e0, e1 in qevs]) if args.query_path else None
     k_avg_s = float(k_ms.mean()) / 1e3
 
     tokens_per_step = B * Sq
@@ -264,8 +286,8 @@ def main():
             "layers_rotated": args.layers,
             "cache_dtype": wl.cache_dtype,
             "fp8_scores": bool(args.fp8_scores),
-            "step": ("cache append of %d token(s)/seq + absorbed decode, one layer" % Sq
-                     if wl.append else "absorbed decode, one layer"),
+            "step": (("cache append of %d token(s)/seq + " % Sq if wl.append else "")
+                     + ("query path + " if args.query_path else "") + "absorbed decode, one layer"),
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
@@ -284,6 +306,19 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.query_path:
+        # algorithmic bytes: the three weights, gamma, h and the two outputs
+        ql, d = synth.Q_LORA_RANK_V3, wl.d_model
+        hq = H * (wl.qk_nope_dim + wl.qk_rope_dim)
+        q_bytes = 2 * (ql * d + ql + hq * ql + B * Sq * d + B * Sq * hq)
+        q_s = float(q_ms.mean()) / 1e3
+        result["config"]["q_lora_rank"] = ql
+        result["query_path"] = {
+            "avg_us": round(q_s * 1e6, 2), "algorithmic_bytes": q_bytes,
+            "gbs": round(q_bytes / q_s / 1e9, 1), "frac": round(q_bytes / q_s / 1e9 / HBM_PEAK_GBS, 4),
+        }
+        log(f"query path {q_s * 1e6:.1f} us: {q_bytes / 1e6:.1f} MB -> {q_bytes / q_s / 1e9:.0f} GB/s "
+            f"({q_bytes / q_s / 1e9 / HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, wl, layers[0], torch)

@@ -236,6 +236,53 @@ mla_status mla_decode_absorbed_stages(const mla_dims* dims, int32_t batch, int32
                                       size_t workspace_bytes, uint32_t stages,
                                       void* stream);
 
+/* ---- query path ------------------------------------------------------------
+ *
+ * The decode's query inputs from the layer input ("DeepSeek-V2: MLA
+ * Explained", "MLA Full Formulas", step 1, query compression).  For query row
+ * s of sequence b, at position p = start_pos[b] + s:
+ *     c_Q = W_DQ h                            (h itself when q_lora_rank == 0:
+ *                                              full-rank queries)
+ *     c_Q = RMSNorm(c_Q) * q_norm_gamma       when q_norm_gamma is not NULL
+ *                                              (the norm V3 applies after its
+ *                                              compressed vectors, "KV
+ *                                              Compression -- DeepSeek-V3",
+ *                                              "How it works"); NULL leaves
+ *                                              the formula as printed
+ *     q^C = W_UQ c_Q,   q^R = RoPE(W_QR c_Q, p)
+ * split into head blocks [q_1; ...; q_H].  RoPE turns pairs (x[2k], x[2k+1])
+ * of each head's rotary block by p * rope_base^(-2k/qk_rope_dim), as the cache
+ * append turns the keys.  c_Q is rounded to bf16 between the two products;
+ * accumulation is fp32.
+ *
+ *  h            [batch][q_len][d_model] bf16
+ *  w_dq         [q_lora_rank][d_model] bf16 (NULL when q_lora_rank == 0)
+ *  q_norm_gamma [q_lora_rank] bf16 or NULL (must be NULL when q_lora_rank == 0)
+ *  w_uq         [n_heads * qk_nope_dim][f] bf16, f = q_lora_rank or d_model
+ *  w_qr         [n_heads * qk_rope_dim][f] bf16
+ *  start_pos    [batch] int32, device
+ *  q_nope       [batch][q_len][n_heads][qk_nope_dim] bf16 (out): the decode's q_nope
+ *  q_pe         [batch][q_len][n_heads][qk_rope_dim] bf16 (out): the decode's
+ *               q_pe, rotated
+ *  workspace    device scratch of mla_query_workspace_size bytes (0 bytes, and
+ *               NULL allowed, when q_lora_rank == 0)
+ *
+ * Requirements (else MLA_ERR_BAD_SHAPE / MLA_ERR_UNSUPPORTED): act_dtype
+ * MLA_BF16; d_model a multiple of 64 in [64, 65536]; q_lora_rank 0 or a
+ * multiple of 64 up to 2048; n_heads *
+ * qk_nope_dim and n_heads * qk_rope_dim multiples of 32; batch * q_len <=
+ * 65536; every operand under 2 GiB.  Every tensor 16-byte aligned.
+ * Of mla_dims only the head shape and act_dtype are used (all fields are
+ * validated as for the other calls). */
+mla_status mla_query_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                   int32_t d_model, int32_t q_lora_rank, size_t* bytes);
+mla_status mla_query_project(const mla_dims* dims, int32_t batch, int32_t q_len, int32_t d_model,
+                             int32_t q_lora_rank, const void* h, const void* w_dq,
+                             const void* q_norm_gamma, float rms_eps, const void* w_uq,
+                             const void* w_qr, float rope_base, const int32_t* start_pos,
+                             void* q_nope, void* q_pe, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,7 +38,7 @@ _TORCH_OF = {MLA_F32: (torch.float32,), MLA_BF16: (torch.bfloat16,),
 EXPORTED = ("mla_status_string", "mla_last_error", "mla_cache_row_bytes",
             "mla_cache_block_bytes", "mla_cache_append_workspace_size", "mla_cache_append",
             "mla_decode_default_splits", "mla_decode_workspace_size", "mla_decode_absorbed",
-            "mla_decode_absorbed_stages")
+            "mla_decode_absorbed_stages", "mla_query_workspace_size", "mla_query_project")
 
 
 class Dims(ctypes.Structure):
@@ -88,6 +88,11 @@ _lib.mla_decode_workspace_size.argtypes = [_DP, _I, _I, _I, ctypes.POINTER(_SZ)]
 _lib.mla_decode_absorbed.restype = ctypes.c_int
 _lib.mla_decode_absorbed.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I,
                                      _P, _P, _P, _SZ, _P]
+_lib.mla_query_workspace_size.restype = ctypes.c_int
+_lib.mla_query_workspace_size.argtypes = [_DP, _I, _I, _I, _I, ctypes.POINTER(_SZ)]
+_lib.mla_query_project.restype = ctypes.c_int
+_lib.mla_query_project.argtypes = [_DP, _I, _I, _I, _I, _P, _P, _P, ctypes.c_float, _P, _P,
+                                   ctypes.c_float, _P, _P, _P, _P, _SZ, _P]
 _lib.mla_decode_absorbed_stages.restype = ctypes.c_int
 _lib.mla_decode_absorbed_stages.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I,
                                             _P, _P, _P, _SZ, ctypes.c_uint32, _P]
@@ -136,6 +141,13 @@ def append_workspace_size(dims: Dims, batch: int, n_new: int, d_model: int) -> i
     n = _SZ(0)
     _check(_lib.mla_cache_append_workspace_size(ctypes.byref(dims), batch, n_new, d_model,
                                                 ctypes.byref(n)), "mla_cache_append_workspace_size")
+    return n.value
+
+
+def query_workspace_size(dims: Dims, batch: int, q_len: int, d_model: int, q_lora_rank: int) -> int:
+    n = _SZ(0)
+    _check(_lib.mla_query_workspace_size(ctypes.byref(dims), batch, q_len, d_model, q_lora_rank,
+                                         ctypes.byref(n)), "mla_query_workspace_size")
     return n.value
 
 
@@ -245,3 +257,45 @@ def append(dims: Dims, h, w_kv_a, kv_norm_gamma, block_table, start_pos, cache_p
 
 def softmax_scale(dims: Dims) -> float:
     return dims.softmax_scale or 1.0 / math.sqrt(dims.qk_nope_dim + dims.qk_rope_dim)
+
+
+def query_project(dims: Dims, h, w_dq, q_norm_gamma, w_uq, w_qr, start_pos,
+                  rms_eps: float = 1e-6, rope_base: float = 10000.0, q_nope=None, q_pe=None,
+                  workspace=None):
+    """The decode's query inputs from the layer input (mla_query_project).
+
+    h [B, Sq, d] bf16; w_dq [d_q, d] bf16, or None for full-rank queries
+    (d_q = 0); q_norm_gamma [d_q] bf16 or None; w_uq [H N, f], w_qr [H R, f]
+    bf16 (f = d_q, or d); start_pos [B] int32.  Returns (q_nope [B, Sq, H, N],
+    q_pe [B, Sq, H, R])."""
+    B, Sq, d = h.shape
+    H, N, R = dims.n_heads, dims.qk_nope_dim, dims.qk_rope_dim
+    dq = 0 if w_dq is None else w_dq.shape[0]
+    f = dq if dq else d
+    dev = h.device
+    bf = (torch.bfloat16,)
+    _need(h, "h", bf, None, dev)
+    if w_dq is not None:
+        _need(w_dq, "w_dq", bf, (dq, d), dev)
+    if q_norm_gamma is not None:
+        _need(q_norm_gamma, "q_norm_gamma", bf, (dq,), dev)
+    _need(w_uq, "w_uq", bf, (H * N, f), dev)
+    _need(w_qr, "w_qr", bf, (H * R, f), dev)
+    _need(start_pos, "start_pos", (torch.int32,), (B,), dev)
+    if q_nope is None:
+        q_nope = torch.empty((B, Sq, H, N), dtype=torch.bfloat16, device=dev)
+    if q_pe is None:
+        q_pe = torch.empty((B, Sq, H, R), dtype=torch.bfloat16, device=dev)
+    _need(q_nope, "q_nope", bf, (B, Sq, H, N), dev)
+    _need(q_pe, "q_pe", bf, (B, Sq, H, R), dev)
+    ws_bytes = query_workspace_size(dims, B, Sq, d, dq)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8,), None, dev)
+    st = _lib.mla_query_project(
+        ctypes.byref(dims), B, Sq, d, dq, _ptr(h), _ptr(w_dq), _ptr(q_norm_gamma), float(rms_eps),
+        _ptr(w_uq), _ptr(w_qr), float(rope_base), _ptr(start_pos), _ptr(q_nope), _ptr(q_pe),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev))
+    _check(st, "mla_query_project")
+    return q_nope, q_pe

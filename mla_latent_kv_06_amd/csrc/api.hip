@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "internal.hpp"
+#include "query.hpp"
 
 namespace {
 
@@ -191,6 +192,51 @@ mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const
     return ok();
 }
 
+// Query path: shape checks shared by the sizing call and the entry point.
+mla_status check_query_shape(const mla_dims* dims, int32_t batch, int32_t q_len, int32_t d_model,
+                             int32_t q_lora_rank) {
+    if (mla_status st = check_dims(dims); st != MLA_OK) return st;
+    const mla_dims& d = *dims;
+    if (d.act_dtype != MLA_BF16)
+        return fail(MLA_ERR_UNSUPPORTED, "the query path needs act_dtype MLA_BF16");
+    if (batch < 0 || q_len < 1 || q_len > 1024)
+        return fail(MLA_ERR_BAD_SHAPE, "batch=%d must be >= 0 and q_len=%d in [1, 1024]", batch, q_len);
+    if ((long long)batch * q_len > 65536)
+        return fail(MLA_ERR_BAD_SHAPE, "batch * q_len = %lld exceeds 65536", (long long)batch * q_len);
+    if (d_model < 64 || d_model > 65536 || d_model % 64)
+        return fail(MLA_ERR_BAD_SHAPE, "d_model=%d must be a multiple of 64 in [64, 65536]", d_model);
+    if (q_lora_rank < 0 || q_lora_rank > 2048 || q_lora_rank % 64)
+        return fail(MLA_ERR_BAD_SHAPE, "q_lora_rank=%d must be 0 or a multiple of 64 up to 2048",
+                    q_lora_rank);
+    if ((d.n_heads * d.qk_nope_dim) % 32 || (d.n_heads * d.qk_rope_dim) % 32)
+        return fail(MLA_ERR_UNSUPPORTED, "n_heads * qk_nope_dim and n_heads * qk_rope_dim must be "
+                                         "multiples of 32");
+    if (d.qk_rope_dim < 2)
+        return fail(MLA_ERR_UNSUPPORTED, "the query path needs qk_rope_dim >= 2");
+    const long long K = q_lora_rank ? q_lora_rank : d_model;
+    if ((long long)batch * q_len * K * 2 >= (1ll << 31) ||
+        (long long)d.n_heads * (d.qk_nope_dim + d.qk_rope_dim) * K * 2 >= (1ll << 31) ||
+        (long long)q_lora_rank * d_model * 2 >= (1ll << 31))
+        return fail(MLA_ERR_BAD_SHAPE, "a query-path operand exceeds 2 GiB");
+    return MLA_OK;
+}
+
+struct QueryWs {
+    size_t part, cq, total;
+    int kc;
+};
+
+QueryWs query_ws(int batch, int q_len, int d_model, int q_lora_rank) {
+    QueryWs w{};
+    if (q_lora_rank == 0) return w;
+    const size_t T = (size_t)batch * q_len;
+    w.kc = mla::query_splits(q_lora_rank, d_model);
+    w.part = 0;
+    w.cq = align_up((size_t)w.kc * T * q_lora_rank * 4, 256);
+    w.total = w.cq + align_up(T * q_lora_rank * 2, 256);
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -325,6 +371,67 @@ mla_status mla_decode_absorbed_stages(const mla_dims* dims, int32_t batch, int32
     return decode_impl(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
                        block_table, max_blocks_per_seq, seq_lens, num_splits, out, lse, workspace,
                        workspace_bytes, stages, stream);
+}
+
+mla_status mla_query_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                   int32_t d_model, int32_t q_lora_rank, size_t* bytes) {
+    if (mla_status st = check_query_shape(dims, batch, q_len, d_model, q_lora_rank); st != MLA_OK)
+        return st;
+    if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes is NULL");
+    *bytes = query_ws(batch, q_len, d_model, q_lora_rank).total;
+    return ok();
+}
+
+mla_status mla_query_project(const mla_dims* dims, int32_t batch, int32_t q_len, int32_t d_model,
+                             int32_t q_lora_rank, const void* h, const void* w_dq,
+                             const void* q_norm_gamma, float rms_eps, const void* w_uq,
+                             const void* w_qr, float rope_base, const int32_t* start_pos,
+                             void* q_nope, void* q_pe, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    if (mla_status st = check_query_shape(dims, batch, q_len, d_model, q_lora_rank); st != MLA_OK)
+        return st;
+    const mla_dims& d = *dims;
+    if (!(rms_eps >= 0.f) || !(rope_base > 0.f) || std::isinf(rope_base))
+        return fail(MLA_ERR_BAD_SHAPE, "rms_eps must be >= 0 and rope_base finite and > 0");
+    if (q_lora_rank == 0 && (w_dq || q_norm_gamma))
+        return fail(MLA_ERR_BAD_SHAPE, "q_lora_rank 0 (full-rank queries) takes no w_dq or q_norm_gamma");
+    if (batch == 0) return ok();
+    if (!h || !w_uq || !w_qr || !start_pos || !q_nope || !q_pe)
+        return fail(MLA_ERR_NULL_POINTER, "h, w_uq, w_qr, start_pos, q_nope and q_pe are required");
+    if (q_lora_rank > 0 && (!w_dq || !workspace))
+        return fail(MLA_ERR_NULL_POINTER, "w_dq and workspace are required when q_lora_rank > 0");
+    const QueryWs ws = query_ws(batch, q_len, d_model, q_lora_rank);
+    if (workspace_bytes < ws.total)
+        return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu", workspace_bytes, ws.total);
+    const void* ptrs[] = {h, w_dq, w_uq, w_qr, q_nope, q_pe, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(MLA_ERR_ALIGNMENT, "tensor at %p is not 16-byte aligned", p);
+    mla::QueryLaunch a;
+    a.H = d.n_heads;
+    a.N = d.qk_nope_dim;
+    a.R = d.qk_rope_dim;
+    a.T = batch * q_len;
+    a.q_len = q_len;
+    a.d_model = d_model;
+    a.q_lora = q_lora_rank;
+    a.h = h;
+    a.w_dq = w_dq;
+    a.gamma = q_norm_gamma;
+    a.eps = rms_eps;
+    a.rope_base = rope_base;
+    a.w_uq = w_uq;
+    a.w_qr = w_qr;
+    a.start_pos = start_pos;
+    a.q_nope = q_nope;
+    a.q_pe = q_pe;
+    char* base = static_cast<char*>(workspace);
+    a.part = q_lora_rank ? reinterpret_cast<float*>(base + ws.part) : nullptr;
+    a.kc = ws.kc;
+    a.cq = q_lora_rank ? reinterpret_cast<unsigned short*>(base + ws.cq) : nullptr;
+    a.stream = static_cast<hipStream_t>(stream);
+    const hipError_t e = mla::launch_query(a);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 }  // extern "C"

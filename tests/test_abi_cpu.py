@@ -141,3 +141,41 @@ def test_append_validation_rejects_before_launch(b):
     assert call(base=-1.0) == 2
     assert call(h=24) == 4
     assert call(n_new=0) == 0
+
+
+def test_query_workspace_sizes(b):
+    d = v3_dims(b)
+    kc = 16             # depth splits: 16 groups of 96 outputs x 16 = 256 workgroups
+    T = 64
+    raw = kc * T * 1536 * 4
+    want = (raw + 255) // 256 * 256 + (T * 1536 * 2 + 255) // 256 * 256
+    assert b.query_workspace_size(d, 64, 1, 7168, 1536) == want
+    assert b.query_workspace_size(d, 64, 1, 7168, 0) == 0       # full-rank queries
+    assert b.query_workspace_size(d, 0, 1, 7168, 1536) == 0
+
+
+def test_query_validation_rejects_before_launch(b):
+    lib = b.lib()
+    P = ctypes.c_void_p
+    def call(dims=None, **kw):
+        d = v3_dims(b) if dims is None else dims
+        a = dict(batch=2, q_len=1, d_model=7168, dq=1536, h=16, wdq=16, g=16, wuq=16, wqr=16,
+                 sp=16, qn=16, qp=16, ws=16, ws_bytes=1 << 40, eps=1e-6, base=10000.0)
+        a.update(kw)
+        pp = lambda v: None if v is None else P(v)
+        return lib.mla_query_project(ctypes.byref(d), a["batch"], a["q_len"], a["d_model"], a["dq"],
+                                     pp(a["h"]), pp(a["wdq"]), pp(a["g"]), a["eps"], pp(a["wuq"]),
+                                     pp(a["wqr"]), a["base"], pp(a["sp"]), pp(a["qn"]), pp(a["qp"]),
+                                     pp(a["ws"]), a["ws_bytes"], None)
+    assert call(h=None) == 1
+    assert call(wdq=None) == 1                                   # needed when d_q > 0
+    assert call(d_model=7160) == 2                               # not a multiple of 64
+    assert call(dq=96) == 2                                      # not a multiple of 64
+    assert call(dq=0) == 2                                       # full rank takes no w_dq / gamma
+    assert call(dq=0, wdq=None, g=None, ws=None, ws_bytes=0, h=24) == 4
+    assert call(ws_bytes=8) == 5
+    assert call(base=0.0) == 2
+    assert call(q_len=0) == 2
+    assert call(dims=b.Dims.make(128, 512, 64, 128, 128, 64, "bf16", "f32")) == 3
+    assert call(dims=b.Dims.make(3, 512, 2, 10, 128, 64, "bf16", "bf16")) == 3   # 3*10 % 32
+    assert call(batch=0) == 0
