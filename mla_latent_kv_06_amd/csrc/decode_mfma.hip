@@ -288,10 +288,11 @@ __device__ __forceinline__ void convert_tile_fp8_latent(lds_u8* lstage, lds_u8* 
             const u32x4 raw = *reinterpret_cast<const MLA_LDS u32x4*>(lstage + (t * F8ROW + c) * 16);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[q], false);
-                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[q], true);
-                const unsigned int p0 = f32_to_bf16_bits(lo[0]) | ((unsigned)f32_to_bf16_bits(lo[1]) << 16);
-                const unsigned int p1 = f32_to_bf16_bits(hi[0]) | ((unsigned)f32_to_bf16_bits(hi[1]) << 16);
+                // codes 4q, 4q+1 and 4q+2, 4q+3 as bf16 pairs (exact: unit scale)
+                const unsigned int p0 = __builtin_bit_cast(
+                    unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, false));
+                const unsigned int p1 = __builtin_bit_cast(
+                    unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, true));
                 outw[q >> 1][(q & 1) * 2 + 0] = p0;
                 outw[q >> 1][(q & 1) * 2 + 1] = p1;
             }
@@ -322,10 +323,11 @@ __device__ __forceinline__ void convert_tile_fp8(lds_u8* lstage, lds_u8* ltile, 
             const u32x4 raw = *reinterpret_cast<const MLA_LDS u32x4*>(lstage + p * 16);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[q], false);
-                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[q], true);
-                const unsigned int p0 = f32_to_bf16_bits(lo[0]) | ((unsigned)f32_to_bf16_bits(lo[1]) << 16);
-                const unsigned int p1 = f32_to_bf16_bits(hi[0]) | ((unsigned)f32_to_bf16_bits(hi[1]) << 16);
+                // codes 4q, 4q+1 and 4q+2, 4q+3 as bf16 pairs (exact: unit scale)
+                const unsigned int p0 = __builtin_bit_cast(
+                    unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, false));
+                const unsigned int p1 = __builtin_bit_cast(
+                    unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, true));
                 outw[q >> 1][(q & 1) * 2 + 0] = p0;
                 outw[q >> 1][(q & 1) * 2 + 1] = p1;
             }
