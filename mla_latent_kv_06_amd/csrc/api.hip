@@ -109,6 +109,21 @@ DecodeWs decode_ws(const mla_dims& d, int batch, int q_len, int num_splits) {
 
 int append_kc(int d_model) { return (d_model + mla::kAppendChunk - 1) / mla::kAppendChunk; }
 
+// The append's MFMA projection runs on the weight-streaming GEMM when
+// d_model is a multiple of 64 and its operands stay under 2 GiB (32-bit
+// buffer ranges), else on the split-K kernel of append.hip.
+bool append_streams(const mla_dims& d, long long T, int d_model) {
+    const long long Dout = d.kv_lora_rank + d.qk_rope_dim;
+    return d_model % 64 == 0 && T * d_model * 2 < (1ll << 31) && Dout * d_model * 2 < (1ll << 31);
+}
+
+// partial slices of the append's MFMA projection
+int append_slices(const mla_dims& d, long long T, int d_model) {
+    return append_streams(d, T, d_model)
+               ? mla::append_stream_splits(d.kv_lora_rank + d.qk_rope_dim, d_model)
+               : append_kc(d_model);
+}
+
 bool append_uses_mfma(const mla_dims& d, int d_model) {
     return d.act_dtype == MLA_BF16 && (d.kv_lora_rank + d.qk_rope_dim) % 32 == 0 &&
            d_model % 16 == 0;
@@ -272,7 +287,8 @@ mla_status mla_cache_append_workspace_size(const mla_dims* dims, int32_t batch, 
     if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes is NULL");
     if (batch < 0 || n_new < 0 || d_model < 1)
         return fail(MLA_ERR_BAD_SHAPE, "batch=%d n_new=%d d_model=%d", batch, n_new, d_model);
-    const int kc = append_uses_mfma(*dims, d_model) ? append_kc(d_model) : 1;
+    const int kc = append_uses_mfma(*dims, d_model)
+                       ? append_slices(*dims, (long long)batch * n_new, d_model) : 1;
     *bytes = align_up((size_t)kc * batch * n_new * (dims->kv_lora_rank + dims->qk_rope_dim) * 4, 256);
     return ok();
 }
@@ -325,7 +341,8 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t n_new, 
     a.pool = cache_pool;
     a.pool_scale = cache_scale;
     a.part = static_cast<float*>(workspace);
-    a.kc = mfma ? append_kc(d_model) : 1;
+    a.stream_gemm = mfma && append_streams(d, (long long)batch * n_new, d_model);
+    a.kc = mfma ? append_slices(d, (long long)batch * n_new, d_model) : 1;
     a.kchunk = mfma ? mla::kAppendChunk : d_model;
     a.stream = static_cast<hipStream_t>(stream);
     const hipError_t e = mla::launch_append(a, mfma);

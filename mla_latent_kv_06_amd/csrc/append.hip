@@ -3,12 +3,15 @@
 // token's paged slot ("KV Compression -- DeepSeek-V3", "How it works").
 //
 // Two kernels: a split-K projection writing fp32 partial sums to the
-// workspace (MFMA for bf16 activations, fp32 VALU otherwise), then one
+// workspace (for bf16 activations the weight-streaming MFMA GEMM of
+// stream_gemm.hpp when d is a multiple of 64, else the MFMA kernel below;
+// fp32 VALU for f32 activations), then one
 // workgroup per token that adds the partials in a fixed order (so results do
 // not depend on scheduling), normalises, rotates, rounds and stores.
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "stream_gemm.hpp"
 
 namespace mla {
 namespace {
@@ -210,11 +213,22 @@ hipError_t finalize(const AppendLaunch& a) {
 
 }  // namespace
 
+int append_stream_splits(int Dout, int d_model) {
+    // the finalize adds at most 32 partial slices on its fast path
+    return stream_gemm_splits(Dout, d_model, 32);
+}
+
 hipError_t launch_append(const AppendLaunch& a, bool mfma_gemm) {
     const int T = a.batch * a.n_new;
     if (T == 0) return hipSuccess;
     const int Dout = a.DC + a.DR;
-    if (mfma_gemm) {
+    if (mfma_gemm && a.stream_gemm) {
+        const int n_ob = (Dout / 32 + kQWaves - 1) / kQWaves;
+        stream_gemm_mfma<true><<<n_ob * a.kc, kQWaves * kWave, 0, a.stream>>>(
+            static_cast<const unsigned short*>(a.h), T, a.d_model,
+            static_cast<const unsigned short*>(a.w_kv_a), nullptr, Dout, 0, 2, 1, nullptr, 1.0f, nullptr,
+            nullptr, a.part, n_ob);
+    } else if (mfma_gemm) {
         const int P = ((Dout / 32) * ((T + 31) / 32) + 3) / 4;
         append_gemm_mfma<<<P * a.kc, 256, 0, a.stream>>>(
             static_cast<const unsigned short*>(a.h), static_cast<const unsigned short*>(a.w_kv_a), T,

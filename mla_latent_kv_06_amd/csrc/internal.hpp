@@ -55,8 +55,9 @@ struct AppendLaunch {
     void* pool;
     float* pool_scale;
     float* part;                 // [KC][T][DC+DR] f32
-    int kc;                      // K chunks in `part`
-    int kchunk;                  // d_model columns per chunk
+    int kc;                      // partial slices in `part`
+    int kchunk;                  // d_model columns per chunk (split-K kernel)
+    bool stream_gemm = false;    // projection on the weight-streaming GEMM
     hipStream_t stream;
 };
 

@@ -107,6 +107,14 @@ def test_append_mid_bf16(n_new):
     _bf16_append(wl, f"v3_mid_append n_new={n_new}")
 
 
+def test_append_split_k_kernel():
+    """d_model a multiple of 16 but not of 64: the split-K MFMA projection
+    (other V3 appends use the weight-streaming GEMM)."""
+    wl = W["v3_b64_ctx1k8k_paged_bf16"].replace(name="v3_append_d1040", batch=3, ctx_lo=60,
+                                                ctx_hi=200, q_len=2, d_model=1040)
+    _bf16_append(wl, "v3 append d_model=1040")
+
+
 def test_append_long_positions():
     """Positions near 131072: the rotary angle needs double precision."""
     wl = W["v3_b64_ctx1k8k_paged_bf16"].replace(name="v3_far_append", batch=2, ctx_lo=131000,
