@@ -21,9 +21,9 @@ __device__ __forceinline__ f32x16 sg_mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // kQRows rows.  The depth K is walked in chunks of 64 columns; each chunk of
 // the workgroup's weight rows and of the pass's query rows is copied HBM ->
 // LDS by the buffer-to-LDS path (no VGPR round trip), kQStages chunks deep,
-// so kQStages - 1 chunks are in flight while one is multiplied: the weights
-// (75.5 MB on the V3 shape) stream at memory speed although each chunk holds
-// little arithmetic.
+// so kQStages - 1 chunks are in flight while one is multiplied.  (Measured on
+// the V3 up-projection: 2-3 stages stream the weights at ~3 TB/s, 6 stages
+// at ~2.6 TB/s; more copies in flight do not help this access pattern.)
 //
 // Copies: instruction i of a tile covers rows 8 i .. 8 i + 7 (8 lanes of 16
 // bytes per 128-byte row); each wave issues the same number per stage (4 of
@@ -44,15 +44,15 @@ __device__ __forceinline__ f32x16 sg_mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // cache append.
 constexpr int kQWaves = 3;
 constexpr int kQRows = 96;                        // query rows per pass (3 MFMA row blocks)
-constexpr int kQStages = 6;
+constexpr int kQStages = 3;
 constexpr int kQTileBytes = 96 * 128;             // 96 rows x 64 bf16
 __device__ __forceinline__ int qswz(int t) {
     return (((t & 3) << 1) | ((t >> 2) & 1)) ^ ((t >> 2) & 2);
 }
-__device__ __forceinline__ void wait_vmem_40() {
-    // s_waitcnt vmcnt(40) (= 8 (kQStages - 1)): vmcnt bits 3:0 and 15:14;
+__device__ __forceinline__ void wait_vmem_16() {
+    // s_waitcnt vmcnt(16) (= 8 (kQStages - 1)): vmcnt bits 3:0 and 15:14;
     // expcnt / lgkmcnt unconstrained
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (40 & 15) | ((40 >> 4) << 14));
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (16 & 15) | ((16 >> 4) << 14));
 }
 __device__ __forceinline__ void wait_vmem_0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Workgroup barrier that waits for this wave's LDS operations only: the
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kQWaves * kWave) void stream_gemm_mfma(
     int HN, int HR, int R, int q_len, const int* __restrict__ start_pos, float rope_base,
     unsigned short* __restrict__ q_nope, unsigned short* __restrict__ q_pe,
     float* __restrict__ part, int n_ob) {
-    static_assert(8 * (kQStages - 1) == 40, "wait_vmem_40 counts the copies of kQStages - 1 stages");
+    static_assert(8 * (kQStages - 1) == 16, "wait_vmem_16 counts the copies of kQStages - 1 stages");
     __shared__ __attribute__((aligned(16))) unsigned char smem[kQStages * 2 * kQTileBytes];
     MLA_LDS unsigned char* lds = (MLA_LDS unsigned char*)smem;
     const int lane = threadIdx.x & 63;
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kQWaves * kWave) void stream_gemm_mfma(
         for (int c = 0; c < n_chunks; ++c) {
             stage_barrier();                      // everyone is done with chunk c - 1's stage
             issue(c + kQStages - 1);
-            wait_vmem_40();                       // this wave's copies of chunk c landed
+            wait_vmem_16();                       // this wave's copies of chunk c landed
             stage_barrier();                      // ... and everyone's
             const MLA_LDS unsigned char* st = lds + (c % kQStages) * 2 * kQTileBytes;
             // all of the chunk's fragments first, then the MFMAs: one LDS
