@@ -283,6 +283,67 @@ mla_status mla_query_project(const mla_dims* dims, int32_t batch, int32_t q_len,
                              void* q_nope, void* q_pe, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* ---- prefill -----------------------------------------------------------------
+ *
+ * Causal attention of many query rows per sequence over the paged latent
+ * cache, in the decompressed form ("DeepSeek-V2: MLA Explained", "MLA Full
+ * Formulas", steps 2 and 3): for every token j of sequence b and head i the
+ * keys and values are rebuilt,
+ *     K_{j,i} = [W_UK[i] c_j ; k^R_j],   V_{j,i} = W_UV[i] c_j,
+ * and query s (of q_len) attends to tokens 0 .. seq_lens[b] - q_len + s:
+ *     out = softmax(q . K^T * scale) V.
+ * The arguments and the result are those of mla_decode_absorbed with the same
+ * q_len (rows with no visible token: zeros and lse -inf); the two calls differ
+ * in cost.  Per (query, key) pair the rebuilt form costs 2 H (N + R + V)
+ * flops against 2 H (2 kv_lora_rank + R) for the absorbed one, and the
+ * rebuild, 4 H N kv_lora_rank flops per token, is shared by all of a
+ * sequence's queries: the call for long prompts, chunked or not.
+ *
+ * Steps (MLA_PREFILL_* bits for mla_prefill_stages): gather the rows of each
+ * sequence from the pool into the workspace; rebuild K^C and V (bf16, fp32
+ * accumulation; an fp8 cache enters as the codes' exact values with the
+ * token scale applied to the fp32 products, its rotary keys as code * scale
+ * rounded to bf16); attend (bf16 MFMA, fp32 accumulation, softmax weights
+ * rounded to bf16 for the value product).
+ *
+ *  q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_table, seq_lens,
+ *  out, lse      as for mla_decode_absorbed; lse may be NULL.
+ *  workspace     mla_prefill_workspace_size bytes: about 66 KB per token of
+ *                batch * max_blocks_per_seq * block_size (rebuilt keys and
+ *                values of every head)
+ *
+ * Requirements (else MLA_ERR_UNSUPPORTED / MLA_ERR_BAD_SHAPE): the
+ * DeepSeek-V3 shape (128 heads, kv_lora_rank 512, qk_rope_dim 64, qk_nope_dim
+ * and v_head_dim 128, block_size 64, act_dtype MLA_BF16, cache MLA_BF16 or
+ * MLA_FP8_E4M3, no flags); q_len in [1, 2^20]; max_blocks_per_seq in
+ * [1, 65536] with batch * max_blocks_per_seq * 64 <= 2^22; every tensor
+ * 16-byte aligned.  seq_lens[b] above max_blocks_per_seq * block_size is
+ * taken as that maximum. */
+enum {
+    MLA_PREFILL_GATHER = 1,      /* pool rows -> contiguous latents / rotary keys */
+    MLA_PREFILL_DECOMPRESS = 2,  /* K^C = W_UK c, V = W_UV c for every token      */
+    MLA_PREFILL_ATTEND = 4,      /* causal attention over the rebuilt keys        */
+    MLA_PREFILL_ALL = 7
+};
+mla_status mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                      int32_t max_blocks_per_seq, size_t* bytes);
+mla_status mla_prefill(const mla_dims* dims, int32_t batch, int32_t q_len,
+                       const void* q_nope, const void* q_pe, const void* w_uk,
+                       const void* w_uv, const void* cache_pool, const float* cache_scale,
+                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream);
+/* mla_prefill restricted to the steps in `stages` (MLA_PREFILL_* bits), for
+ * timing them separately.  Each step reads what the previous one left in the
+ * workspace. */
+mla_status mla_prefill_stages(const mla_dims* dims, int32_t batch, int32_t q_len,
+                              const void* q_nope, const void* q_pe, const void* w_uk,
+                              const void* w_uv, const void* cache_pool,
+                              const float* cache_scale, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              uint32_t stages, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

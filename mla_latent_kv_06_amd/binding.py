@@ -30,6 +30,7 @@ STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_BAD_SHAPE",
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 STAGE_ABSORB_Q, STAGE_SPLIT_KV, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 FLAG_FP8_SCORES = 1          # mla_dims.flags: fp8 score product (fp8 cache, MFMA shape)
+PREFILL_GATHER, PREFILL_DECOMPRESS, PREFILL_ATTEND, PREFILL_ALL = 1, 2, 4, 7
 
 DTYPE_CODES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 _TORCH_OF = {MLA_F32: (torch.float32,), MLA_BF16: (torch.bfloat16,),
@@ -38,7 +39,8 @@ _TORCH_OF = {MLA_F32: (torch.float32,), MLA_BF16: (torch.bfloat16,),
 EXPORTED = ("mla_status_string", "mla_last_error", "mla_cache_row_bytes",
             "mla_cache_block_bytes", "mla_cache_append_workspace_size", "mla_cache_append",
             "mla_decode_default_splits", "mla_decode_workspace_size", "mla_decode_absorbed",
-            "mla_decode_absorbed_stages", "mla_query_workspace_size", "mla_query_project")
+            "mla_decode_absorbed_stages", "mla_query_workspace_size", "mla_query_project",
+            "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_stages")
 
 
 class Dims(ctypes.Structure):
@@ -97,6 +99,14 @@ _lib.mla_decode_absorbed_stages.restype = ctypes.c_int
 _lib.mla_decode_absorbed_stages.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I,
                                             _P, _P, _P, _SZ, ctypes.c_uint32, _P]
 
+_lib.mla_prefill_workspace_size.restype = ctypes.c_int
+_lib.mla_prefill_workspace_size.argtypes = [_DP, _I, _I, _I, ctypes.POINTER(_SZ)]
+_lib.mla_prefill.restype = ctypes.c_int
+_lib.mla_prefill.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _SZ, _P]
+_lib.mla_prefill_stages.restype = ctypes.c_int
+_lib.mla_prefill_stages.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _SZ,
+                                    ctypes.c_uint32, _P]
+
 
 class MLAError(RuntimeError):
     def __init__(self, status: int, where: str):
@@ -148,6 +158,13 @@ def query_workspace_size(dims: Dims, batch: int, q_len: int, d_model: int, q_lor
     n = _SZ(0)
     _check(_lib.mla_query_workspace_size(ctypes.byref(dims), batch, q_len, d_model, q_lora_rank,
                                          ctypes.byref(n)), "mla_query_workspace_size")
+    return n.value
+
+
+def prefill_workspace_size(dims: Dims, batch: int, q_len: int, max_blocks_per_seq: int) -> int:
+    n = _SZ(0)
+    _check(_lib.mla_prefill_workspace_size(ctypes.byref(dims), batch, q_len, max_blocks_per_seq,
+                                           ctypes.byref(n)), "mla_prefill_workspace_size")
     return n.value
 
 
@@ -220,6 +237,48 @@ def decode(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_
         _ptr(seq_lens), num_splits, _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel(), stages, _stream(dev))
     _check(st, "mla_decode_absorbed_stages")
+    return out, lse
+
+
+def prefill(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_table, seq_lens,
+            out=None, lse=None, workspace=None, stages: int = PREFILL_ALL, want_lse: bool = True):
+    """Causal prefill attention in the decompressed form (mla_prefill[_stages]).
+    Arguments and result as for ``decode``.  Returns (out, lse)."""
+    act = _TORCH_OF[dims.act_dtype]
+    B, Sq = q_nope.shape[0], q_nope.shape[1]
+    H, N, R = dims.n_heads, dims.qk_nope_dim, dims.qk_rope_dim
+    dc, V = dims.kv_lora_rank, dims.v_head_dim
+    dev = q_nope.device
+    _need(q_nope, "q_nope", act, (B, Sq, H, N), dev)
+    _need(q_pe, "q_pe", act, (B, Sq, H, R), dev)
+    _need(w_uk, "w_uk", act, (H, N, dc), dev)
+    _need(w_uv, "w_uv", act, (H, V, dc), dev)
+    _need(cache_pool, "cache_pool", _TORCH_OF[dims.cache_dtype], None, dev)
+    if cache_pool.dim() != 3 or cache_pool.shape[1:] != (dims.block_size, dc + R):
+        raise ValueError(f"cache_pool shape {tuple(cache_pool.shape)}")
+    if dims.cache_dtype == MLA_FP8_E4M3:
+        _need(cache_scale, "cache_scale", (torch.float32,), cache_pool.shape[:2], dev)
+    _need(block_table, "block_table", (torch.int32,), None, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table shape {tuple(block_table.shape)}")
+    _need(seq_lens, "seq_lens", (torch.int32,), (B,), dev)
+    if out is None:
+        out = torch.empty((B, Sq, H, V), dtype=act[0], device=dev)
+    _need(out, "out", act, (B, Sq, H, V), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), (B, Sq, H), dev)
+    ws_bytes = prefill_workspace_size(dims, B, Sq, block_table.shape[1])
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), None, dev)
+    st = _lib.mla_prefill_stages(
+        ctypes.byref(dims), B, Sq, _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+        _ptr(cache_pool), _ptr(cache_scale), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), stages,
+        _stream(dev))
+    _check(st, "mla_prefill_stages")
     return out, lse
 
 

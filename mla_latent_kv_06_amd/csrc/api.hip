@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "internal.hpp"
+#include "prefill.hpp"
 #include "query.hpp"
 
 namespace {
@@ -252,6 +253,96 @@ QueryWs query_ws(int batch, int q_len, int d_model, int q_lora_rank) {
     return w;
 }
 
+// Prefill: shape checks shared by the sizing call and the entry point.
+mla_status check_prefill_shape(const mla_dims* dims, int32_t batch, int32_t q_len,
+                               int32_t max_blocks_per_seq) {
+    if (mla_status st = check_dims(dims); st != MLA_OK) return st;
+    const mla_dims& d = *dims;
+    if (!mla::is_v3_shape(d))
+        return fail(MLA_ERR_UNSUPPORTED, "the prefill serves the DeepSeek-V3 head shape "
+                                         "(128 heads, 512 + 64, 128 / 128, blocks of 64, bf16 activations)");
+    if (d.flags & MLA_FLAG_FP8_SCORES)
+        return fail(MLA_ERR_UNSUPPORTED, "MLA_FLAG_FP8_SCORES applies to the decode only");
+    if (batch < 0 || q_len < 1 || q_len > (1 << 20))
+        return fail(MLA_ERR_BAD_SHAPE, "batch=%d must be >= 0 and q_len=%d in [1, 2^20]", batch, q_len);
+    if (max_blocks_per_seq < 1 || max_blocks_per_seq > (1 << 16))
+        return fail(MLA_ERR_BAD_SHAPE, "max_blocks_per_seq=%d outside [1, 65536]", max_blocks_per_seq);
+    if ((long long)batch * mla::prefill_tpad(max_blocks_per_seq) > (1ll << 22))
+        return fail(MLA_ERR_BAD_SHAPE, "batch * max_blocks_per_seq * 64 exceeds 2^22 tokens");
+    return MLA_OK;
+}
+
+struct PrefillWs {
+    size_t x, kr, ts, kc, vv, total;
+};
+
+PrefillWs prefill_ws(int batch, int max_blocks) {
+    const size_t rows = (size_t)batch * mla::prefill_tpad(max_blocks);
+    PrefillWs w;
+    w.x = 0;
+    w.kr = align_up(rows * 512 * 2, 256);
+    w.ts = w.kr + align_up(rows * 64 * 2, 256);
+    w.kc = w.ts + align_up(rows * 4, 256);
+    w.vv = w.kc + align_up(rows * 128 * 128 * 2, 256);
+    w.total = w.vv + align_up(rows * 128 * 128 * 2, 256);
+    return w;
+}
+
+mla_status prefill_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
+                        const void* q_pe, const void* w_uk, const void* w_uv, const void* cache_pool,
+                        const float* cache_scale, const int32_t* block_table,
+                        int32_t max_blocks_per_seq, const int32_t* seq_lens, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, uint32_t stages, void* stream) {
+    if (mla_status st = check_prefill_shape(dims, batch, q_len, max_blocks_per_seq); st != MLA_OK)
+        return st;
+    const mla_dims& d = *dims;
+    if (stages == 0 || (stages & ~(uint32_t)MLA_PREFILL_ALL))
+        return fail(MLA_ERR_BAD_SHAPE, "stages=0x%x: use MLA_PREFILL_* bits", stages);
+    if (batch == 0) return ok();
+    if ((stages & MLA_PREFILL_GATHER) && (!cache_pool || !block_table || !seq_lens))
+        return fail(MLA_ERR_NULL_POINTER, "cache_pool, block_table and seq_lens are required");
+    if ((stages & MLA_PREFILL_GATHER) && d.cache_dtype == MLA_FP8_E4M3 && !cache_scale)
+        return fail(MLA_ERR_NULL_POINTER, "cache_scale is required for an FP8 cache");
+    if ((stages & MLA_PREFILL_DECOMPRESS) && (!w_uk || !w_uv || !seq_lens))
+        return fail(MLA_ERR_NULL_POINTER, "w_uk, w_uv and seq_lens are required");
+    if ((stages & MLA_PREFILL_ATTEND) && (!q_nope || !q_pe || !out || !seq_lens))
+        return fail(MLA_ERR_NULL_POINTER, "q_nope, q_pe, out and seq_lens are required");
+    if (!workspace) return fail(MLA_ERR_NULL_POINTER, "workspace is NULL");
+    const PrefillWs ws = prefill_ws(batch, max_blocks_per_seq);
+    if (workspace_bytes < ws.total)
+        return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu", workspace_bytes, ws.total);
+    const void* ptrs[] = {q_nope, q_pe, w_uk, w_uv, cache_pool, out, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(MLA_ERR_ALIGNMENT, "tensor at %p is not 16-byte aligned", p);
+    mla::PrefillLaunch a;
+    a.cache_dtype = d.cache_dtype;
+    a.scale = resolved_scale(d);
+    a.batch = batch;
+    a.q_len = q_len;
+    a.q_nope = q_nope;
+    a.q_pe = q_pe;
+    a.w_uk = w_uk;
+    a.w_uv = w_uv;
+    a.pool = cache_pool;
+    a.pool_scale = cache_scale;
+    a.block_table = block_table;
+    a.max_blocks = max_blocks_per_seq;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.lse = lse;
+    char* base = static_cast<char*>(workspace);
+    a.x = reinterpret_cast<unsigned short*>(base + ws.x);
+    a.kr = reinterpret_cast<unsigned short*>(base + ws.kr);
+    a.ts = reinterpret_cast<float*>(base + ws.ts);
+    a.kc = reinterpret_cast<unsigned short*>(base + ws.kc);
+    a.vv = reinterpret_cast<unsigned short*>(base + ws.vv);
+    a.stages = stages;
+    a.stream = static_cast<hipStream_t>(stream);
+    const hipError_t e = mla::launch_prefill(a);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -449,6 +540,36 @@ mla_status mla_query_project(const mla_dims* dims, int32_t batch, int32_t q_len,
     const hipError_t e = mla::launch_query(a);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+mla_status mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                      int32_t max_blocks_per_seq, size_t* bytes) {
+    if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes is NULL");
+    if (mla_status st = check_prefill_shape(dims, batch, q_len, max_blocks_per_seq); st != MLA_OK)
+        return st;
+    *bytes = prefill_ws(batch, max_blocks_per_seq).total;
+    return ok();
+}
+
+mla_status mla_prefill(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
+                       const void* q_pe, const void* w_uk, const void* w_uv, const void* cache_pool,
+                       const float* cache_scale, const int32_t* block_table,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                        block_table, max_blocks_per_seq, seq_lens, out, lse, workspace,
+                        workspace_bytes, MLA_PREFILL_ALL, stream);
+}
+
+mla_status mla_prefill_stages(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
+                              const void* q_pe, const void* w_uk, const void* w_uv,
+                              const void* cache_pool, const float* cache_scale,
+                              const int32_t* block_table, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, uint32_t stages, void* stream) {
+    return prefill_impl(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                        block_table, max_blocks_per_seq, seq_lens, out, lse, workspace,
+                        workspace_bytes, stages, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,564 @@
+// MLA prefill in the decompressed form, DeepSeek-V3 head shape (128 heads,
+// latent 512, rotary 64, q_nope 128, v_head 128, cache blocks of 64 tokens).
+//
+// A prompt's attention costs 2 H (N + R + V) = 2 H 320 flops per (query, key)
+// pair when keys and values are rebuilt from the latent ("DeepSeek-V2: MLA
+// Explained", "MLA Full Formulas": k^C = W_UK c, v^C = W_UV c, keys
+// [k^C ; k^R]), against 2 H (d_c + R + d_c) = 2 H 1088 in the absorbed form
+// the decode uses.  With many query rows per sequence the rebuild is paid
+// once per token and shared by every query, so prefill rebuilds:
+//
+//  1. gather:      the sequence's cache rows (paged) -> contiguous latents X
+//                  [b][t][512] and rotary keys KR [b][t][64], bf16; an fp8
+//                  cache gives X the codes' exact values, KR the dequantised
+//                  values rounded to bf16, and its token scales to TS.
+//  2. decompress:  K^C[b][h][t][:] = W_UK[h] X[b][t],  V[b][h][t][:] = W_UV[h]
+//                  X[b][t] (times the token scale), bf16, on MFMA.
+//  3. attention:   causal softmax attention of each head's queries [q^C ; q^R]
+//                  over its keys [K^C ; KR] and values V, MFMA with an online
+//                  softmax; query s of a sequence of L tokens and q_len queries
+//                  sees tokens 0 .. L - q_len + s (the decode's rule).
+//
+// Workspace rows of sequence b start at b * Tpad (Tpad = max_blocks * 64
+// rounded up to 128), so the host never reads lengths.  Token tiles past a
+// sequence's length are skipped by every kernel; the gather zeroes the rows
+// between the length and the next multiple of 128, which the decompression
+// reads.
+
+#include "common.hpp"
+#include "internal.hpp"
+#include "prefill.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int PH = 128;                 // heads
+constexpr int PDC = 512;                // latent width
+constexpr int PDR = 64;                 // rotary width
+constexpr int PN = 128;                 // q_nope / k^C width
+constexpr int PV = 128;                 // value width
+constexpr int PBS = 64;                 // tokens per cache block
+
+__device__ __forceinline__ f32x16 pf_mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// XOR slot pattern of the LDS tiles: 16-byte chunk c of row t sits at slot
+// c ^ g(t) of the row's 8 slots, so that the 16-byte reads of 16 consecutive
+// rows at one chunk, and the 8-byte transposed reads of 4 rows x 2 chunks,
+// land on disjoint banks.
+__device__ __forceinline__ int pswz(int t) {
+    return (((t & 3) << 1) | ((t >> 2) & 1)) ^ ((t >> 2) & 2);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t p_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt vmcnt(N), expcnt / lgkmcnt unconstrained (vmcnt: bits 3:0, 15:14)
+template <int N>
+__device__ __forceinline__ void p_wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier after this wave's LDS operations only: buffer-to-LDS
+// copies of later stages stay in flight across it.
+__device__ __forceinline__ void p_stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int seq_len_of(const int* __restrict__ seq_lens, int b, int Tmax) {
+    return min(max(seq_lens[b], 0), Tmax);
+}
+
+// ---------------------------------------------------------------------------
+// 1. gather
+// ---------------------------------------------------------------------------
+
+// grid: batch * Tpad / 64 workgroups of 256; workgroup (b, k) handles tokens
+// 64 k .. +64 of sequence b (cache block k of its table).
+__global__ __launch_bounds__(256) void prefill_gather_kernel(
+    const unsigned char* __restrict__ pool, const float* __restrict__ pool_scale, int fp8,
+    const int* __restrict__ block_table, int max_blocks, const int* __restrict__ seq_lens,
+    int Tmax, int Tpad, unsigned short* __restrict__ x, unsigned short* __restrict__ kr,
+    float* __restrict__ ts) {
+    const int per = Tpad / PBS;
+    const int b = blockIdx.x / per, k = blockIdx.x - b * per;
+    const int len = seq_len_of(seq_lens, b, Tmax);
+    const int lim = (len + 127) / 128 * 128;
+    if (k * PBS >= lim) return;
+    const long long blk = k * PBS < len ? block_table[(size_t)b * max_blocks + k] : 0;
+    const size_t row0 = (size_t)b * Tpad + (size_t)k * PBS;
+    const int tid = threadIdx.x;
+    if (!fp8) {
+        const unsigned char* src = pool + (size_t)blk * PBS * (PDC + PDR) * 2;
+        for (int p = tid; p < PBS * 72; p += 256) {          // 72 16-byte chunks per row
+            const int r = p / 72, c = p - r * 72;
+            const int t = k * PBS + r;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (t < len) v = *reinterpret_cast<const u32x4*>(src + ((size_t)r * 72 + c) * 16);
+            unsigned short* dst = c < 64 ? x + (row0 + r) * PDC + c * 8 : kr + (row0 + r) * PDR + (c - 64) * 8;
+            *reinterpret_cast<u32x4*>(dst) = v;
+        }
+        return;
+    }
+    const unsigned char* src = pool + (size_t)blk * PBS * (PDC + PDR);
+    const float* ssrc = pool_scale + (size_t)blk * PBS;
+    for (int p = tid; p < PBS * 36; p += 256) {               // 36 chunks of 16 codes per row
+        const int r = p / 36, c = p - r * 36;
+        const int t = k * PBS + r;
+        const bool live = t < len;
+        const u32x4 raw = live ? *reinterpret_cast<const u32x4*>(src + ((size_t)r * 36 + c) * 16)
+                               : u32x4{0u, 0u, 0u, 0u};
+        const float s = live ? ssrc[r] : 0.f;
+        if (c < 32) {
+            // latent codes as their exact bf16 values; the scale is applied
+            // to the decompressed keys and values
+            u32x4 o[2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                o[q >> 1][(q & 1) * 2 + 0] = __builtin_bit_cast(
+                    unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, false));
+                o[q >> 1][(q & 1) * 2 + 1] = __builtin_bit_cast(
+                    unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, true));
+            }
+            unsigned short* dst = x + (row0 + r) * PDC + c * 16;
+            *reinterpret_cast<u32x4*>(dst) = o[0];
+            *reinterpret_cast<u32x4*>(dst + 8) = o[1];
+            if (c == 0) ts[row0 + r] = s;
+        } else {
+            // rotary codes dequantised (code * scale) and rounded to bf16
+            u16x8 o[2];
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                o[e >> 3][e & 7] = f32_to_bf16_bits(e4m3_to_f32((raw[e >> 2] >> (8 * (e & 3))) & 0xFFu) * s);
+            unsigned short* dst = kr + (row0 + r) * PDR + (c - 32) * 16;
+            *reinterpret_cast<u16x8*>(dst) = o[0];
+            *reinterpret_cast<u16x8*>(dst + 8) = o[1];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2. decompression
+// ---------------------------------------------------------------------------
+
+// grid: H * batch * Tpad / 128 workgroups of 256 (head fastest: the 16 heads
+// an XCD receives keep their weights, 4 MB, in its L2).  Workgroup (h, b,
+// tile) computes, for tokens t0 .. t0 + 128 of sequence b, the 256 outputs
+// [W_UK[h] ; W_UV[h]] X^T: wave w owns outputs 64 w .. +64 (waves 0-1 the
+// keys, 2-3 the values) for all 128 tokens.  The depth 512 is walked in
+// chunks of 64 columns, copied HBM -> LDS by the buffer-to-LDS path two
+// stages deep (one chunk in flight while one is multiplied): per stage 256
+// weight rows and 128 token rows of 128 bytes, 48 copy instructions, 12 per
+// wave.  Instruction i covers rows 8 i .. 8 i + 7 of the stage (weights, then
+// tokens), LDS bytes 1024 i .. +1024.
+constexpr int kDTok = 128;
+constexpr int kDOut = 256;
+constexpr int kDWBytes = kDOut * 128;
+constexpr int kDStage = kDWBytes + kDTok * 128;      // 48 KB
+constexpr int kDOutStride = 144;                     // bytes per token row of the store staging
+
+__global__ __launch_bounds__(256, 1) void prefill_decompress_kernel(
+    const unsigned short* __restrict__ x, const float* __restrict__ ts,
+    const unsigned short* __restrict__ w_uk, const unsigned short* __restrict__ w_uv,
+    const int* __restrict__ seq_lens, int Tmax, int Tpad,
+    unsigned short* __restrict__ kc, unsigned short* __restrict__ vv) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kDStage];
+    MLA_LDS unsigned char* lds = (MLA_LDS unsigned char*)smem;
+    const int h = blockIdx.x % PH;
+    const int tile = blockIdx.x / PH;
+    const int ntt = Tpad / kDTok;
+    const int b = tile / ntt, t0 = (tile - b * ntt) * kDTok;
+    const int len = seq_len_of(seq_lens, b, Tmax);
+    if (t0 >= len) return;                           // uniform
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int r8 = lane >> 3, s8 = lane & 7;
+
+    const __amdgpu_buffer_rsrc_t wk_r = p_rsrc(w_uk + (size_t)h * PN * PDC, PN * PDC * 2);
+    const __amdgpu_buffer_rsrc_t wv_r = p_rsrc(w_uv + (size_t)h * PV * PDC, PV * PDC * 2);
+    const __amdgpu_buffer_rsrc_t x_r = p_rsrc(x + ((size_t)b * Tpad + t0) * PDC, kDTok * PDC * 2);
+    // instruction i = w + 4 j: j < 4 W_UK rows, j < 8 W_UV rows, else token rows
+    unsigned voff[12];
+#pragma unroll
+    for (int j = 0; j < 12; ++j) {
+        const int i = w + 4 * j;
+        const int row = 8 * (j < 4 ? i : (j < 8 ? i - 16 : i - 32)) + r8;
+        voff[j] = (unsigned)row * (PDC * 2) + (unsigned)((s8 ^ pswz(row)) << 4);
+    }
+    auto issue = [&](int c) {
+        MLA_LDS unsigned char* st = lds + (c & 1) * kDStage;
+        const unsigned col = c < PDC / 64 ? (unsigned)c * 128u : 0x80000000u;
+#pragma unroll
+        for (int j = 0; j < 12; ++j) {
+            const __amdgpu_buffer_rsrc_t r = j < 4 ? wk_r : (j < 8 ? wv_r : x_r);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MLA_LDS void*)(st + (w + 4 * j) * 1024), 16,
+                                                     voff[j] + col, 0, 0, 0);
+        }
+    };
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[ob][tb] = f32x16{};
+    issue(0);
+    for (int c = 0; c < PDC / 64; ++c) {
+        p_stage_barrier();                           // everyone is done with chunk c - 1's stage
+        issue(c + 1);
+        p_wait_vmem<12>();                           // this wave's copies of chunk c landed
+        p_stage_barrier();                           // ... and everyone's
+        const MLA_LDS unsigned char* st = lds + (c & 1) * kDStage;
+#pragma unroll
+        for (int sx = 0; sx < 4; ++sx) {
+            const int cx = 2 * sx + hf;              // 16-byte slot of K-step sx
+            bf16x8 wf[2], xf[4];
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob) {
+                const int row = 64 * w + 32 * ob + l32;
+                wf[ob] = *reinterpret_cast<const MLA_LDS bf16x8*>(st + (8 * row + (cx ^ pswz(row))) * 16);
+            }
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int row = 32 * tb + l32;
+                xf[tb] = *reinterpret_cast<const MLA_LDS bf16x8*>(st + kDWBytes + (8 * row + (cx ^ pswz(row))) * 16);
+            }
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) acc[ob][tb] = pf_mfma(wf[ob], xf[tb], acc[ob][tb]);
+        }
+    }
+    p_wait_vmem<0>();                                // the record-less copies of chunk 8 too
+    __syncthreads();                                 // stages free for the store staging
+
+    // acc[ob][tb][i]: output 64 w + 32 ob + 8 (i/4) + 4 hf + i%4 of token
+    // 32 tb + l32.  Staged per wave as [token][64 outputs] bf16 (rows of 144
+    // bytes), then stored as 128-byte row pieces.
+    MLA_LDS unsigned char* ost = lds + w * (kDTok * kDOutStride);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const int tok = 32 * tb + l32;
+        const float sc = ts != nullptr ? ts[(size_t)b * Tpad + t0 + tok] : 1.0f;
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u16x4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = f32_to_bf16_bits(acc[ob][tb][4 * g + e] * sc);
+                *reinterpret_cast<MLA_LDS u16x4*>(ost + tok * kDOutStride + (32 * ob + 8 * g + 4 * hf) * 2) = hv;
+            }
+    }
+    // LDS operations of one wave complete in order: the reads see the writes
+    unsigned short* dst = (w < 2 ? kc : vv) + (((size_t)b * PH + h) * Tpad + t0) * 128 + (w & 1) * 64;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int tok = 8 * k + r8;
+        const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(ost + tok * kDOutStride + s8 * 16);
+        *reinterpret_cast<u32x4*>(dst + (size_t)tok * 128 + s8 * 8) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. causal attention
+// ---------------------------------------------------------------------------
+
+// grid: batch * H * nqb workgroups of 256 (nqb = ceil(q_len / 256)).  The 8
+// XCDs take workgroups in turn (XCD = id % 8), so the ids are laid out to
+// give all query blocks of one (sequence, head) to one XCD, longest first:
+// they stream the same key and value tiles at about the same time, and the
+// XCD's L2 serves all but the first read.
+//
+// Workgroup (b, h, qblk): queries s = 256 qblk .. +256 of sequence b, head h;
+// wave w owns 64 of them as two blocks of 32 (query block qb: queries
+// 256 qblk + 64 w + 32 qb + l32).  Key tiles of 64 tokens are copied HBM ->
+// LDS three stages deep (two in flight while one is used): the 24 KB key tile
+// [K^C | KR] (24 chunks per row: 16 of K^C, 8 of KR) and the 16 KB value tile
+// in the XOR layout, chunk c of row t at 16-byte position
+//   (c / 8) * 512 + 8 t + (c % 8 ^ g(t)),
+// 40 copy instructions per tile (10 per wave), instruction i writing LDS bytes
+// 1024 i .. +1024 of the stage (key groups 0-2, then value groups 0-1).
+//
+// Per half tile (32 keys), per query block:
+//   S^T (32 keys x 32 queries) = K . Q^T      12 MFMA, K from LDS, Q in VGPRs
+//   O^T (128 x 32)            += V^T . P^T     8 MFMA, V^T by transposed reads
+// so a lane holds 16 scores of one query and the query's softmax statistics
+// need one cross-lane exchange (lanes l and l + 32).  Each LDS fragment feeds
+// the MFMAs of both query blocks.
+//
+// Softmax: weights exp2(s * log2(e) * scale - m) with a per-query reference
+// m that is raised only when a score exceeds it by more than kLazy (weights
+// stay below 2^kLazy); raising it rescales the query's accumulators and sum
+// (a wave-uniform branch, taken a few times per query).
+constexpr int kPQ = 256;                 // queries per workgroup
+constexpr int kPStages = 3;
+constexpr int kPKBytes = PBS * (PN + PDR) * 2;      // 24 KB
+constexpr int kPStage = kPKBytes + PBS * PV * 2;    // 40 KB
+constexpr float kLazy = 8.0f;
+
+__global__ __launch_bounds__(256, 1) void prefill_attn_kernel(
+    const unsigned short* __restrict__ q_nope,   // [batch * q_len][H][128]
+    const unsigned short* __restrict__ q_pe,     // [batch * q_len][H][64]
+    const unsigned short* __restrict__ kc,       // [batch][H][Tpad][128]
+    const unsigned short* __restrict__ vv,       // [batch][H][Tpad][128]
+    const unsigned short* __restrict__ kr,       // [batch * Tpad][64]
+    const int* __restrict__ seq_lens, int Tmax, int Tpad, int q_len, int nqb, float scale_log2,
+    unsigned short* __restrict__ out,            // [batch * q_len][H][128]
+    float* __restrict__ lse) {                   // [batch * q_len][H]
+    static_assert(10 * (kPStages - 1) == 20, "the wait below counts the copies of two stages");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kPStages * kPStage];
+    MLA_LDS unsigned char* lds = (MLA_LDS unsigned char*)smem;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int r8 = lane >> 3, s8 = lane & 7;
+
+    const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
+    const int pair = (jj / nqb) * 8 + xcd;
+    const int qblk = nqb - 1 - (jj - (jj / nqb) * nqb);
+    const int b = pair / PH, h = pair - b * PH;
+    const int len = seq_len_of(seq_lens, b, Tmax);
+    const int base_vis = len - q_len;            // query s sees tokens < base_vis + s + 1
+    const int q0 = qblk * kPQ;
+    const int qa = q0 + 64 * w;                  // this wave's first query
+    const int vis_blk = min(len, base_vis + min(q0 + kPQ, q_len));
+    const int n_tiles = vis_blk > 0 ? (vis_blk + PBS - 1) / PBS : 0;
+    const int vis_w = qa < q_len ? min(len, base_vis + min(qa + 64, q_len)) : 0;
+
+    // ---- copies ----------------------------------------------------------------
+    const size_t kv_base = ((size_t)b * PH + h) * Tpad * 128;
+    const __amdgpu_buffer_rsrc_t kc_r = p_rsrc(kc + kv_base, (unsigned)Tpad * 256u);
+    const __amdgpu_buffer_rsrc_t vv_r = p_rsrc(vv + kv_base, (unsigned)Tpad * 256u);
+    const __amdgpu_buffer_rsrc_t kr_r = p_rsrc(kr + (size_t)b * Tpad * PDR, (unsigned)Tpad * 128u);
+    // instruction i = w + 4 j: j < 4 K^C (groups 0-1), j < 6 KR (group 2),
+    // else V (groups 0-1); row 8 (i % 8) + r8 of the tile
+    unsigned voff[10];
+#pragma unroll
+    for (int j = 0; j < 10; ++j) {
+        const int i = w + 4 * j;
+        const int ii = j < 4 ? i : (j < 6 ? i - 16 : i - 24);
+        const int row = 8 * (ii & 7) + r8;
+        const int chunk = (j < 4 || j >= 6 ? 8 * (ii >> 3) : 0) + (s8 ^ pswz(row));
+        voff[j] = (unsigned)row * (j < 4 || j >= 6 ? 256u : 128u) + (unsigned)chunk * 16u;
+    }
+    auto issue = [&](int t) {
+        MLA_LDS unsigned char* st = lds + (t % kPStages) * kPStage;
+        const bool live = t < n_tiles;
+#pragma unroll
+        for (int j = 0; j < 10; ++j) {
+            const bool is_kr = j >= 4 && j < 6;
+            const __amdgpu_buffer_rsrc_t r = j < 4 ? kc_r : (is_kr ? kr_r : vv_r);
+            const unsigned off = live ? voff[j] + (unsigned)t * (is_kr ? 8192u : 16384u) : 0x80000000u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MLA_LDS void*)(st + (w + 4 * j) * 1024), 16, off,
+                                                     0, 0, 0);
+        }
+    };
+    // the first two tiles go out before the query loads
+    issue(0);
+    issue(1);
+
+    // ---- this wave's queries as MFMA B fragments: lane (hf, l32) holds
+    // channels 16 ks + 8 hf .. +8 of query qa + 32 qb + l32 (ks < 8: q^C, else q^R)
+    bf16x8 qf[2][12];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int s = qa + 32 * qb + l32;
+        const size_t row = ((size_t)b * q_len + min(s, q_len - 1)) * PH + h;
+        const bool ok = s < q_len;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(q_nope + row * PN + 16 * ks + 8 * hf);
+            qf[qb][ks] = ok ? v : bf16x8{};
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(q_pe + row * PDR + 16 * ks + 8 * hf);
+            qf[qb][8 + ks] = ok ? v : bf16x8{};
+        }
+    }
+
+    // per-lane LDS offsets: score operand (chunk 2 ks + hf of row 32 hb + l32)
+    // by ks % 4; transposed value reads (lane 4 r + c of a 16-lane group reads
+    // row 4 hf + r (+ 8), channels 4 c .. +4 of a 16-channel block) by the
+    // block's parity within its 32 channels and by the + 8 row offset
+    int qk_off[4], tr_off[2][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qk_off[j] = (l32 * 8 + ((2 * j + hf) ^ pswz(l32 & 15))) * 16;
+    {
+        const int r = (lane & 15) >> 2, g1 = (lane >> 4) & 1, b1 = (lane >> 1) & 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int t = 8 * e + 4 * hf + r;
+                tr_off[j][e] = (t * 8 + ((4 * j + 2 * g1 + b1) ^ pswz(t))) * 16 + (lane & 1) * 8;
+            }
+    }
+
+    f32x16 o[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int cm = 0; cm < 4; ++cm) o[qb][cm] = f32x16{};
+    float m_ref[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
+
+    for (int t = 0; t < n_tiles; ++t) {
+        p_stage_barrier();                       // everyone is done with tile t - 1's stage
+        issue(t + 2);
+        p_wait_vmem<20>();                       // this wave's copies of tile t landed
+        p_stage_barrier();                       // ... and everyone's
+        if (t * PBS >= vis_w) continue;          // nothing of this tile is visible to the wave
+        const MLA_LDS unsigned char* st = lds + (t % kPStages) * kPStage;
+        const MLA_LDS unsigned char* vt = st + kPKBytes;
+        // does the tile reach past the first query's visible range?
+        const bool need_mask = t * PBS + PBS - 1 >= base_vis + qa + 1;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            if (t * PBS + 32 * hb >= vis_w) break;
+            // ---- S^T = K . Q^T ------------------------------------------------------
+            const MLA_LDS unsigned char* kb = st + hb * 32 * 128;
+            auto ka = [&](int ks) {
+                return *reinterpret_cast<const MLA_LDS bf16x8*>(kb + qk_off[ks & 3] + (ks >> 2) * 8192);
+            };
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+            bf16x8 a0 = ka(0), a1 = ka(1), a2;
+#pragma unroll
+            for (int ks = 0; ks < 12; ++ks) {
+                if (ks + 2 < 12) a2 = ka(ks + 2);
+                sacc[0] = pf_mfma(a0, qf[0][ks], sacc[0]);
+                sacc[1] = pf_mfma(a0, qf[1][ks], sacc[1]);
+                a0 = a1;
+                a1 = a2;
+            }
+            // lane: query qa + 32 qb + l32, keys t*64 + 32 hb + 8 (i/4) + 4 hf + i%4
+            bf16x8 pf[2][2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                float sv[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sv[i] = sacc[qb][i];
+                if (need_mask) {
+                    const int lim = base_vis + qa + 32 * qb + l32;   // last visible key
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = t * PBS + 32 * hb + 8 * (i >> 2) + 4 * hf + (i & 3);
+                        if (key > lim) sv[i] = kNegInf;
+                    }
+                }
+                float hmax = sv[0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) hmax = fmaxf(hmax, sv[i]);
+                hmax *= scale_log2;
+                hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
+                const bool raise = hmax > m_ref[qb] + kLazy;
+                if (__builtin_amdgcn_ballot_w64(raise) != 0) {     // uniform
+                    const float alpha = raise ? __builtin_amdgcn_exp2f(m_ref[qb] - hmax) : 1.0f;
+                    m_ref[qb] = raise ? hmax : m_ref[qb];
+                    l_run[qb] *= alpha;
+#pragma unroll
+                    for (int cm = 0; cm < 4; ++cm)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) o[qb][cm][i] *= alpha;
+                }
+                // a query with nothing visible yet has m_ref = -inf and only
+                // -inf scores: its weights are exp2(-inf) = 0
+                const float m_use = m_ref[qb] == kNegInf ? 0.f : m_ref[qb];
+                float psum = 0.f;
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    u16x8 pu;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[8 * k2 + e], scale_log2, -m_use));
+                        psum += pv;
+                        pu[e] = f32_to_bf16_bits(pv);
+                    }
+                    pf[qb][k2] = __builtin_bit_cast(bf16x8, pu);
+                }
+                l_run[qb] += psum;
+            }
+            // ---- O^T += V^T . P^T ----------------------------------------------------
+            // K-step k2 covers keys 32 hb + 16 k2 + {0..3, 8..11} (lanes 0-31) and
+            // {4..7, 12..15} (lanes 32-63), matching P's layout
+            auto va = [&](int k2, int cm) {
+                const MLA_LDS unsigned char* vb = vt + (cm >> 1) * 8192 + (hb * 32 + k2 * 16) * 128;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (MLA_LDS bf16x4*)(vb + tr_off[cm & 1][0]));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (MLA_LDS bf16x4*)(vb + tr_off[cm & 1][1]));
+                return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            bf16x8 v0 = va(0, 0), v1;
+#pragma unroll
+            for (int st8 = 0; st8 < 8; ++st8) {
+                const int k2 = st8 >> 2, cm = st8 & 3;
+                if (st8 + 1 < 8) v1 = va((st8 + 1) >> 2, (st8 + 1) & 3);
+                o[0][cm] = pf_mfma(v0, pf[0][k2], o[0][cm]);
+                o[1][cm] = pf_mfma(v0, pf[1][k2], o[1][cm]);
+                v0 = v1;
+            }
+        }
+    }
+    p_wait_vmem<0>();                            // the record-less copies too
+
+    // ---- epilogue: out = O / l, lse = (m + log2 l) ln 2 ------------------------------
+    // o[qb][cm][i]: channel 32 cm + 8 (i/4) + 4 hf + i%4 of query qa + 32 qb + l32
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int s = qa + 32 * qb + l32;
+        const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);   // disjoint keys
+        if (s >= q_len) continue;
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        const size_t row = ((size_t)b * q_len + s) * PH + h;
+        unsigned short* dst = out + row * PV + 4 * hf;
+#pragma unroll
+        for (int cm = 0; cm < 4; ++cm)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u16x4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = f32_to_bf16_bits(o[qb][cm][4 * g + e] * inv);
+                *reinterpret_cast<u16x4*>(dst + 32 * cm + 8 * g) = hv;
+            }
+        if (hf == 0 && lse != nullptr) lse[row] = l_tot > 0.f ? (m_ref[qb] + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+    }
+}
+
+}  // namespace
+
+int prefill_tpad(int max_blocks) { return (max_blocks * PBS + 127) / 128 * 128; }
+
+hipError_t launch_prefill(const PrefillLaunch& a) {
+    if (a.batch == 0) return hipSuccess;
+    const int Tmax = a.max_blocks * PBS, Tpad = prefill_tpad(a.max_blocks);
+    if (a.stages & 1u) {
+        prefill_gather_kernel<<<a.batch * (Tpad / PBS), 256, 0, a.stream>>>(
+            static_cast<const unsigned char*>(a.pool), a.pool_scale, a.cache_dtype == MLA_FP8_E4M3 ? 1 : 0,
+            a.block_table, a.max_blocks, a.seq_lens, Tmax, Tpad, a.x, a.kr, a.ts);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    if (a.stages & 2u) {
+        prefill_decompress_kernel<<<PH * a.batch * (Tpad / kDTok), 256, 0, a.stream>>>(
+            a.x, a.cache_dtype == MLA_FP8_E4M3 ? a.ts : nullptr, static_cast<const unsigned short*>(a.w_uk),
+            static_cast<const unsigned short*>(a.w_uv), a.seq_lens, Tmax, Tpad, a.kc, a.vv);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    if (a.stages & 4u) {
+        const int nqb = (a.q_len + kPQ - 1) / kPQ;
+        prefill_attn_kernel<<<a.batch * PH * nqb, 256, 0, a.stream>>>(
+            static_cast<const unsigned short*>(a.q_nope), static_cast<const unsigned short*>(a.q_pe), a.kc,
+            a.vv, a.kr, a.seq_lens, Tmax, Tpad, a.q_len, nqb, a.scale * kLog2e,
+            static_cast<unsigned short*>(a.out), a.lse);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace mla

@@ -70,6 +70,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 //
+// A grid with gridDim.y > 1 spreads the row passes over workgroups (many
+// rows: the weights are then re-read per pass, from the caches).
+//
 // PART (the query down-projection): one weight tensor (w_uq = W_DQ, HN its
 // rows, HR = 0), the depth split over gridDim.x / n_ob workgroups, each
 // writing fp32 partial sums part[split][row][output] for the finalize.
@@ -119,7 +122,8 @@ __global__ __launch_bounds__(kQWaves * kWave) void stream_gemm_mfma(
     }
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, T * row_bytes);
 
-    for (int r0 = 0; r0 < T; r0 += kQRows) {
+    // row passes: this workgroup takes passes blockIdx.y, blockIdx.y + gridDim.y, ...
+    for (int r0 = (int)blockIdx.y * kQRows; r0 < T; r0 += kQRows * (int)gridDim.y) {
         const int nbs = min(3, (T - r0 + 31) / 32);
         unsigned xvo[4];
 #pragma unroll

@@ -179,3 +179,42 @@ def test_query_validation_rejects_before_launch(b):
     assert call(dims=b.Dims.make(128, 512, 64, 128, 128, 64, "bf16", "f32")) == 3
     assert call(dims=b.Dims.make(3, 512, 2, 10, 128, 64, "bf16", "bf16")) == 3   # 3*10 % 32
     assert call(batch=0) == 0
+
+
+def test_prefill_workspace_sizes(b):
+    d = v3_dims(b)
+    # rows per sequence: 3 blocks of 64 tokens rounded up to 256 (a multiple of 128)
+    rows = 2 * 256
+    al = lambda n: (n + 255) // 256 * 256
+    want = al(rows * 1024) + al(rows * 128) + al(rows * 4) + 2 * al(rows * 128 * 256)
+    assert b.prefill_workspace_size(d, 2, 100, 3) == want
+    assert b.prefill_workspace_size(d, 2, 100, 4) == want       # 256 tokens: no padding
+    assert b.prefill_workspace_size(d, 0, 1, 1) == 0
+
+
+def test_prefill_validation_rejects_before_launch(b):
+    lib = b.lib()
+    P = ctypes.c_void_p
+    def call(dims=None, **kw):
+        d = v3_dims(b) if dims is None else dims
+        a = dict(batch=2, q_len=300, qn=16, qp=16, wuk=16, wuv=16, pool=16, scale=None, bt=16,
+                 mb=8, sl=16, out=16, lse=16, ws=16, ws_bytes=1 << 40, stages=7)
+        a.update(kw)
+        pp = lambda v: None if v is None else P(v)
+        return lib.mla_prefill_stages(ctypes.byref(d), a["batch"], a["q_len"], pp(a["qn"]), pp(a["qp"]),
+                                      pp(a["wuk"]), pp(a["wuv"]), pp(a["pool"]), pp(a["scale"]),
+                                      pp(a["bt"]), a["mb"], pp(a["sl"]), pp(a["out"]), pp(a["lse"]),
+                                      pp(a["ws"]), a["ws_bytes"], a["stages"], None)
+    assert call(qn=None) == 1
+    assert call(pool=None) == 1
+    assert call(dims=v3_dims(b, "fp8")) == 1                     # no token scales
+    assert call(ws=None) == 1
+    assert call(q_len=0) == 2
+    assert call(mb=0) == 2
+    assert call(batch=64, mb=4096) == 2                          # 2^24 tokens of workspace rows
+    assert call(stages=8) == 2
+    assert call(ws_bytes=8) == 5
+    assert call(out=24) == 4
+    assert call(dims=b.Dims.make(64, 512, 64, 128, 128, 64, "bf16", "bf16")) == 3
+    assert call(dims=b.Dims.make(128, 512, 64, 128, 128, 64, "fp8", "bf16", flags=1), scale=16) == 3
+    assert call(batch=0) == 0

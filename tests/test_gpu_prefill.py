@@ -2,8 +2,9 @@
 
 A prompt of L tokens per sequence is processed in chunks: for each chunk of
 C tokens, mla_cache_append writes their cache rows, mla_query_project forms
-their queries from the same layer input h, and mla_decode_absorbed (q_len =
-C, causal inside the chunk) attends over everything cached so far.  The
+their queries from the same layer input h, and mla_decode_absorbed or
+mla_prefill (q_len = C, causal inside the chunk) attends over everything
+cached so far.  The
 concatenated outputs must equal causal attention over the whole prompt:
 ``decode_naive`` with q_len = L on the oracle's own cache rows
 (``append_rows``) and queries (``query_rows``), all from the same seeded
@@ -48,14 +49,15 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
 
 
-@pytest.mark.parametrize("L,C", [(300, 128), (200, 64)])
-def test_chunked_prefill(L, C):
+@pytest.mark.parametrize("L,C,attn", [(300, 128, "decode"), (200, 64, "decode"),
+                                      (300, 128, "prefill"), (300, 300, "prefill")])
+def test_chunked_prefill(L, C, attn):
     from mla_latent_kv_06_amd import binding as b
     B = 2
     wl = synth.WORKLOADS["v3_b64_ctx1k8k_paged_bf16"].replace(
         name="v3_prefill", batch=B, q_len=L, ctx_lo=0, ctx_hi=0, append=True)
     ql = synth.Q_LORA_RANK_V3
-    announce("chunked prefill", "L", L, "C", C)
+    announce("chunked prefill", "L", L, "C", C, "attention", attn)
     dims = b.Dims.from_workload(wl)
     H, N, R, V, dc = wl.n_heads, wl.qk_nope_dim, wl.qk_rope_dim, wl.v_head_dim, wl.kv_lora_rank
 
@@ -91,7 +93,10 @@ def test_chunked_prefill(L, C):
         qn, qp = b.query_project(dchunk, hc, wdq_d, gq_d, wuq_d, wqr_d, start,
                                  rms_eps=casebuild.RMS_EPS, rope_base=casebuild.ROPE_BASE)
         lens = torch.full((B,), s0 + c, dtype=torch.int32, device=DEV)
-        out, lse = b.decode(dchunk, qn, qp, wuk_d, wuv_d, pool, None, bt, lens, num_splits=0)
+        if attn == "decode":
+            out, lse = b.decode(dchunk, qn, qp, wuk_d, wuv_d, pool, None, bt, lens, num_splits=0)
+        else:
+            out, lse = b.prefill(dchunk, qn, qp, wuk_d, wuv_d, pool, None, bt, lens)
         outs.append(out)
         lses.append(lse)
     torch.cuda.synchronize()
