@@ -81,6 +81,9 @@ def parse():
                    help="fp8 cache: score product on the fp8 matrix cores (MLA_FLAG_FP8_SCORES)")
     p.add_argument("--query-path", action="store_true",
                    help="add the query path (W_DQ, norm, W_UQ / W_QR, RoPE) to each step")
+    p.add_argument("--prefill", default=None, metavar="WORKLOAD",
+                   help="time the prefill (gather, K/V rebuild, causal attention) on a "
+                        "prefill workload, e.g. v3_prefill_b2_8k_bf16, instead of the decode step")
     p.add_argument("--cpu-tokens", type=int, default=262144,
                    help="CPU-baseline sample: first sequences of layer 0 up to this many cached tokens")
     p.add_argument("--report", default=None)
@@ -164,6 +167,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {n} bytes 5 times")
+        return
+    if args.prefill:
+        prefill_main(args, torch, synth, b, dev)
         return
     wl = synth.WORKLOADS[args.workload]
     if wl.act_dtype != "bf16" or wl.cache_dtype not in ("bf16", "fp8"):
@@ -327,6 +333,178 @@ def main():
     if args.report:
         with open(args.report, "w") as f:
             json.dump(result, f, indent=1)
+
+
+class PrefillLayer:
+    """One layer's prefill inputs: queries of every prompt token, the absorbed
+    weights, and a paged pool holding the prompt's cache rows."""
+
+    def __init__(self, wl, li, dev, torch, synth):
+        seed = 2000 + li
+        bf = torch.bfloat16
+
+        def up(x):
+            return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(bf)
+
+        self.q_nope = up(synth.q_nope(wl, seed))
+        self.q_pe = up(synth.q_pe(wl, seed))
+        self.w_uk = up(synth.w_uk(wl, seed))
+        self.w_uv = up(synth.w_uv(wl, seed))
+        seq_lens = synth.seq_lens(wl, seed)
+        table, nblk = synth.block_tables(seq_lens, wl.block_size, wl.paged, seed)
+        self.seq_lens_host = seq_lens
+        self.table_host = table
+        self.block_table = torch.from_numpy(table).to(dev)
+        self.seq_lens = torch.from_numpy(seq_lens).to(dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        fp8 = wl.cache_dtype == "fp8"
+        x = torch.randn((nblk, wl.block_size, wl.row_width), generator=g, device=dev)
+        self.pool = (x * 64.0).to(torch.float8_e4m3fn).view(torch.uint8) if fp8 else x.to(bf)
+        self.scale = (torch.full((nblk, wl.block_size), 1.0 / 64.0, dtype=torch.float32, device=dev)
+                      if fp8 else None)
+        self.out = torch.empty((wl.batch, wl.q_len, wl.n_heads, wl.v_head_dim), dtype=bf, device=dev)
+        self.lse = torch.empty((wl.batch, wl.q_len, wl.n_heads), dtype=torch.float32, device=dev)
+
+
+def prefill_main(args, torch, synth, b, dev):
+    """One step = mla_prefill over every prompt of the batch for one layer
+    (gather, K/V rebuild, causal attention), inputs resident in HBM; layers
+    rotate as for the decode.  Roofline: the attention kernel against the
+    bf16 MFMA peak, 2 H (N + R + V) flops per visible (query, key) pair."""
+    wl = synth.PREFILL_WORKLOADS[args.prefill]
+    dims = b.Dims.from_workload(wl)
+    B, Sq, H = wl.batch, wl.q_len, wl.n_heads
+    n_layers = min(args.layers, 2)
+    t_setup = time.time()
+    layers = [PrefillLayer(wl, li, dev, torch, synth) for li in range(n_layers)]
+    ws = torch.empty(b.prefill_workspace_size(dims, B, Sq, layers[0].table_host.shape[1]),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s: {n_layers} layers, workspace {ws.numel() / 1e9:.2f} GB")
+    stream = torch.cuda.current_stream(dev)
+
+    def step(L, ev=None):
+        common = (dims, L.q_nope, L.q_pe, L.w_uk, L.w_uv, L.pool, L.scale, L.block_table, L.seq_lens)
+        kw = dict(out=L.out, lse=L.lse, workspace=ws)
+        if ev is not None:
+            ev[0].record(stream)
+        b.prefill(*common, stages=b.PREFILL_GATHER, **kw)
+        if ev is not None:
+            ev[1].record(stream)
+        b.prefill(*common, stages=b.PREFILL_DECOMPRESS, **kw)
+        if ev is not None:
+            ev[2].record(stream)
+        b.prefill(*common, stages=b.PREFILL_ATTEND, **kw)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(layers[i % n_layers])
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(K):
+        step(layers[i % n_layers], evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / K
+    span = lambda j: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) / 1e3
+    g_s, d_s, a_s = span(0), span(1), span(2)
+
+    seq_lens = layers[0].seq_lens_host.astype(np.int64)
+    pairs = sum(int(min(L, L - Sq + s + 1)) for L in seq_lens for s in range(Sq) if L - Sq + s + 1 > 0)
+    attn_flops = pairs * 2 * H * (wl.qk_nope_dim + wl.qk_rope_dim + wl.v_head_dim)
+    dec_flops = int(seq_lens.sum()) * 2 * H * (wl.qk_nope_dim + wl.v_head_dim) * wl.kv_lora_rank
+    tokens = B * Sq
+    value = tokens / (ms_step / 1e3)
+    a_tf, d_tf = attn_flops / a_s / 1e12, dec_flops / d_s / 1e12
+    log(f"step {ms_step:.3f} ms ({value:.4g} prompt tok/s): gather {g_s * 1e6:.0f} us, "
+        f"rebuild {d_s * 1e6:.0f} us ({d_tf:.0f} TFLOP/s), attention {a_s * 1e6:.0f} us "
+        f"({a_tf:.0f} TFLOP/s, {a_tf / BF16_PEAK_TFLOPS:.1%} of {BF16_PEAK_TFLOPS:.0f})")
+    result = {
+        "metric": "MLA prefill tokens/s (decompressed form, causal, one layer)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": B, "prompt": Sq, "ctx": int(seq_lens.max()),
+            "heads": H, "kv_lora_rank": wl.kv_lora_rank, "rope_dim": wl.qk_rope_dim,
+            "block_size": wl.block_size, "paged": wl.paged, "cache_dtype": wl.cache_dtype,
+            "layers_rotated": n_layers,
+            "step": "prefill of every prompt token (gather, K/V rebuild, causal attention), one layer",
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "prefill_attn_kernel",
+            "achieved": round(a_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(a_tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops": attn_flops, "avg_launch_us": round(a_s * 1e6, 2),
+        },
+        "rebuild": {"kernel": "prefill_decompress_kernel", "avg_us": round(d_s * 1e6, 2),
+                    "algorithmic_flops": dec_flops, "tflops": round(d_tf, 1),
+                    "frac": round(d_tf / BF16_PEAK_TFLOPS, 4)},
+        "gather_us": round(g_s * 1e6, 2),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(wl, layers[0], torch)
+    print(json.dumps(result), flush=True)
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump(result, f, indent=1)
+
+
+def prefill_cpu_baseline(wl, L, torch, n_q=8192, heads=tuple(range(16))):
+    """The CPU oracle (naive float64 attention) on a bounded sample: the first
+    n_q queries of prompt 0 (all of it at 8192) for 16 of the 128 heads, each
+    query seeing its causal prefix; the rate is scaled to whole prompt tokens
+    (all heads).  Also checks the GPU output on that sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    torch.cuda.synchronize()
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    nb = (n_q + wl.block_size - 1) // wl.block_size
+    ids = torch.from_numpy(L.table_host[0, :nb].astype(np.int64)).to(L.pool.device)
+    blocks = L.pool.index_select(0, ids).view(-1, wl.row_width)
+    if wl.cache_dtype == "fp8":
+        rows64 = oracle.dequantize_rows_fp8(blocks.cpu().numpy(),
+                                            L.scale.index_select(0, ids).reshape(-1).cpu().numpy())
+    else:
+        rows64 = f64(blocks)
+    rows = oracle.gather_sequence(rows64, np.arange(nb), n_q, wl.block_size)
+    hs = list(heads)
+    qn = f64(L.q_nope[:1, :n_q])[:, :, hs]
+    qp = f64(L.q_pe[:1, :n_q])[:, :, hs]
+    wuk, wuv = f64(L.w_uk)[hs], f64(L.w_uv)[hs]
+    t = time.time()
+    ref, _ = oracle.decode_naive(qn, qp, wuk, wuv, [rows], n_q)
+    dt = time.time() - t
+    got = f64(L.out[:1, :n_q])[:, :, hs]
+    err = float(np.max(np.abs(got - ref)))
+    log(f"cpu oracle: {n_q} queries x {len(hs)} heads in {dt:.1f}s on {threads} threads; "
+        f"GPU vs oracle max-abs {err:.2e}")
+    return {"value": round(n_q * len(hs) / wl.n_heads / dt, 4), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {n_q} of {wl.q_len} queries of prompt 0, heads {hs[0]}-{hs[-1]} of "
+                      f"{wl.n_heads}, naive float64 attention, {dt:.1f}s; rate scaled to all heads",
+            "gpu_vs_oracle_max_abs": err}
 
 
 def cpu_baseline(args, wl, L, torch):

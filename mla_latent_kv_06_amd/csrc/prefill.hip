@@ -302,8 +302,10 @@ constexpr int kPStages = 3;
 constexpr int kPKBytes = PBS * (PN + PDR) * 2;      // 24 KB
 constexpr int kPStage = kPKBytes + PBS * PV * 2;    // 40 KB
 constexpr float kLazy = 8.0f;
+constexpr int kPWaves = 8;               // waves per workgroup (4: 64 queries each, 8: 32)
 
-__global__ __launch_bounds__(256, 1) void prefill_attn_kernel(
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
     const unsigned short* __restrict__ q_nope,   // [batch * q_len][H][128]
     const unsigned short* __restrict__ q_pe,     // [batch * q_len][H][64]
     const unsigned short* __restrict__ kc,       // [batch][H][Tpad][128]
@@ -312,7 +314,9 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(
     const int* __restrict__ seq_lens, int Tmax, int Tpad, int q_len, int nqb, float scale_log2,
     unsigned short* __restrict__ out,            // [batch * q_len][H][128]
     float* __restrict__ lse) {                   // [batch * q_len][H]
-    static_assert(10 * (kPStages - 1) == 20, "the wait below counts the copies of two stages");
+    constexpr int QB = kPQ / (32 * NW);          // query blocks of 32 per wave
+    constexpr int NCP = 40 / NW;                 // copy instructions per wave and tile
+    static_assert(QB * 32 * NW == kPQ && NCP * NW == 40 && 16 % NW == 0 && 24 % NW == 0, "wave split");
     __shared__ __attribute__((aligned(16))) unsigned char smem[kPStages * kPStage];
     MLA_LDS unsigned char* lds = (MLA_LDS unsigned char*)smem;
     const int lane = threadIdx.x & 63;
@@ -327,36 +331,39 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(
     const int len = seq_len_of(seq_lens, b, Tmax);
     const int base_vis = len - q_len;            // query s sees tokens < base_vis + s + 1
     const int q0 = qblk * kPQ;
-    const int qa = q0 + 64 * w;                  // this wave's first query
+    const int qa = q0 + 32 * QB * w;             // this wave's first query
     const int vis_blk = min(len, base_vis + min(q0 + kPQ, q_len));
     const int n_tiles = vis_blk > 0 ? (vis_blk + PBS - 1) / PBS : 0;
-    const int vis_w = qa < q_len ? min(len, base_vis + min(qa + 64, q_len)) : 0;
+    const int vis_w = qa < q_len ? min(len, base_vis + min(qa + 32 * QB, q_len)) : 0;
 
     // ---- copies ----------------------------------------------------------------
     const size_t kv_base = ((size_t)b * PH + h) * Tpad * 128;
     const __amdgpu_buffer_rsrc_t kc_r = p_rsrc(kc + kv_base, (unsigned)Tpad * 256u);
     const __amdgpu_buffer_rsrc_t vv_r = p_rsrc(vv + kv_base, (unsigned)Tpad * 256u);
     const __amdgpu_buffer_rsrc_t kr_r = p_rsrc(kr + (size_t)b * Tpad * PDR, (unsigned)Tpad * 128u);
-    // instruction i = w + 4 j: j < 4 K^C (groups 0-1), j < 6 KR (group 2),
-    // else V (groups 0-1); row 8 (i % 8) + r8 of the tile
-    unsigned voff[10];
+    // instruction i = w + NW j: i < 16 K^C (groups 0-1), i < 24 KR (group 2),
+    // else V (groups 0-1); row 8 (i % 8) + r8 of the tile.  Which tensor is
+    // fixed per j.
+    constexpr int JKC = 16 / NW, JKR = 24 / NW;
+    unsigned voff[NCP];
 #pragma unroll
-    for (int j = 0; j < 10; ++j) {
-        const int i = w + 4 * j;
-        const int ii = j < 4 ? i : (j < 6 ? i - 16 : i - 24);
+    for (int j = 0; j < NCP; ++j) {
+        const int i = w + NW * j;
+        const int ii = j < JKC ? i : (j < JKR ? i - 16 : i - 24);
         const int row = 8 * (ii & 7) + r8;
-        const int chunk = (j < 4 || j >= 6 ? 8 * (ii >> 3) : 0) + (s8 ^ pswz(row));
-        voff[j] = (unsigned)row * (j < 4 || j >= 6 ? 256u : 128u) + (unsigned)chunk * 16u;
+        const bool wide = j < JKC || j >= JKR;
+        const int chunk = (wide ? 8 * (ii >> 3) : 0) + (s8 ^ pswz(row));
+        voff[j] = (unsigned)row * (wide ? 256u : 128u) + (unsigned)chunk * 16u;
     }
     auto issue = [&](int t) {
         MLA_LDS unsigned char* st = lds + (t % kPStages) * kPStage;
         const bool live = t < n_tiles;
 #pragma unroll
-        for (int j = 0; j < 10; ++j) {
-            const bool is_kr = j >= 4 && j < 6;
-            const __amdgpu_buffer_rsrc_t r = j < 4 ? kc_r : (is_kr ? kr_r : vv_r);
+        for (int j = 0; j < NCP; ++j) {
+            const bool is_kr = j >= JKC && j < JKR;
+            const __amdgpu_buffer_rsrc_t r = j < JKC ? kc_r : (is_kr ? kr_r : vv_r);
             const unsigned off = live ? voff[j] + (unsigned)t * (is_kr ? 8192u : 16384u) : 0x80000000u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MLA_LDS void*)(st + (w + 4 * j) * 1024), 16, off,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MLA_LDS void*)(st + (w + NW * j) * 1024), 16, off,
                                                      0, 0, 0);
         }
     };
@@ -366,9 +373,9 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(
 
     // ---- this wave's queries as MFMA B fragments: lane (hf, l32) holds
     // channels 16 ks + 8 hf .. +8 of query qa + 32 qb + l32 (ks < 8: q^C, else q^R)
-    bf16x8 qf[2][12];
+    bf16x8 qf[QB][12];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const int s = qa + 32 * qb + l32;
         const size_t row = ((size_t)b * q_len + min(s, q_len - 1)) * PH + h;
         const bool ok = s < q_len;
@@ -402,116 +409,159 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(
             }
     }
 
-    f32x16 o[2][4];
+    f32x16 o[QB][4];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int cm = 0; cm < 4; ++cm) o[qb][cm] = f32x16{};
-    float m_ref[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
+    float m_ref[QB], l_run[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m_ref[qb] = kNegInf;
+        l_run[qb] = 0.f;
+    }
+
+    // One tile, both halves, ordered so that independent work can overlap:
+    //   S_0 MFMAs | max_0, rare raise | S_1 MFMAs + exp(S_0) | max_1, rare raise
+    //   | PV_0 MFMAs + exp(S_1) | PV_1 MFMAs
+    // A raise after S_1 (its scores exceed the reference) rescales O and l
+    // and recomputes P_0, which S_0's scores still allow.
+    auto score_half = [&](const MLA_LDS unsigned char* st, int hb, f32x16 (&sacc)[QB]) __attribute__((always_inline)) {
+        const MLA_LDS unsigned char* kb = st + hb * 32 * 128;
+        auto ka = [&](int ks) {
+            return *reinterpret_cast<const MLA_LDS bf16x8*>(kb + qk_off[ks & 3] + (ks >> 2) * 8192);
+        };
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb] = f32x16{};
+        bf16x8 a0 = ka(0), a1 = ka(1), a2;
+#pragma unroll
+        for (int ks = 0; ks < 12; ++ks) {
+            if (ks + 2 < 12) a2 = ka(ks + 2);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sacc[qb] = pf_mfma(a0, qf[qb][ks], sacc[qb]);
+            a0 = a1;
+            a1 = a2;
+        }
+    };
+    // lane: query qa + 32 qb + l32, keys t*64 + 32 hb + 8 (i/4) + 4 hf + i%4
+    auto mask_half = [&](int t, int hb, f32x16 (&sacc)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int lim = base_vis + qa + 32 * qb + l32;       // last visible key
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = t * PBS + 32 * hb + 8 * (i >> 2) + 4 * hf + (i & 3);
+                if (key > lim) sacc[qb][i] = kNegInf;
+            }
+        }
+    };
+    // per-query maxima of the half (log2 domain, both lanes of a query), and
+    // the raise: returns true when some reference moved (O and l rescaled)
+    auto raise_half = [&](const f32x16 (&sacc)[QB]) __attribute__((always_inline)) -> bool {
+        float mx[QB];
+        bool raise[QB];
+        bool any = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float hmax = sacc[qb][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) hmax = fmaxf(hmax, sacc[qb][i]);
+            hmax *= scale_log2;
+            mx[qb] = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
+            raise[qb] = mx[qb] > m_ref[qb] + kLazy;
+            any = any || raise[qb];
+        }
+        if (__builtin_amdgcn_ballot_w64(any) == 0) return false;   // uniform
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float alpha = raise[qb] ? __builtin_amdgcn_exp2f(m_ref[qb] - mx[qb]) : 1.0f;
+            m_ref[qb] = raise[qb] ? mx[qb] : m_ref[qb];
+            l_run[qb] *= alpha;
+#pragma unroll
+            for (int cm = 0; cm < 4; ++cm)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[qb][cm][i] *= alpha;
+        }
+        return true;
+    };
+    // weights exp2(s log2(e) scale - m) as bf16 B fragments of the value
+    // product, and their sums.  A query with nothing visible yet has m_ref =
+    // -inf and only -inf scores: its weights are exp2(-inf) = 0.
+    auto exp_half = [&](const f32x16 (&sacc)[QB], bf16x8 (&pf)[QB][2], float (&psum)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float m_use = m_ref[qb] == kNegInf ? 0.f : m_ref[qb];
+            float ps = 0.f;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                u16x8 pu;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][8 * k2 + e], scale_log2, -m_use));
+                    ps += pv;
+                    pu[e] = f32_to_bf16_bits(pv);
+                }
+                pf[qb][k2] = __builtin_bit_cast(bf16x8, pu);
+            }
+            psum[qb] = ps;
+        }
+    };
+    // O^T += V^T . P^T over the half's 32 keys.  K-step k2 covers keys
+    // 32 hb + 16 k2 + {0..3, 8..11} (lanes 0-31) and {4..7, 12..15} (lanes
+    // 32-63), matching P's layout.
+    auto pv_half = [&](const MLA_LDS unsigned char* vt, int hb, const bf16x8 (&pf)[QB][2]) __attribute__((always_inline)) {
+        auto va = [&](int k2, int cm) {
+            const MLA_LDS unsigned char* vb = vt + (cm >> 1) * 8192 + (hb * 32 + k2 * 16) * 128;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + tr_off[cm & 1][0]));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + tr_off[cm & 1][1]));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 v0 = va(0, 0), v1;
+#pragma unroll
+        for (int st8 = 0; st8 < 8; ++st8) {
+            const int k2 = st8 >> 2, cm = st8 & 3;
+            if (st8 + 1 < 8) v1 = va((st8 + 1) >> 2, (st8 + 1) & 3);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) o[qb][cm] = pf_mfma(v0, pf[qb][k2], o[qb][cm]);
+            v0 = v1;
+        }
+    };
 
     for (int t = 0; t < n_tiles; ++t) {
         p_stage_barrier();                       // everyone is done with tile t - 1's stage
         issue(t + 2);
-        p_wait_vmem<20>();                       // this wave's copies of tile t landed
+        p_wait_vmem<NCP * (kPStages - 1)>();     // this wave's copies of tile t landed
         p_stage_barrier();                       // ... and everyone's
         if (t * PBS >= vis_w) continue;          // nothing of this tile is visible to the wave
         const MLA_LDS unsigned char* st = lds + (t % kPStages) * kPStage;
         const MLA_LDS unsigned char* vt = st + kPKBytes;
-        // does the tile reach past the first query's visible range?
+        // does the tile reach past the first query's visible range?  (A half
+        // past the wave's last query is then masked whole: its weights are 0.)
         const bool need_mask = t * PBS + PBS - 1 >= base_vis + qa + 1;
+        f32x16 s0[QB], s1[QB];
+        bf16x8 p0[QB][2], p1[QB][2];
+        float ps0[QB], ps1[QB];
+        score_half(st, 0, s0);
+        if (need_mask) mask_half(t, 0, s0);
+        raise_half(s0);
+        score_half(st, 1, s1);
+        exp_half(s0, p0, ps0);
+        if (need_mask) mask_half(t, 1, s1);
+        if (raise_half(s1)) exp_half(s0, p0, ps0);   // P_0 against the raised reference
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            if (t * PBS + 32 * hb >= vis_w) break;
-            // ---- S^T = K . Q^T ------------------------------------------------------
-            const MLA_LDS unsigned char* kb = st + hb * 32 * 128;
-            auto ka = [&](int ks) {
-                return *reinterpret_cast<const MLA_LDS bf16x8*>(kb + qk_off[ks & 3] + (ks >> 2) * 8192);
-            };
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
-            bf16x8 a0 = ka(0), a1 = ka(1), a2;
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] += ps0[qb];
+        pv_half(vt, 0, p0);
+        exp_half(s1, p1, ps1);
 #pragma unroll
-            for (int ks = 0; ks < 12; ++ks) {
-                if (ks + 2 < 12) a2 = ka(ks + 2);
-                sacc[0] = pf_mfma(a0, qf[0][ks], sacc[0]);
-                sacc[1] = pf_mfma(a0, qf[1][ks], sacc[1]);
-                a0 = a1;
-                a1 = a2;
-            }
-            // lane: query qa + 32 qb + l32, keys t*64 + 32 hb + 8 (i/4) + 4 hf + i%4
-            bf16x8 pf[2][2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                float sv[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sv[i] = sacc[qb][i];
-                if (need_mask) {
-                    const int lim = base_vis + qa + 32 * qb + l32;   // last visible key
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = t * PBS + 32 * hb + 8 * (i >> 2) + 4 * hf + (i & 3);
-                        if (key > lim) sv[i] = kNegInf;
-                    }
-                }
-                float hmax = sv[0];
-#pragma unroll
-                for (int i = 1; i < 16; ++i) hmax = fmaxf(hmax, sv[i]);
-                hmax *= scale_log2;
-                hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
-                const bool raise = hmax > m_ref[qb] + kLazy;
-                if (__builtin_amdgcn_ballot_w64(raise) != 0) {     // uniform
-                    const float alpha = raise ? __builtin_amdgcn_exp2f(m_ref[qb] - hmax) : 1.0f;
-                    m_ref[qb] = raise ? hmax : m_ref[qb];
-                    l_run[qb] *= alpha;
-#pragma unroll
-                    for (int cm = 0; cm < 4; ++cm)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) o[qb][cm][i] *= alpha;
-                }
-                // a query with nothing visible yet has m_ref = -inf and only
-                // -inf scores: its weights are exp2(-inf) = 0
-                const float m_use = m_ref[qb] == kNegInf ? 0.f : m_ref[qb];
-                float psum = 0.f;
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
-                    u16x8 pu;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[8 * k2 + e], scale_log2, -m_use));
-                        psum += pv;
-                        pu[e] = f32_to_bf16_bits(pv);
-                    }
-                    pf[qb][k2] = __builtin_bit_cast(bf16x8, pu);
-                }
-                l_run[qb] += psum;
-            }
-            // ---- O^T += V^T . P^T ----------------------------------------------------
-            // K-step k2 covers keys 32 hb + 16 k2 + {0..3, 8..11} (lanes 0-31) and
-            // {4..7, 12..15} (lanes 32-63), matching P's layout
-            auto va = [&](int k2, int cm) {
-                const MLA_LDS unsigned char* vb = vt + (cm >> 1) * 8192 + (hb * 32 + k2 * 16) * 128;
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (MLA_LDS bf16x4*)(vb + tr_off[cm & 1][0]));
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (MLA_LDS bf16x4*)(vb + tr_off[cm & 1][1]));
-                return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            };
-            bf16x8 v0 = va(0, 0), v1;
-#pragma unroll
-            for (int st8 = 0; st8 < 8; ++st8) {
-                const int k2 = st8 >> 2, cm = st8 & 3;
-                if (st8 + 1 < 8) v1 = va((st8 + 1) >> 2, (st8 + 1) & 3);
-                o[0][cm] = pf_mfma(v0, pf[0][k2], o[0][cm]);
-                o[1][cm] = pf_mfma(v0, pf[1][k2], o[1][cm]);
-                v0 = v1;
-            }
-        }
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] += ps1[qb];
+        pv_half(vt, 1, p1);
     }
     p_wait_vmem<0>();                            // the record-less copies too
 
     // ---- epilogue: out = O / l, lse = (m + log2 l) ln 2 ------------------------------
     // o[qb][cm][i]: channel 32 cm + 8 (i/4) + 4 hf + i%4 of query qa + 32 qb + l32
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const int s = qa + 32 * qb + l32;
         const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);   // disjoint keys
         if (s >= q_len) continue;
@@ -552,7 +602,7 @@ hipError_t launch_prefill(const PrefillLaunch& a) {
     }
     if (a.stages & 4u) {
         const int nqb = (a.q_len + kPQ - 1) / kPQ;
-        prefill_attn_kernel<<<a.batch * PH * nqb, 256, 0, a.stream>>>(
+        prefill_attn_kernel<kPWaves><<<a.batch * PH * nqb, kPWaves * 64, 0, a.stream>>>(
             static_cast<const unsigned short*>(a.q_nope), static_cast<const unsigned short*>(a.q_pe), a.kc,
             a.vv, a.kr, a.seq_lens, Tmax, Tpad, a.q_len, nqb, a.scale * kLog2e,
             static_cast<unsigned short*>(a.out), a.lse);

@@ -103,6 +103,17 @@ WORKLOADS = {
                                         append=True),
 }
 
+# Prefill measurement point: two fresh 8192-token prompts (nothing cached
+# before them), paged, bf16; every query sees its causal prefix.
+PREFILL_WORKLOADS = {
+    "v3_prefill_b2_8k_bf16": Workload("v3_prefill_b2_8k_bf16", **_V3, batch=2, q_len=8192,
+                                      ctx_lo=0, ctx_hi=0, paged=True, cache_dtype="bf16",
+                                      act_dtype="bf16"),
+    "v3_prefill_b2_8k_fp8": Workload("v3_prefill_b2_8k_fp8", **_V3, batch=2, q_len=8192,
+                                     ctx_lo=0, ctx_hi=0, paged=True, cache_dtype="fp8",
+                                     act_dtype="bf16"),
+}
+
 
 def _rng(seed: int, *tags: int) -> np.random.Generator:
     return np.random.default_rng([int(seed), *[int(t) for t in tags]])

@@ -37,3 +37,9 @@ def test_weight_scales():
     assert abs(synth.w_uk(wl).std() * np.sqrt(512) - 1) < 0.01
     assert abs(synth.w_uv(wl).std() * np.sqrt(512) - 1) < 0.01
     assert abs(synth.w_kv_a(wl).std() * np.sqrt(7168) - 1) < 0.01
+
+
+def test_prefill_workloads():
+    for wl in synth.PREFILL_WORKLOADS.values():
+        assert synth.seq_lens(wl).tolist() == [8192, 8192]        # fresh prompts
+        assert wl.n_heads == 128 and wl.kv_lora_rank == 512 and wl.block_size == 64
