@@ -421,57 +421,66 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
         l_run[qb] = 0.f;
     }
 
-    // One tile, both halves, ordered so that independent work can overlap:
-    //   S_0 MFMAs | max_0, rare raise | S_1 MFMAs + exp(S_0) | max_1, rare raise
-    //   | PV_0 MFMAs + exp(S_1) | PV_1 MFMAs
-    // A raise after S_1 (its scores exceed the reference) rescales O and l
-    // and recomputes P_0, which S_0's scores still allow.
-    auto score_half = [&](const MLA_LDS unsigned char* st, int hb, f32x16 (&sacc)[QB]) __attribute__((always_inline)) {
-        const MLA_LDS unsigned char* kb = st + hb * 32 * 128;
-        auto ka = [&](int ks) {
-            return *reinterpret_cast<const MLA_LDS bf16x8*>(kb + qk_off[ks & 3] + (ks >> 2) * 8192);
+    // One tile: the scores of both halves (32 keys each) as two interleaved
+    // MFMA chains, one maximum and reference check per query over the tile's
+    // 64 keys, the weights, then the value product over four accumulators.
+    // (A wave's dependent MFMAs would otherwise wait on each other; the
+    // second wave of the SIMD fills the remaining gaps.)
+    auto scores = [&](const MLA_LDS unsigned char* st, f32x16 (&sacc)[2][QB]) __attribute__((always_inline)) {
+        auto ka = [&](int hb, int ks) {
+            return *reinterpret_cast<const MLA_LDS bf16x8*>(st + hb * 32 * 128 + qk_off[ks & 3] + (ks >> 2) * 8192);
         };
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[qb] = f32x16{};
-        bf16x8 a0 = ka(0), a1 = ka(1), a2;
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sacc[hb][qb] = f32x16{};
+        bf16x8 a0[2] = {ka(0, 0), ka(1, 0)}, a1[2] = {ka(0, 1), ka(1, 1)}, a2[2];
 #pragma unroll
         for (int ks = 0; ks < 12; ++ks) {
-            if (ks + 2 < 12) a2 = ka(ks + 2);
+            if (ks + 2 < 12) {
+                a2[0] = ka(0, ks + 2);
+                a2[1] = ka(1, ks + 2);
+            }
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sacc[qb] = pf_mfma(a0, qf[qb][ks], sacc[qb]);
-            a0 = a1;
-            a1 = a2;
-        }
-    };
-    // lane: query qa + 32 qb + l32, keys t*64 + 32 hb + 8 (i/4) + 4 hf + i%4
-    auto mask_half = [&](int t, int hb, f32x16 (&sacc)[QB]) __attribute__((always_inline)) {
+            for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int lim = base_vis + qa + 32 * qb + l32;       // last visible key
+                for (int qb = 0; qb < QB; ++qb) sacc[hb][qb] = pf_mfma(a0[hb], qf[qb][ks], sacc[hb][qb]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = t * PBS + 32 * hb + 8 * (i >> 2) + 4 * hf + (i & 3);
-                if (key > lim) sacc[qb][i] = kNegInf;
+            for (int hb = 0; hb < 2; ++hb) {
+                a0[hb] = a1[hb];
+                a1[hb] = a2[hb];
             }
         }
     };
-    // per-query maxima of the half (log2 domain, both lanes of a query), and
-    // the raise: returns true when some reference moved (O and l rescaled)
-    auto raise_half = [&](const f32x16 (&sacc)[QB]) __attribute__((always_inline)) -> bool {
+    // lane: query qa + 32 qb + l32, keys t*64 + 32 hb + 8 (i/4) + 4 hf + i%4
+    auto mask_tile = [&](int t, f32x16 (&sacc)[2][QB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int lim = base_vis + qa + 32 * qb + l32 - t * PBS - 4 * hf;   // last visible key, relative
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * hb + 8 * (i >> 2) + (i & 3) > lim) sacc[hb][qb][i] = kNegInf;
+        }
+    };
+    // per-query maxima over the tile (log2 domain, both lanes of a query) and
+    // the raise of the reference when they exceed it by more than kLazy
+    auto raise_tile = [&](const f32x16 (&sacc)[2][QB]) __attribute__((always_inline)) {
         float mx[QB];
         bool raise[QB];
         bool any = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float hmax = sacc[qb][0];
+            float hmax = fmaxf(sacc[0][qb][0], sacc[1][qb][0]);
 #pragma unroll
-            for (int i = 1; i < 16; ++i) hmax = fmaxf(hmax, sacc[qb][i]);
+            for (int i = 1; i < 16; ++i) hmax = fmaxf(hmax, fmaxf(sacc[0][qb][i], sacc[1][qb][i]));
             hmax *= scale_log2;
             mx[qb] = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
             raise[qb] = mx[qb] > m_ref[qb] + kLazy;
             any = any || raise[qb];
         }
-        if (__builtin_amdgcn_ballot_w64(any) == 0) return false;   // uniform
+        if (__builtin_amdgcn_ballot_w64(any) == 0) return;   // uniform
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const float alpha = raise[qb] ? __builtin_amdgcn_exp2f(m_ref[qb] - mx[qb]) : 1.0f;
@@ -482,47 +491,50 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[qb][cm][i] *= alpha;
         }
-        return true;
     };
     // weights exp2(s log2(e) scale - m) as bf16 B fragments of the value
-    // product, and their sums.  A query with nothing visible yet has m_ref =
-    // -inf and only -inf scores: its weights are exp2(-inf) = 0.
-    auto exp_half = [&](const f32x16 (&sacc)[QB], bf16x8 (&pf)[QB][2], float (&psum)[QB]) __attribute__((always_inline)) {
+    // product (pf[hb][qb][k2]), summed into l.  A query with nothing visible
+    // yet has m_ref = -inf and only -inf scores: its weights are exp2(-inf) = 0.
+    auto weights = [&](const f32x16 (&sacc)[2][QB], bf16x8 (&pf)[2][QB][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const float m_use = m_ref[qb] == kNegInf ? 0.f : m_ref[qb];
             float ps = 0.f;
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                u16x8 pu;
+            for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][8 * k2 + e], scale_log2, -m_use));
-                    ps += pv;
-                    pu[e] = f32_to_bf16_bits(pv);
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    u16x8 pu;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float pv = __builtin_amdgcn_exp2f(
+                            __builtin_fmaf(sacc[hb][qb][8 * k2 + e], scale_log2, -m_use));
+                        ps += pv;
+                        pu[e] = f32_to_bf16_bits(pv);
+                    }
+                    pf[hb][qb][k2] = __builtin_bit_cast(bf16x8, pu);
                 }
-                pf[qb][k2] = __builtin_bit_cast(bf16x8, pu);
-            }
-            psum[qb] = ps;
+            l_run[qb] += ps;
         }
     };
-    // O^T += V^T . P^T over the half's 32 keys.  K-step k2 covers keys
+    // O^T += V^T . P^T over the tile's 64 keys.  K-step (hb, k2) covers keys
     // 32 hb + 16 k2 + {0..3, 8..11} (lanes 0-31) and {4..7, 12..15} (lanes
-    // 32-63), matching P's layout.
-    auto pv_half = [&](const MLA_LDS unsigned char* vt, int hb, const bf16x8 (&pf)[QB][2]) __attribute__((always_inline)) {
-        auto va = [&](int k2, int cm) {
-            const MLA_LDS unsigned char* vb = vt + (cm >> 1) * 8192 + (hb * 32 + k2 * 16) * 128;
+    // 32-63), matching P's layout; consecutive MFMAs update different
+    // accumulators.
+    auto values = [&](const MLA_LDS unsigned char* vt, const bf16x8 (&pf)[2][QB][2]) __attribute__((always_inline)) {
+        auto va = [&](int kk, int cm) {
+            const MLA_LDS unsigned char* vb = vt + (cm >> 1) * 8192 + kk * 16 * 128;
             const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + tr_off[cm & 1][0]));
             const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + tr_off[cm & 1][1]));
             return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         };
         bf16x8 v0 = va(0, 0), v1;
 #pragma unroll
-        for (int st8 = 0; st8 < 8; ++st8) {
-            const int k2 = st8 >> 2, cm = st8 & 3;
-            if (st8 + 1 < 8) v1 = va((st8 + 1) >> 2, (st8 + 1) & 3);
+        for (int st16 = 0; st16 < 16; ++st16) {
+            const int kk = st16 >> 2, cm = st16 & 3;      // kk = 2 hb + k2
+            if (st16 + 1 < 16) v1 = va((st16 + 1) >> 2, (st16 + 1) & 3);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) o[qb][cm] = pf_mfma(v0, pf[qb][k2], o[qb][cm]);
+            for (int qb = 0; qb < QB; ++qb) o[qb][cm] = pf_mfma(v0, pf[kk >> 1][qb][kk & 1], o[qb][cm]);
             v0 = v1;
         }
     };
@@ -534,27 +546,16 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
         p_stage_barrier();                       // ... and everyone's
         if (t * PBS >= vis_w) continue;          // nothing of this tile is visible to the wave
         const MLA_LDS unsigned char* st = lds + (t % kPStages) * kPStage;
-        const MLA_LDS unsigned char* vt = st + kPKBytes;
         // does the tile reach past the first query's visible range?  (A half
         // past the wave's last query is then masked whole: its weights are 0.)
         const bool need_mask = t * PBS + PBS - 1 >= base_vis + qa + 1;
-        f32x16 s0[QB], s1[QB];
-        bf16x8 p0[QB][2], p1[QB][2];
-        float ps0[QB], ps1[QB];
-        score_half(st, 0, s0);
-        if (need_mask) mask_half(t, 0, s0);
-        raise_half(s0);
-        score_half(st, 1, s1);
-        exp_half(s0, p0, ps0);
-        if (need_mask) mask_half(t, 1, s1);
-        if (raise_half(s1)) exp_half(s0, p0, ps0);   // P_0 against the raised reference
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) l_run[qb] += ps0[qb];
-        pv_half(vt, 0, p0);
-        exp_half(s1, p1, ps1);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) l_run[qb] += ps1[qb];
-        pv_half(vt, 1, p1);
+        f32x16 sacc[2][QB];
+        bf16x8 pf[2][QB][2];
+        scores(st, sacc);
+        if (need_mask) mask_tile(t, sacc);
+        raise_tile(sacc);
+        weights(sacc, pf);
+        values(st + kPKBytes, pf);
     }
     p_wait_vmem<0>();                            // the record-less copies too
 
