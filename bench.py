@@ -51,6 +51,29 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
+PREFILL_SOURCES = ("prefill.hip", "prefill.hpp", "common.hpp", "internal.hpp")
+PREFILL_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "prefill_attn_kernel_v3_b2_8k_bf16_hbm_traffic.txt")
+
+
+def prefill_traffic(workload):
+    """HBM bytes per prefill attention launch from the committed counter
+    summary, or None when it was taken on other sources or another workload."""
+    import hashlib
+    import re
+    if workload != "v3_prefill_b2_8k_bf16" or not os.path.exists(PREFILL_TRAFFIC_PROFILE):
+        return None
+    h = hashlib.sha256()
+    for f in PREFILL_SOURCES:
+        with open(os.path.join(ROOT, "mla_latent_kv_06_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    text = open(PREFILL_TRAFFIC_PROFILE).read()
+    d = re.search(r"first 16 hex\):\s*([0-9a-f]{16})", text)
+    t = re.search(r"total HBM traffic per launch\s*=\s*([0-9,]+) B", text)
+    if not d or not t or d.group(1) != h.hexdigest()[:16]:
+        return None
+    return int(t.group(1).replace(",", ""))
+
+
 def profiled_traffic(workload):
     """HBM bytes per split-KV launch from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE, copy-calibrated), or None when that summary
@@ -450,7 +473,8 @@ def prefill_main(args, torch, synth, b, dev):
         "roofline": {
             "bound": "mfma", "kernel": "prefill_attn_kernel",
             "achieved": round(a_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(a_tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "frac": round(a_tf / BF16_PEAK_TFLOPS, 4), "traffic": prefill_traffic(wl.name),
+            "traffic_unit": "bytes per launch",
             "algorithmic_flops": attn_flops, "avg_launch_us": round(a_s * 1e6, 2),
         },
         "rebuild": {"kernel": "prefill_decompress_kernel", "avg_us": round(d_s * 1e6, 2),

@@ -270,8 +270,9 @@ mla_status mla_decode_absorbed_stages(const mla_dims* dims, int32_t batch, int32
  * Requirements (else MLA_ERR_BAD_SHAPE / MLA_ERR_UNSUPPORTED): act_dtype
  * MLA_BF16; d_model a multiple of 64 in [64, 65536]; q_lora_rank 0 or a
  * multiple of 64 up to 2048; n_heads *
- * qk_nope_dim and n_heads * qk_rope_dim multiples of 32; batch * q_len <=
- * 65536; every operand under 2 GiB.  Every tensor 16-byte aligned.
+ * qk_nope_dim and n_heads * qk_rope_dim multiples of 32; q_len and batch *
+ * q_len at most 65536 (a whole prompt may be projected at once); every
+ * operand under 2 GiB.  Every tensor 16-byte aligned.
  * Of mla_dims only the head shape and act_dtype are used (all fields are
  * validated as for the other calls). */
 mla_status mla_query_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,

@@ -121,7 +121,7 @@ bool append_streams(const mla_dims& d, long long T, int d_model) {
 // partial slices of the append's MFMA projection
 int append_slices(const mla_dims& d, long long T, int d_model) {
     return append_streams(d, T, d_model)
-               ? mla::append_stream_splits(d.kv_lora_rank + d.qk_rope_dim, d_model)
+               ? mla::append_stream_splits(d.kv_lora_rank + d.qk_rope_dim, d_model, T)
                : append_kc(d_model);
 }
 
@@ -215,8 +215,8 @@ mla_status check_query_shape(const mla_dims* dims, int32_t batch, int32_t q_len,
     const mla_dims& d = *dims;
     if (d.act_dtype != MLA_BF16)
         return fail(MLA_ERR_UNSUPPORTED, "the query path needs act_dtype MLA_BF16");
-    if (batch < 0 || q_len < 1 || q_len > 1024)
-        return fail(MLA_ERR_BAD_SHAPE, "batch=%d must be >= 0 and q_len=%d in [1, 1024]", batch, q_len);
+    if (batch < 0 || q_len < 1 || q_len > 65536)
+        return fail(MLA_ERR_BAD_SHAPE, "batch=%d must be >= 0 and q_len=%d in [1, 65536]", batch, q_len);
     if ((long long)batch * q_len > 65536)
         return fail(MLA_ERR_BAD_SHAPE, "batch * q_len = %lld exceeds 65536", (long long)batch * q_len);
     if (d_model < 64 || d_model > 65536 || d_model % 64)
@@ -246,7 +246,7 @@ QueryWs query_ws(int batch, int q_len, int d_model, int q_lora_rank) {
     QueryWs w{};
     if (q_lora_rank == 0) return w;
     const size_t T = (size_t)batch * q_len;
-    w.kc = mla::query_splits(q_lora_rank, d_model);
+    w.kc = mla::query_splits(q_lora_rank, d_model, (long long)T);
     w.part = 0;
     w.cq = align_up((size_t)w.kc * T * q_lora_rank * 4, 256);
     w.total = w.cq + align_up(T * q_lora_rank * 2, 256);

@@ -213,9 +213,9 @@ hipError_t finalize(const AppendLaunch& a) {
 
 }  // namespace
 
-int append_stream_splits(int Dout, int d_model) {
+int append_stream_splits(int Dout, int d_model, long long T) {
     // the finalize adds at most 32 partial slices on its fast path
-    return stream_gemm_splits(Dout, d_model, 32);
+    return stream_gemm_splits(Dout, d_model, 32, T);
 }
 
 hipError_t launch_append(const AppendLaunch& a, bool mfma_gemm) {
@@ -224,7 +224,8 @@ hipError_t launch_append(const AppendLaunch& a, bool mfma_gemm) {
     const int Dout = a.DC + a.DR;
     if (mfma_gemm && a.stream_gemm) {
         const int n_ob = (Dout / 32 + kQWaves - 1) / kQWaves;
-        stream_gemm_mfma<true><<<n_ob * a.kc, kQWaves * kWave, 0, a.stream>>>(
+        const dim3 grid(n_ob * a.kc, stream_gemm_row_groups(T));
+        stream_gemm_mfma<true><<<grid, kQWaves * kWave, 0, a.stream>>>(
             static_cast<const unsigned short*>(a.h), T, a.d_model,
             static_cast<const unsigned short*>(a.w_kv_a), nullptr, Dout, 0, 2, 1, nullptr, 1.0f, nullptr,
             nullptr, a.part, n_ob);

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kQFinThreads) void query_latent_finalize(
 
 }  // namespace
 
-int query_splits(int d_q, int K) { return stream_gemm_splits(d_q, K, kNumCUs); }
+int query_splits(int d_q, int K, long long T) { return stream_gemm_splits(d_q, K, kNumCUs, T); }
 
 hipError_t launch_query(const QueryLaunch& a) {
     if (a.T == 0) return hipSuccess;
@@ -83,7 +83,7 @@ hipError_t launch_query(const QueryLaunch& a) {
     if (a.q_lora > 0) {
         // c_Q partial sums: W_DQ as the single weight tensor, depth split a.kc ways
         const int n_ob = (a.q_lora / 32 + kQWaves - 1) / kQWaves;
-        stream_gemm_mfma<true><<<n_ob * a.kc, kQWaves * kWave, 0, a.stream>>>(
+        stream_gemm_mfma<true><<<dim3(n_ob * a.kc, stream_gemm_row_groups(a.T)), kQWaves * kWave, 0, a.stream>>>(
             x, a.T, a.d_model, static_cast<const unsigned short*>(a.w_dq), nullptr, a.q_lora, 0, 2, 1,
             a.start_pos, a.rope_base, nullptr, nullptr, a.part, n_ob);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
@@ -96,7 +96,7 @@ hipError_t launch_query(const QueryLaunch& a) {
     const int HN = a.H * a.N, HR = a.H * a.R;
     const int n_mb = (HN + HR) / 32;
     const int n_ob = (n_mb + kQWaves - 1) / kQWaves;
-    stream_gemm_mfma<false><<<n_ob, kQWaves * kWave, 0, a.stream>>>(
+    stream_gemm_mfma<false><<<dim3(n_ob, stream_gemm_row_groups(a.T)), kQWaves * kWave, 0, a.stream>>>(
         x, a.T, K, static_cast<const unsigned short*>(a.w_uq),
         static_cast<const unsigned short*>(a.w_qr), HN, HR, a.R, a.q_len, a.start_pos, a.rope_base,
         static_cast<unsigned short*>(a.q_nope), static_cast<unsigned short*>(a.q_pe), nullptr, n_ob);

@@ -27,10 +27,12 @@ struct QueryLaunch {
 
 hipError_t launch_query(const QueryLaunch& a);
 
-// Depth splits of the query down-projection (workspace partial slices).
-int query_splits(int q_lora, int d_model);
+// Depth splits of the query down-projection for T rows (workspace partial
+// slices).
+int query_splits(int q_lora, int d_model, long long T);
 // Depth splits of the cache append's projection on the weight-streaming
-// GEMM (which needs d_model a multiple of 64 and operands under 2 GiB).
-int append_stream_splits(int Dout, int d_model);
+// GEMM for T rows (which needs d_model a multiple of 64 and operands under
+// 2 GiB).
+int append_stream_splits(int Dout, int d_model, long long T);
 
 }  // namespace mla

@@ -226,12 +226,19 @@ __global__ __launch_bounds__(kQWaves * kWave) void stream_gemm_mfma(
     }
 }
 
-// Depth splits for the PART mode: enough workgroups for the compute units,
-// at most max_splits and at most one per 64-column chunk.
-inline int stream_gemm_splits(int n_out, int K, int max_splits) {
-    const int n_ob = (n_out / 32 + kQWaves - 1) / kQWaves;
-    const int s = kNumCUs / n_ob;
-    return s < 1 ? 1 : (s > max_splits ? max_splits : (s > K / 64 ? K / 64 : s));
+// Row-pass groups (gridDim.y) for T rows: one pass of kQRows rows each.
+inline int stream_gemm_row_groups(long long T) {
+    const long long g = (T + kQRows - 1) / kQRows;
+    return (int)(g < 1 ? 1 : (g > 65535 ? 65535 : g));
+}
+
+// Depth splits for the PART mode: enough workgroups for the compute units
+// together with the row-pass groups, at most max_splits and at most one per
+// 64-column chunk (1 once the row passes alone fill the chip).
+inline int stream_gemm_splits(int n_out, int K, int max_splits, long long T) {
+    const long long n_ob = (n_out / 32 + kQWaves - 1) / kQWaves;
+    const long long s = kNumCUs / (n_ob * stream_gemm_row_groups(T));
+    return (int)(s < 1 ? 1 : (s > max_splits ? max_splits : (s > K / 64 ? K / 64 : s)));
 }
 
 }  // namespace

@@ -29,3 +29,13 @@ def test_traffic_only_for_matching_sources_and_workload(tmp_path, monkeypatch):
     assert bench.profiled_traffic("tiny_f32") is None
     prof.write_text("first 16 hex): 0000000000000000\n  total HBM traffic per launch = 1,234 B\n")
     assert bench.profiled_traffic("v3_b64_ctx8k_paged_bf16") is None
+
+
+def test_prefill_traffic_only_for_matching_sources_and_workload(tmp_path, monkeypatch):
+    # the committed summary matches the committed prefill sources
+    assert bench.prefill_traffic("v3_prefill_b2_8k_bf16") is not None
+    assert bench.prefill_traffic("v3_prefill_b2_8k_fp8") is None
+    prof = tmp_path / "p.txt"
+    prof.write_text("first 16 hex): 0000000000000000\n  total HBM traffic per launch = 1,234 B\n")
+    monkeypatch.setattr(bench, "PREFILL_TRAFFIC_PROFILE", str(prof))
+    assert bench.prefill_traffic("v3_prefill_b2_8k_bf16") is None
