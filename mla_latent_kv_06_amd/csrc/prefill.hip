@@ -71,6 +71,15 @@ __device__ __forceinline__ void p_stage_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// max(a, b, c) in one instruction.  (fmaxf on matrix-core results first
+// quiets each input in IEEE mode, one extra instruction per value; the
+// scores here are never NaN: masked ones are -inf.)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ int seq_len_of(const int* __restrict__ seq_lens, int b, int Tmax) {
     return min(max(seq_lens[b], 0), Tmax);
 }
@@ -426,9 +435,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
     // 64 keys, the weights, then the value product over four accumulators.
     // (A wave's dependent MFMAs would otherwise wait on each other; the
     // second wave of the SIMD fills the remaining gaps.)
+    // LDS addresses: a per-lane base per tile (stage + lane offset), plus
+    // constants that fit the instructions' offset field
     auto scores = [&](const MLA_LDS unsigned char* st, f32x16 (&sacc)[2][QB]) __attribute__((always_inline)) {
+        const MLA_LDS unsigned char* kb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kb[j] = st + qk_off[j];
         auto ka = [&](int hb, int ks) {
-            return *reinterpret_cast<const MLA_LDS bf16x8*>(st + hb * 32 * 128 + qk_off[ks & 3] + (ks >> 2) * 8192);
+            return *reinterpret_cast<const MLA_LDS bf16x8*>(kb[ks & 3] + (hb * 32 * 128 + (ks >> 2) * 8192));
         };
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
@@ -472,9 +486,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
         bool any = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float hmax = fmaxf(sacc[0][qb][0], sacc[1][qb][0]);
+            float hmax = max3f(sacc[0][qb][0], sacc[1][qb][0], sacc[0][qb][1]);
+            hmax = max3f(hmax, sacc[1][qb][1], sacc[0][qb][2]);
 #pragma unroll
-            for (int i = 1; i < 16; ++i) hmax = fmaxf(hmax, fmaxf(sacc[0][qb][i], sacc[1][qb][i]));
+            for (int i = 2; i < 15; ++i) hmax = max3f(hmax, sacc[1][qb][i], sacc[0][qb][i + 1]);
+            hmax = fmaxf(hmax, sacc[1][qb][15]);
             hmax *= scale_log2;
             mx[qb] = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
             raise[qb] = mx[qb] > m_ref[qb] + kLazy;
@@ -522,10 +538,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
     // 32-63), matching P's layout; consecutive MFMAs update different
     // accumulators.
     auto values = [&](const MLA_LDS unsigned char* vt, const bf16x8 (&pf)[2][QB][2]) __attribute__((always_inline)) {
+        const MLA_LDS unsigned char* vb[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) vb[j][e] = vt + tr_off[j][e];
         auto va = [&](int kk, int cm) {
-            const MLA_LDS unsigned char* vb = vt + (cm >> 1) * 8192 + kk * 16 * 128;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + tr_off[cm & 1][0]));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + tr_off[cm & 1][1]));
+            const int c = (cm >> 1) * 8192 + kk * 16 * 128;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb[cm & 1][0] + c));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb[cm & 1][1] + c));
             return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         };
         bf16x8 v0 = va(0, 0), v1;
