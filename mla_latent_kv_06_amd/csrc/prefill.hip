@@ -20,9 +20,9 @@
 //                  sees tokens 0 .. L - q_len + s (the decode's rule).
 //
 // Workspace rows of sequence b start at b * Tpad (Tpad = max_blocks * 64
-// rounded up to 128), so the host never reads lengths.  Token tiles past a
+// rounded up to 256), so the host never reads lengths.  Token tiles past a
 // sequence's length are skipped by every kernel; the gather zeroes the rows
-// between the length and the next multiple of 128, which the decompression
+// between the length and the next multiple of 256, which the decompression
 // reads.
 
 #include "common.hpp"
@@ -38,6 +38,7 @@ constexpr int PDR = 64;                 // rotary width
 constexpr int PN = 128;                 // q_nope / k^C width
 constexpr int PV = 128;                 // value width
 constexpr int PBS = 64;                 // tokens per cache block
+constexpr int kDTok = 256;              // tokens per rebuild tile (workspace rows round up to it)
 
 __device__ __forceinline__ f32x16 pf_mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(
     const int per = Tpad / PBS;
     const int b = blockIdx.x / per, k = blockIdx.x - b * per;
     const int len = seq_len_of(seq_lens, b, Tmax);
-    const int lim = (len + 127) / 128 * 128;
+    const int lim = (len + kDTok - 1) / kDTok * kDTok;   // the rebuild reads whole tiles
     if (k * PBS >= lim) return;
     const long long blk = k * PBS < len ? block_table[(size_t)b * max_blocks + k] : 0;
     const size_t row0 = (size_t)b * Tpad + (size_t)k * PBS;
@@ -156,28 +157,30 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(
 // 2. decompression
 // ---------------------------------------------------------------------------
 
-// grid: H * batch * Tpad / 128 workgroups of 256 (head fastest: the 16 heads
+// grid: H * batch * Tpad / 256 workgroups of 512 (head fastest: the 16 heads
 // an XCD receives keep their weights, 4 MB, in its L2).  Workgroup (h, b,
-// tile) computes, for tokens t0 .. t0 + 128 of sequence b, the 256 outputs
-// [W_UK[h] ; W_UV[h]] X^T: wave w owns outputs 64 w .. +64 (waves 0-1 the
-// keys, 2-3 the values) for all 128 tokens.  The depth 512 is walked in
-// chunks of 64 columns, copied HBM -> LDS by the buffer-to-LDS path two
-// stages deep (one chunk in flight while one is multiplied): per stage 256
-// weight rows and 128 token rows of 128 bytes, 48 copy instructions, 12 per
-// wave.  Instruction i covers rows 8 i .. 8 i + 7 of the stage (weights, then
-// tokens), LDS bytes 1024 i .. +1024.
-constexpr int kDTok = 128;
+// tile) computes, for tokens t0 .. t0 + 256 of sequence b, the 256 outputs
+// [W_UK[h] ; W_UV[h]] X^T: wave w owns outputs 64 (w % 4) .. +64 (waves with
+// w % 4 < 2 the keys, the others the values) for tokens 128 (w / 4) .. +128.
+// The depth 512 is walked in chunks of 64 columns, copied HBM -> LDS by the
+// buffer-to-LDS path two stages deep (one chunk in flight while one is
+// multiplied): per stage 256 weight rows and 256 token rows of 128 bytes, 64
+// copy instructions, 8 per wave.  Instruction i covers rows 8 i .. 8 i + 7 of
+// the stage (weights, then tokens), LDS bytes 1024 i .. +1024.  Two waves per
+// SIMD; each byte copied into LDS feeds twice the products of a 128-token
+// tile.
 constexpr int kDOut = 256;
 constexpr int kDWBytes = kDOut * 128;
-constexpr int kDStage = kDWBytes + kDTok * 128;      // 48 KB
+constexpr int kDStage = kDWBytes + kDTok * 128;      // 64 KB
 constexpr int kDOutStride = 144;                     // bytes per token row of the store staging
+constexpr int kDLds = 8 * 128 * kDOutStride > 2 * kDStage ? 8 * 128 * kDOutStride : 2 * kDStage;
 
-__global__ __launch_bounds__(256, 1) void prefill_decompress_kernel(
+__global__ __launch_bounds__(512, 1) void prefill_decompress_kernel(
     const unsigned short* __restrict__ x, const float* __restrict__ ts,
     const unsigned short* __restrict__ w_uk, const unsigned short* __restrict__ w_uv,
     const int* __restrict__ seq_lens, int Tmax, int Tpad,
     unsigned short* __restrict__ kc, unsigned short* __restrict__ vv) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kDStage];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kDLds];
     MLA_LDS unsigned char* lds = (MLA_LDS unsigned char*)smem;
     const int h = blockIdx.x % PH;
     const int tile = blockIdx.x / PH;
@@ -189,25 +192,26 @@ __global__ __launch_bounds__(256, 1) void prefill_decompress_kernel(
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, hf = lane >> 5;
     const int r8 = lane >> 3, s8 = lane & 7;
+    const int wo = w & 3, wt = w >> 2;               // output quarter, token half
 
     const __amdgpu_buffer_rsrc_t wk_r = p_rsrc(w_uk + (size_t)h * PN * PDC, PN * PDC * 2);
     const __amdgpu_buffer_rsrc_t wv_r = p_rsrc(w_uv + (size_t)h * PV * PDC, PV * PDC * 2);
     const __amdgpu_buffer_rsrc_t x_r = p_rsrc(x + ((size_t)b * Tpad + t0) * PDC, kDTok * PDC * 2);
-    // instruction i = w + 4 j: j < 4 W_UK rows, j < 8 W_UV rows, else token rows
-    unsigned voff[12];
+    // instruction i = w + 8 j: j < 2 W_UK rows, j < 4 W_UV rows, else token rows
+    unsigned voff[8];
 #pragma unroll
-    for (int j = 0; j < 12; ++j) {
-        const int i = w + 4 * j;
-        const int row = 8 * (j < 4 ? i : (j < 8 ? i - 16 : i - 32)) + r8;
+    for (int j = 0; j < 8; ++j) {
+        const int i = w + 8 * j;
+        const int row = 8 * (j < 2 ? i : (j < 4 ? i - 16 : i - 32)) + r8;
         voff[j] = (unsigned)row * (PDC * 2) + (unsigned)((s8 ^ pswz(row)) << 4);
     }
     auto issue = [&](int c) {
         MLA_LDS unsigned char* st = lds + (c & 1) * kDStage;
         const unsigned col = c < PDC / 64 ? (unsigned)c * 128u : 0x80000000u;
 #pragma unroll
-        for (int j = 0; j < 12; ++j) {
-            const __amdgpu_buffer_rsrc_t r = j < 4 ? wk_r : (j < 8 ? wv_r : x_r);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MLA_LDS void*)(st + (w + 4 * j) * 1024), 16,
+        for (int j = 0; j < 8; ++j) {
+            const __amdgpu_buffer_rsrc_t r = j < 2 ? wk_r : (j < 4 ? wv_r : x_r);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MLA_LDS void*)(st + (w + 8 * j) * 1024), 16,
                                                      voff[j] + col, 0, 0, 0);
         }
     };
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(256, 1) void prefill_decompress_kernel(
     for (int c = 0; c < PDC / 64; ++c) {
         p_stage_barrier();                           // everyone is done with chunk c - 1's stage
         issue(c + 1);
-        p_wait_vmem<12>();                           // this wave's copies of chunk c landed
+        p_wait_vmem<8>();                            // this wave's copies of chunk c landed
         p_stage_barrier();                           // ... and everyone's
         const MLA_LDS unsigned char* st = lds + (c & 1) * kDStage;
 #pragma unroll
@@ -230,12 +234,12 @@ __global__ __launch_bounds__(256, 1) void prefill_decompress_kernel(
             bf16x8 wf[2], xf[4];
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob) {
-                const int row = 64 * w + 32 * ob + l32;
+                const int row = 64 * wo + 32 * ob + l32;
                 wf[ob] = *reinterpret_cast<const MLA_LDS bf16x8*>(st + (8 * row + (cx ^ pswz(row))) * 16);
             }
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const int row = 32 * tb + l32;
+                const int row = 128 * wt + 32 * tb + l32;
                 xf[tb] = *reinterpret_cast<const MLA_LDS bf16x8*>(st + kDWBytes + (8 * row + (cx ^ pswz(row))) * 16);
             }
 #pragma unroll
@@ -247,14 +251,14 @@ __global__ __launch_bounds__(256, 1) void prefill_decompress_kernel(
     p_wait_vmem<0>();                                // the record-less copies of chunk 8 too
     __syncthreads();                                 // stages free for the store staging
 
-    // acc[ob][tb][i]: output 64 w + 32 ob + 8 (i/4) + 4 hf + i%4 of token
-    // 32 tb + l32.  Staged per wave as [token][64 outputs] bf16 (rows of 144
-    // bytes), then stored as 128-byte row pieces.
-    MLA_LDS unsigned char* ost = lds + w * (kDTok * kDOutStride);
+    // acc[ob][tb][i]: output 64 wo + 32 ob + 8 (i/4) + 4 hf + i%4 of token
+    // 128 wt + 32 tb + l32.  Staged per wave as [token][64 outputs] bf16 (rows
+    // of 144 bytes), then stored as 128-byte row pieces.
+    MLA_LDS unsigned char* ost = lds + w * (128 * kDOutStride);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
         const int tok = 32 * tb + l32;
-        const float sc = ts != nullptr ? ts[(size_t)b * Tpad + t0 + tok] : 1.0f;
+        const float sc = ts != nullptr ? ts[(size_t)b * Tpad + t0 + 128 * wt + tok] : 1.0f;
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(256, 1) void prefill_decompress_kernel(
             }
     }
     // LDS operations of one wave complete in order: the reads see the writes
-    unsigned short* dst = (w < 2 ? kc : vv) + (((size_t)b * PH + h) * Tpad + t0) * 128 + (w & 1) * 64;
+    unsigned short* dst = (wo < 2 ? kc : vv) + (((size_t)b * PH + h) * Tpad + t0 + 128 * wt) * 128 + (wo & 1) * 64;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int tok = 8 * k + r8;
@@ -605,7 +609,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
 
 }  // namespace
 
-int prefill_tpad(int max_blocks) { return (max_blocks * PBS + 127) / 128 * 128; }
+int prefill_tpad(int max_blocks) { return (max_blocks * PBS + kDTok - 1) / kDTok * kDTok; }
 
 hipError_t launch_prefill(const PrefillLaunch& a) {
     if (a.batch == 0) return hipSuccess;
@@ -617,7 +621,7 @@ hipError_t launch_prefill(const PrefillLaunch& a) {
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     if (a.stages & 2u) {
-        prefill_decompress_kernel<<<PH * a.batch * (Tpad / kDTok), 256, 0, a.stream>>>(
+        prefill_decompress_kernel<<<PH * a.batch * (Tpad / kDTok), 512, 0, a.stream>>>(
             a.x, a.cache_dtype == MLA_FP8_E4M3 ? a.ts : nullptr, static_cast<const unsigned short*>(a.w_uk),
             static_cast<const unsigned short*>(a.w_uv), a.seq_lens, Tmax, Tpad, a.kc, a.vv);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;

@@ -31,7 +31,7 @@ struct PrefillLaunch {
     hipStream_t stream;
 };
 
-// Workspace rows per sequence: max_blocks * 64 rounded up to 128.
+// Workspace rows per sequence: max_blocks * 64 rounded up to 256 (the rebuild tile).
 int prefill_tpad(int max_blocks);
 hipError_t launch_prefill(const PrefillLaunch& a);
 
