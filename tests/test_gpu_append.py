@@ -176,3 +176,12 @@ def test_append_portable(act):
     wl = synth.Workload("portable_append", 6, 48, 8, 24, 20, 40, 16, 3, 2, 5, 60, True,
                         "bf16", act, append=True)
     _bf16_append(wl, f"portable append {act}")
+
+
+def test_append_whole_prompt():
+    """4400 new rows at once (two prompts of 2200 tokens after short prefixes):
+    the projection's row passes spread over 46 workgroup rows with no depth
+    split, the path a whole prompt takes."""
+    wl = W["v3_b64_ctx1k8k_paged_bf16"].replace(name="v3_append_prompt", batch=2, ctx_lo=0,
+                                                ctx_hi=100, q_len=2200)
+    _bf16_append(wl, "v3 append of 2 x 2200 tokens")

@@ -184,3 +184,17 @@ def test_query_path_then_decode():
     d_lse = float(np.max(np.abs(lse - ref_lse)))
     print(f"query path + decode: max-abs {max_abs:.3e} rel-L2 {rel:.3e} lse {d_lse:.3e}", flush=True)
     assert max_abs <= 2e-2 and rel <= 5e-3 and d_lse <= 1e-2, (max_abs, rel, d_lse)
+
+
+def test_query_whole_prompt_sampled():
+    """Two 1024-token prompts at once (2048 rows): the projections' row passes
+    spread over 22 workgroup rows with no depth split.  Sampled rows across
+    the passes and both prompts."""
+    wl = V3.replace(batch=2, q_len=1024, ctx_lo=0, ctx_hi=0)
+    announce("query whole prompt", "2 x 1024")
+    qc = QueryCase(wl, synth.Q_LORA_RANK_V3)
+    qn, qp = qc.run()
+    rows = np.array([0, 1, 95, 96, 191, 500, 1023, 1024, 1100, 1919, 2047])
+    rn, rp = qc.oracle(rows)
+    check(qn[rows], rn, "q_nope whole prompt")
+    check(qp[rows], rp, "q_pe whole prompt")
