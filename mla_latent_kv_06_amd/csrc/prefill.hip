@@ -12,8 +12,11 @@
 //                  [b][t][512] and rotary keys KR [b][t][64], bf16; an fp8
 //                  cache gives X the codes' exact values, KR the dequantised
 //                  values rounded to bf16, and its token scales to TS.
-//  2. decompress:  K^C[b][h][t][:] = W_UK[h] X[b][t],  V[b][h][t][:] = W_UV[h]
-//                  X[b][t] (times the token scale), bf16, on MFMA.
+//  2. decompress:  K^C[b][h][t][:] = W_UK[h] X[b][t] and V^T[b][h][:][t] =
+//                  W_UV[h] X[b][t] (times the token scale), bf16, on MFMA;
+//                  V^T rows hold each 16-key group in the order the
+//                  attention's softmax weights take (keys 0-3, 8-11, 4-7,
+//                  12-15).
 //  3. attention:   causal softmax attention of each head's queries [q^C ; q^R]
 //                  over its keys [K^C ; KR] and values V, MFMA with an online
 //                  softmax; query s of a sequence of L tokens and q_len queries
@@ -24,6 +27,8 @@
 // sequence's length are skipped by every kernel; the gather zeroes the rows
 // between the length and the next multiple of 256, which the decompression
 // reads.
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -221,40 +226,88 @@ __global__ __launch_bounds__(512, 1) void prefill_decompress_kernel(
     for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) acc[ob][tb] = f32x16{};
-    issue(0);
-    for (int c = 0; c < PDC / 64; ++c) {
-        p_stage_barrier();                           // everyone is done with chunk c - 1's stage
-        issue(c + 1);
-        p_wait_vmem<8>();                            // this wave's copies of chunk c landed
-        p_stage_barrier();                           // ... and everyone's
-        const MLA_LDS unsigned char* st = lds + (c & 1) * kDStage;
+    // The K loop, compiled once per wave role: key waves put outputs on the
+    // MFMA rows (K^C^T, stored per token), value waves put tokens on them
+    // (V^T, stored per channel).  Both copies pass the same barriers.
+    auto kloop = [&](auto value_waves) __attribute__((always_inline)) {
+        constexpr bool VT = decltype(value_waves)::value;
+        issue(0);
+        for (int c = 0; c < PDC / 64; ++c) {
+            p_stage_barrier();                       // everyone is done with chunk c - 1's stage
+            issue(c + 1);
+            p_wait_vmem<8>();                        // this wave's copies of chunk c landed
+            p_stage_barrier();                       // ... and everyone's
+            const MLA_LDS unsigned char* st = lds + (c & 1) * kDStage;
 #pragma unroll
-        for (int sx = 0; sx < 4; ++sx) {
-            const int cx = 2 * sx + hf;              // 16-byte slot of K-step sx
-            bf16x8 wf[2], xf[4];
+            for (int sx = 0; sx < 4; ++sx) {
+                const int cx = 2 * sx + hf;          // 16-byte slot of K-step sx
+                bf16x8 wf[2], xf[4];
 #pragma unroll
-            for (int ob = 0; ob < 2; ++ob) {
-                const int row = 64 * wo + 32 * ob + l32;
-                wf[ob] = *reinterpret_cast<const MLA_LDS bf16x8*>(st + (8 * row + (cx ^ pswz(row))) * 16);
+                for (int ob = 0; ob < 2; ++ob) {
+                    const int row = 64 * wo + 32 * ob + l32;
+                    wf[ob] = *reinterpret_cast<const MLA_LDS bf16x8*>(st + (8 * row + (cx ^ pswz(row))) * 16);
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const int row = 128 * wt + 32 * tb + l32;
+                    xf[tb] = *reinterpret_cast<const MLA_LDS bf16x8*>(st + kDWBytes + (8 * row + (cx ^ pswz(row))) * 16);
+                }
+#pragma unroll
+                for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb)
+                        acc[ob][tb] = VT ? pf_mfma(xf[tb], wf[ob], acc[ob][tb]) : pf_mfma(wf[ob], xf[tb], acc[ob][tb]);
             }
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const int row = 128 * wt + 32 * tb + l32;
-                xf[tb] = *reinterpret_cast<const MLA_LDS bf16x8*>(st + kDWBytes + (8 * row + (cx ^ pswz(row))) * 16);
-            }
-#pragma unroll
-            for (int ob = 0; ob < 2; ++ob)
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) acc[ob][tb] = pf_mfma(wf[ob], xf[tb], acc[ob][tb]);
         }
-    }
+    };
+    if (wo < 2)
+        kloop(std::integral_constant<bool, false>{});
+    else
+        kloop(std::integral_constant<bool, true>{});
     p_wait_vmem<0>();                                // the record-less copies of chunk 8 too
     __syncthreads();                                 // stages free for the store staging
 
-    // acc[ob][tb][i]: output 64 wo + 32 ob + 8 (i/4) + 4 hf + i%4 of token
-    // 128 wt + 32 tb + l32.  Staged per wave as [token][64 outputs] bf16 (rows
-    // of 144 bytes), then stored as 128-byte row pieces.
     MLA_LDS unsigned char* ost = lds + w * (128 * kDOutStride);
+    if (wo >= 2) {
+        // acc[ob][tb][i]: channel 64 (wo - 2) + 32 ob + l32 of token 128 wt +
+        // 32 tb + 8 (i/4) + 4 hf + i%4.  V^T rows: keys of each 16-key group
+        // in the order 0-3, 8-11, 4-7, 12-15 (position = key with bits 2 and 3
+        // swapped), the order in which a lane half holds the softmax weights
+        // of one MFMA K-step; the lane's 4 consecutive tokens stay 4
+        // consecutive positions.  Staged as [64 channels][128 tokens] bf16
+        // (rows of 272 bytes), stored as 256-byte row pieces.
+        constexpr int VST = 272;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int tok = 32 * tb + 8 * g + 4 * hf;                    // first of 4
+                const int pos = (tok & ~12) | ((tok & 4) << 1) | ((tok & 8) >> 1);
+                float sc[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sc[e] = ts != nullptr ? ts[(size_t)b * Tpad + t0 + 128 * wt + tok + e] : 1.0f;
+#pragma unroll
+                for (int ob = 0; ob < 2; ++ob) {
+                    u16x4 hv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) hv[e] = f32_to_bf16_bits(acc[ob][tb][4 * g + e] * sc[e]);
+                    *reinterpret_cast<MLA_LDS u16x4*>(ost + (32 * ob + l32) * VST + pos * 2) = hv;
+                }
+            }
+        }
+        unsigned short* dst = vv + (((size_t)b * PH + h) * 128 + 64 * (wo - 2)) * Tpad + t0 + 128 * wt;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int ch = 4 * k + (lane >> 4), seg = lane & 15;
+            const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(ost + ch * VST + seg * 16);
+            *reinterpret_cast<u32x4*>(dst + (size_t)ch * Tpad + seg * 8) = v;
+        }
+        return;
+    }
+    // key waves.  acc[ob][tb][i]: output 64 wo + 32 ob + 8 (i/4) + 4 hf + i%4
+    // of token 128 wt + 32 tb + l32.  Staged per wave as [token][64 outputs]
+    // bf16 (rows of 144 bytes), then stored as 128-byte row pieces.
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
         const int tok = 32 * tb + l32;
@@ -270,7 +323,7 @@ __global__ __launch_bounds__(512, 1) void prefill_decompress_kernel(
             }
     }
     // LDS operations of one wave complete in order: the reads see the writes
-    unsigned short* dst = (wo < 2 ? kc : vv) + (((size_t)b * PH + h) * Tpad + t0 + 128 * wt) * 128 + (wo & 1) * 64;
+    unsigned short* dst = kc + (((size_t)b * PH + h) * Tpad + t0 + 128 * wt) * 128 + wo * 64;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int tok = 8 * k + r8;
@@ -289,22 +342,21 @@ __global__ __launch_bounds__(512, 1) void prefill_decompress_kernel(
 // they stream the same key and value tiles at about the same time, and the
 // XCD's L2 serves all but the first read.
 //
-// Workgroup (b, h, qblk): queries s = 256 qblk .. +256 of sequence b, head h;
-// wave w owns 64 of them as two blocks of 32 (query block qb: queries
-// 256 qblk + 64 w + 32 qb + l32).  Key tiles of 64 tokens are copied HBM ->
-// LDS three stages deep (two in flight while one is used): the 24 KB key tile
-// [K^C | KR] (24 chunks per row: 16 of K^C, 8 of KR) and the 16 KB value tile
-// in the XOR layout, chunk c of row t at 16-byte position
-//   (c / 8) * 512 + 8 t + (c % 8 ^ g(t)),
-// 40 copy instructions per tile (10 per wave), instruction i writing LDS bytes
-// 1024 i .. +1024 of the stage (key groups 0-2, then value groups 0-1).
+// Workgroup (b, h, qblk): queries s = 256 qblk .. +256 of sequence b, head h,
+// on 8 waves of 32 queries (two waves per SIMD): wave w owns queries 256 qblk
+// + 32 w + l32.  Key tiles of 64 tokens are copied HBM -> LDS three stages
+// deep (two in flight while one is used): the 24 KB key tile [K^C | KR] (24
+// chunks per token row: 16 of K^C, 8 of KR), chunk c of row t at 16-byte
+// position (c / 8) * 512 + 8 t + (c % 8 ^ g(t)), and the 16 KB value tile,
+// 128 channel rows of V^T (the tile's 64 keys, 8 chunks), chunk c of row r
+// at 8 r + (c ^ g(r)); 40 copy instructions per tile (5 per wave),
+// instruction i writing LDS bytes 1024 i .. +1024 of the stage.
 //
-// Per half tile (32 keys), per query block:
-//   S^T (32 keys x 32 queries) = K . Q^T      12 MFMA, K from LDS, Q in VGPRs
-//   O^T (128 x 32)            += V^T . P^T     8 MFMA, V^T by transposed reads
-// so a lane holds 16 scores of one query and the query's softmax statistics
-// need one cross-lane exchange (lanes l and l + 32).  Each LDS fragment feeds
-// the MFMAs of both query blocks.
+// Per tile (64 keys), per wave:
+//   S^T (64 keys x 32 queries) = K . Q^T      24 MFMA, K from LDS, Q in VGPRs
+//   O^T (128 x 32)            += V^T . P^T    16 MFMA, V^T from LDS
+// so a lane holds 32 scores of one query and the query's softmax statistics
+// need one cross-lane exchange (lanes l and l + 32).
 //
 // Softmax: weights exp2(s * log2(e) * scale - m) with a per-query reference
 // m that is raised only when a score exceeds it by more than kLazy (weights
@@ -322,7 +374,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
     const unsigned short* __restrict__ q_nope,   // [batch * q_len][H][128]
     const unsigned short* __restrict__ q_pe,     // [batch * q_len][H][64]
     const unsigned short* __restrict__ kc,       // [batch][H][Tpad][128]
-    const unsigned short* __restrict__ vv,       // [batch][H][Tpad][128]
+    const unsigned short* __restrict__ vv,       // [batch][H][128][Tpad]: V^T, keys permuted
     const unsigned short* __restrict__ kr,       // [batch * Tpad][64]
     const int* __restrict__ seq_lens, int Tmax, int Tpad, int q_len, int nqb, float scale_log2,
     unsigned short* __restrict__ out,            // [batch * q_len][H][128]
@@ -354,19 +406,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
     const __amdgpu_buffer_rsrc_t kc_r = p_rsrc(kc + kv_base, (unsigned)Tpad * 256u);
     const __amdgpu_buffer_rsrc_t vv_r = p_rsrc(vv + kv_base, (unsigned)Tpad * 256u);
     const __amdgpu_buffer_rsrc_t kr_r = p_rsrc(kr + (size_t)b * Tpad * PDR, (unsigned)Tpad * 128u);
-    // instruction i = w + NW j: i < 16 K^C (groups 0-1), i < 24 KR (group 2),
-    // else V (groups 0-1); row 8 (i % 8) + r8 of the tile.  Which tensor is
-    // fixed per j.
+    // instruction i = w + NW j: i < 16 K^C (groups 0-1; token row 8 (i % 8)
+    // + r8), i < 24 KR (group 2), else V^T (channel row 8 (i - 24) + r8, the
+    // tile's 64 keys = 128 bytes of it).  Which tensor is fixed per j.
     constexpr int JKC = 16 / NW, JKR = 24 / NW;
     unsigned voff[NCP];
 #pragma unroll
     for (int j = 0; j < NCP; ++j) {
         const int i = w + NW * j;
-        const int ii = j < JKC ? i : (j < JKR ? i - 16 : i - 24);
-        const int row = 8 * (ii & 7) + r8;
-        const bool wide = j < JKC || j >= JKR;
-        const int chunk = (wide ? 8 * (ii >> 3) : 0) + (s8 ^ pswz(row));
-        voff[j] = (unsigned)row * (wide ? 256u : 128u) + (unsigned)chunk * 16u;
+        if (j < JKR) {
+            const int ii = j < JKC ? i : i - 16;
+            const int row = 8 * (ii & 7) + r8;
+            const int chunk = (j < JKC ? 8 * (ii >> 3) : 0) + (s8 ^ pswz(row));
+            voff[j] = (unsigned)row * (j < JKC ? 256u : 128u) + (unsigned)chunk * 16u;
+        } else {
+            const int row = 8 * (i - 24) + r8;
+            voff[j] = (unsigned)row * (unsigned)Tpad * 2u + (unsigned)((s8 ^ pswz(row)) << 4);
+        }
     }
     auto issue = [&](int t) {
         MLA_LDS unsigned char* st = lds + (t % kPStages) * kPStage;
@@ -375,7 +431,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
         for (int j = 0; j < NCP; ++j) {
             const bool is_kr = j >= JKC && j < JKR;
             const __amdgpu_buffer_rsrc_t r = j < JKC ? kc_r : (is_kr ? kr_r : vv_r);
-            const unsigned off = live ? voff[j] + (unsigned)t * (is_kr ? 8192u : 16384u) : 0x80000000u;
+            const unsigned step = j < JKC ? 16384u : (is_kr ? 8192u : 128u);   // bytes per tile
+            const unsigned off = live ? voff[j] + (unsigned)t * step : 0x80000000u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MLA_LDS void*)(st + (w + NW * j) * 1024), 16, off,
                                                      0, 0, 0);
         }
@@ -404,23 +461,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
         }
     }
 
-    // per-lane LDS offsets: score operand (chunk 2 ks + hf of row 32 hb + l32)
-    // by ks % 4; transposed value reads (lane 4 r + c of a 16-lane group reads
-    // row 4 hf + r (+ 8), channels 4 c .. +4 of a 16-channel block) by the
-    // block's parity within its 32 channels and by the + 8 row offset
-    int qk_off[4], tr_off[2][2];
+    // per-lane LDS offsets of the 16-byte operand reads: chunk 2 j + hf of
+    // row l32 (plus a multiple of 32 rows), for the keys (j = K-step % 4) and
+    // the value rows (j = the value K-step 2 hb + k2)
+    int qk_off[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) qk_off[j] = (l32 * 8 + ((2 * j + hf) ^ pswz(l32 & 15))) * 16;
-    {
-        const int r = (lane & 15) >> 2, g1 = (lane >> 4) & 1, b1 = (lane >> 1) & 1;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int t = 8 * e + 4 * hf + r;
-                tr_off[j][e] = (t * 8 + ((4 * j + 2 * g1 + b1) ^ pswz(t))) * 16 + (lane & 1) * 8;
-            }
-    }
 
     f32x16 o[QB][4];
 #pragma unroll
@@ -537,21 +583,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(
             l_run[qb] += ps;
         }
     };
-    // O^T += V^T . P^T over the tile's 64 keys.  K-step (hb, k2) covers keys
-    // 32 hb + 16 k2 + {0..3, 8..11} (lanes 0-31) and {4..7, 12..15} (lanes
-    // 32-63), matching P's layout; consecutive MFMAs update different
-    // accumulators.
+    // O^T += V^T . P^T over the tile's 64 keys.  K-step kk = 2 hb + k2 covers
+    // keys 32 hb + 16 k2 + {0..3, 8..11} (lanes 0-31) and {4..7, 12..15}
+    // (lanes 32-63), matching P's layout; the V^T tile stores each 16-key
+    // group in that order, so a lane's 8 keys are one 16-byte chunk (2 kk +
+    // hf) of its channel row.  Consecutive MFMAs update different accumulators.
     auto values = [&](const MLA_LDS unsigned char* vt, const bf16x8 (&pf)[2][QB][2]) __attribute__((always_inline)) {
-        const MLA_LDS unsigned char* vb[2][2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) vb[j][e] = vt + tr_off[j][e];
         auto va = [&](int kk, int cm) {
-            const int c = (cm >> 1) * 8192 + kk * 16 * 128;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb[cm & 1][0] + c));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb[cm & 1][1] + c));
-            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            return *reinterpret_cast<const MLA_LDS bf16x8*>(vt + qk_off[kk] + cm * 32 * 128);
         };
         bf16x8 v0 = va(0, 0), v1;
 #pragma unroll
