@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--layers NL] [--splits S] [--no-cpu-baseline] [--cpu-tokens N]
-                    [--report FILE]
+                    [--fp8-scores] [--query-path] [--report FILE]
+    python bench.py --prefill v3_prefill_b2_8k_bf16 [--steps K] [--warmup W]
 
 One step = the whole hot path for one layer over one batch: the cache append
 of the new tokens (wkv_a projection, RMSNorm, RoPE, paged write; workloads
@@ -15,6 +16,11 @@ timing starts.  Prints ONE JSON line on stdout; details go to stderr.
 Default workload: DeepSeek-V3 head shape (128 heads, latent 512, rotary 64),
 bf16, batch 64, every sequence 8192 tokens after the append, paged blocks of 64
 with a randomly permuted block table.
+
+--prefill WORKLOAD times the prefill instead: one step = mla_prefill over every
+prompt token of the batch for one layer (gather, K/V rebuild, causal
+attention); its JSON line reports prompt tokens/s and the attention kernel
+against the bf16 MFMA peak.
 """
 
 from __future__ import annotations
