@@ -162,8 +162,8 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(
 // 2. decompression
 // ---------------------------------------------------------------------------
 
-// grid: H * batch * Tpad / 256 workgroups of 512 (head fastest: the 16 heads
-// an XCD receives keep their weights, 4 MB, in its L2).  Workgroup (h, b,
+// grid: H * (batch * Tpad / 256, rounded up to a multiple of 4) workgroups
+// of 512.  Workgroup (h, b,
 // tile) computes, for tokens t0 .. t0 + 256 of sequence b, the 256 outputs
 // [W_UK[h] ; W_UV[h]] X^T: wave w owns outputs 64 (w % 4) .. +64 (waves with
 // w % 4 < 2 the keys, the others the values) for tokens 128 (w / 4) .. +128.
@@ -183,14 +183,21 @@ constexpr int kDLds = 8 * 128 * kDOutStride > 2 * kDStage ? 8 * 128 * kDOutStrid
 __global__ __launch_bounds__(512, 1) void prefill_decompress_kernel(
     const unsigned short* __restrict__ x, const float* __restrict__ ts,
     const unsigned short* __restrict__ w_uk, const unsigned short* __restrict__ w_uv,
-    const int* __restrict__ seq_lens, int Tmax, int Tpad,
+    const int* __restrict__ seq_lens, int n_seq, int Tmax, int Tpad,
     unsigned short* __restrict__ kc, unsigned short* __restrict__ vv) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kDLds];
     MLA_LDS unsigned char* lds = (MLA_LDS unsigned char*)smem;
-    const int h = blockIdx.x % PH;
-    const int tile = blockIdx.x / PH;
+    // XCD = id % 8.  Each XCD's 32 concurrent workgroups cover 8 of its 16
+    // heads x 4 consecutive token tiles (2 MB of weights + 1 MB of latents in
+    // its L2): id / 8 = 32 g + 8 tl + hl, head = xcd + 8 hl + 64 (g % 2),
+    // tile = 4 (g / 2) + tl.  The grid rounds the tiles up to a multiple of 4.
+    const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
+    const int g = jj >> 5, tl = (jj >> 3) & 3, hl = jj & 7;
+    const int h = xcd + 8 * hl + 64 * (g & 1);
+    const int tile = 4 * (g >> 1) + tl;
     const int ntt = Tpad / kDTok;
     const int b = tile / ntt, t0 = (tile - b * ntt) * kDTok;
+    if (b >= n_seq) return;                          // rounding of the grid
     const int len = seq_len_of(seq_lens, b, Tmax);
     if (t0 >= len) return;                           // uniform
     const int lane = threadIdx.x & 63;
@@ -660,9 +667,10 @@ hipError_t launch_prefill(const PrefillLaunch& a) {
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     if (a.stages & 2u) {
-        prefill_decompress_kernel<<<PH * a.batch * (Tpad / kDTok), 512, 0, a.stream>>>(
+        const int n_tiles = a.batch * (Tpad / kDTok);
+        prefill_decompress_kernel<<<PH * ((n_tiles + 3) / 4 * 4), 512, 0, a.stream>>>(
             a.x, a.cache_dtype == MLA_FP8_E4M3 ? a.ts : nullptr, static_cast<const unsigned short*>(a.w_uk),
-            static_cast<const unsigned short*>(a.w_uv), a.seq_lens, Tmax, Tpad, a.kc, a.vv);
+            static_cast<const unsigned short*>(a.w_uv), a.seq_lens, a.batch, Tmax, Tpad, a.kc, a.vv);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     if (a.stages & 4u) {
