@@ -222,7 +222,12 @@ hipError_t launch_append(const AppendLaunch& a, bool mfma_gemm) {
     const int T = a.batch * a.n_new;
     if (T == 0) return hipSuccess;
     const int Dout = a.DC + a.DR;
-    if (mfma_gemm && a.stream_gemm) {
+    if (mfma_gemm && a.stream_gemm && a.kc == 1 && T >= kQueryTileRows && Dout % 4 == 0) {
+        // a whole prompt: the 256 x 256 tile form, fp32 rows straight into the one slice
+        query_gemm_tiles<true><<<dim3((Dout + kBOut - 1) / kBOut, (T + kBRows - 1) / kBRows), 512, 0, a.stream>>>(
+            static_cast<const unsigned short*>(a.h), T, a.d_model, static_cast<const unsigned short*>(a.w_kv_a),
+            nullptr, Dout, 2, 1, nullptr, 1.0f, nullptr, nullptr, 0, a.part);
+    } else if (mfma_gemm && a.stream_gemm) {
         const int n_ob = (Dout / 32 + kQWaves - 1) / kQWaves;
         const dim3 grid(n_ob * a.kc, stream_gemm_row_groups(T));
         stream_gemm_mfma<true><<<grid, kQWaves * kWave, 0, a.stream>>>(
