@@ -189,6 +189,9 @@ def test_prefill_workspace_sizes(b):
     want = al(rows * 1024) + al(rows * 128) + al(rows * 4) + 2 * al(rows * 128 * 256)
     assert b.prefill_workspace_size(d, 2, 100, 3) == want
     assert b.prefill_workspace_size(d, 2, 100, 4) == want       # 256 tokens: no padding
+    rows = 2 * 512                                               # 5 blocks = 320 tokens -> 512
+    want5 = al(rows * 1024) + al(rows * 128) + al(rows * 4) + 2 * al(rows * 128 * 256)
+    assert b.prefill_workspace_size(d, 2, 100, 5) == want5
     assert b.prefill_workspace_size(d, 0, 1, 1) == 0
 
 
