@@ -96,22 +96,11 @@ typedef struct {
     int32_t cache_dtype;   /* mla_dtype of the cache pool                    */
     int32_t act_dtype;     /* mla_dtype of q, weights, h, gamma and out      */
     float softmax_scale;   /* 0 => 1/sqrt(qk_nope_dim + qk_rope_dim)         */
-    int32_t flags;         /* MLA_FLAG_* bits; 0 for the defaults           */
+    int32_t flags;         /* reserved: must be 0                            */
 } mla_dims;
 
-/* Options in mla_dims.flags.
- *
- * MLA_FLAG_FP8_SCORES (decode, MFMA path, FP8_E4M3 cache only; any other
- * combination returns MLA_ERR_UNSUPPORTED): the score product q . c runs on
- * the fp8 matrix cores.  The cache codes enter as stored and the token scale
- * is applied to the product; each absorbed query vector [q_lat ; q^R] (576
- * values of one query row and head) is rounded to e4m3 (nearest, ties to
- * even) after division by one power of two 2^e, the smallest with
- * amax |q| <= 448 * 2^e, i.e. up to 2^-4 relative error per query element.
- * The value product stays bf16.  This trades accuracy for speed: with the
- * default the scores use bf16 queries against the codes' exact values, with
- * the token scale applied in fp32.  The append ignores flags. */
-enum { MLA_FLAG_FP8_SCORES = 1 };
+/* mla_dims.flags is reserved: no flag is defined and every call that takes
+ * dims returns MLA_ERR_UNSUPPORTED when it is not 0. */
 
 /* Status name, e.g. "MLA_ERR_BAD_SHAPE". Never NULL. */
 const char* mla_status_string(mla_status status);

@@ -10,7 +10,6 @@ Importing this module loads ``libmla.so`` and raises if it has not been built
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch  # loads the HIP runtime the library binds to
@@ -29,7 +28,6 @@ STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_BAD_SHAPE",
                 5: "MLA_ERR_WORKSPACE_TOO_SMALL", 6: "MLA_ERR_HIP"}
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 STAGE_ABSORB_Q, STAGE_SPLIT_KV, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
-FLAG_FP8_SCORES = 1          # mla_dims.flags: fp8 score product (fp8 cache, MFMA shape)
 PREFILL_GATHER, PREFILL_DECOMPRESS, PREFILL_ATTEND, PREFILL_ALL = 1, 2, 4, 7
 
 DTYPE_CODES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
@@ -313,9 +311,6 @@ def append(dims: Dims, h, w_kv_a, kv_norm_gamma, block_table, start_pos, cache_p
         workspace.numel(), _stream(dev))
     _check(st, "mla_cache_append")
 
-
-def softmax_scale(dims: Dims) -> float:
-    return dims.softmax_scale or 1.0 / math.sqrt(dims.qk_nope_dim + dims.qk_rope_dim)
 
 
 def query_project(dims: Dims, h, w_dq, q_norm_gamma, w_uq, w_qr, start_pos,

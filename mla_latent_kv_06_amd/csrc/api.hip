@@ -61,8 +61,8 @@ mla_status check_dims(const mla_dims* d) {
         return fail(MLA_ERR_UNSUPPORTED, "act_dtype=%d must be MLA_F32 or MLA_BF16", d->act_dtype);
     if (!(d->softmax_scale >= 0.f) || std::isinf(d->softmax_scale))
         return fail(MLA_ERR_BAD_SHAPE, "softmax_scale must be finite and >= 0");
-    if (d->flags & ~MLA_FLAG_FP8_SCORES)
-        return fail(MLA_ERR_UNSUPPORTED, "flags=0x%x: unknown bits", (unsigned)d->flags);
+    if (d->flags != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "flags=0x%x: no flags are defined; pass 0", (unsigned)d->flags);
     return MLA_OK;
 }
 
@@ -144,8 +144,6 @@ mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const
         return fail(MLA_ERR_BAD_SHAPE, "num_splits=%d outside [0, %d]", num_splits, mla::kMaxSplits);
     if (stages == 0 || (stages & ~(unsigned)MLA_STAGE_ALL))
         return fail(MLA_ERR_BAD_SHAPE, "stages=0x%x: use MLA_STAGE_* bits", stages);
-    if ((d.flags & MLA_FLAG_FP8_SCORES) && !(mla::is_v3_shape(d) && d.cache_dtype == MLA_FP8_E4M3))
-        return fail(MLA_ERR_UNSUPPORTED, "MLA_FLAG_FP8_SCORES needs the MFMA shape with an FP8_E4M3 cache");
     if (batch == 0) return ok();
     if (max_blocks_per_seq < 1) return fail(MLA_ERR_BAD_SHAPE, "max_blocks_per_seq must be >= 1");
     // 0: balanced scheduling on the MFMA path, the default split count otherwise
@@ -182,7 +180,6 @@ mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const
     a.BS = d.block_size;
     a.cache_dtype = d.cache_dtype;
     a.act_dtype = d.act_dtype;
-    a.fp8_scores = (d.flags & MLA_FLAG_FP8_SCORES) != 0;
     a.scale = resolved_scale(d);
     a.batch = batch;
     a.q_len = q_len;
@@ -261,8 +258,6 @@ mla_status check_prefill_shape(const mla_dims* dims, int32_t batch, int32_t q_le
     if (!mla::is_v3_shape(d))
         return fail(MLA_ERR_UNSUPPORTED, "the prefill serves the DeepSeek-V3 head shape "
                                          "(128 heads, 512 + 64, 128 / 128, blocks of 64, bf16 activations)");
-    if (d.flags & MLA_FLAG_FP8_SCORES)
-        return fail(MLA_ERR_UNSUPPORTED, "MLA_FLAG_FP8_SCORES applies to the decode only");
     if (batch < 0 || q_len < 1 || q_len > (1 << 20))
         return fail(MLA_ERR_BAD_SHAPE, "batch=%d must be >= 0 and q_len=%d in [1, 2^20]", batch, q_len);
     if (max_blocks_per_seq < 1 || max_blocks_per_seq > (1 << 16))

@@ -46,6 +46,21 @@ __device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(unsigned short, h);
 }
 
+// Two floats -> packed bf16 pair (round to nearest even), low half first.
+__device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
+    const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(unsigned int, v);
+}
+
+// max(a, b, c) in one instruction.  (fmaxf on matrix-core results first
+// quiets each input in IEEE mode, one extra instruction per value; the
+// callers pass scores that are never NaN: masked ones are -inf.)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // OCP e4m3 code -> float (bias 7, subnormals, 0x7F / 0xFF NaN).
 __device__ __forceinline__ float e4m3_to_f32(unsigned int code) {
     const unsigned int mag = code & 0x7Fu;

@@ -21,6 +21,8 @@
 // All contractions accumulate in fp32; q_lat and the softmax weights P enter
 // the MFMA as bf16, o_lat enters the W_UV product as a bf16 hi + lo pair.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -68,6 +70,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ void wait_vmem_all() {
     // s_waitcnt vmcnt(0), leaving expcnt / lgkmcnt unconstrained
     __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1 in order: a loop
+// whose index is a compile-time constant in every copy of the body.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -245,66 +257,6 @@ __device__ __forceinline__ void issue_tile_fp8(const unsigned char* __restrict__
     }
 }
 
-// fp8 scores: the staging tile keeps rows 37 chunks (592 bytes) apart, so the
-// score operand reads of 16 consecutive rows (one 16-byte chunk each, row
-// stride 148 dwords) fall on distinct banks.  Position p = 64 i + lane of copy
-// instruction i holds chunk p % 37 of row p / 37; the 37th chunk of a row is
-// padding (it repeats chunk 35).  37 instructions, spread over the 4 waves;
-// the 64 scales follow the codes.
-constexpr int F8ROW = 37;                       // 16-byte chunks per padded staging row
-constexpr int F8SCODES = BS * F8ROW * 16;       // 37888 bytes
-__device__ __forceinline__ void issue_tile_fp8_padded(const unsigned char* __restrict__ gtile,
-                                                      const float* __restrict__ gscale,
-                                                      lds_u8* lstage, int w, int lane) {
-    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(gtile, F8TILE);
-#pragma unroll 1
-    for (int i = w; i < BS * F8ROW / 64; i += 4) {
-        const int p = i * 64 + lane;
-        const int t = p / F8ROW, c = p - t * F8ROW;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(lstage + i * 1024), 16,
-                                                 t * D + min(c, F8CHUNKS - 1) * 16, 0, 0, 0);
-    }
-    if (w == 0) {
-        const __amdgpu_buffer_rsrc_t srs = make_rsrc(gscale, BS * 4);
-        if (lane < 16)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (MLA_LDS void*)(lstage + F8SCODES), 16,
-                                                     lane * 16, 0, 0, 0);
-    }
-}
-
-// Padded fp8 staging -> bf16 tile of the codes' values, latent channels only
-// (the scores read the codes themselves).  Rows at or beyond `valid` become
-// zeros, and so do their token scales.
-__device__ __forceinline__ void convert_tile_fp8_latent(lds_u8* lstage, lds_u8* ltile, int tid,
-                                                        int valid) {
-    MLA_LDS float* lscale = reinterpret_cast<MLA_LDS float*>(lstage + F8SCODES);
-    if (tid < BS && tid >= valid) lscale[tid] = 0.f;
-#pragma unroll 1
-    for (int k = 0; k < 8; ++k) {
-        const int p = k * 256 + tid;                   // 64 rows x 32 latent chunks
-        const int t = p >> 5, c = p & 31;
-        u32x4 outw[2];
-        if (t < valid) {
-            const u32x4 raw = *reinterpret_cast<const MLA_LDS u32x4*>(lstage + (t * F8ROW + c) * 16);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                // codes 4q, 4q+1 and 4q+2, 4q+3 as bf16 pairs (exact: unit scale)
-                const unsigned int p0 = __builtin_bit_cast(
-                    unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, false));
-                const unsigned int p1 = __builtin_bit_cast(
-                    unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[q], 1.0f, true));
-                outw[q >> 1][(q & 1) * 2 + 0] = p0;
-                outw[q >> 1][(q & 1) * 2 + 1] = p1;
-            }
-        } else {
-            outw[0] = u32x4{0, 0, 0, 0};
-            outw[1] = u32x4{0, 0, 0, 0};
-        }
-        *reinterpret_cast<MLA_LDS u32x4*>(ltile + tpos(t, 2 * c) * 16) = outw[0];
-        *reinterpret_cast<MLA_LDS u32x4*>(ltile + tpos(t, 2 * c + 1) * 16) = outw[1];
-    }
-}
-
 // fp8 staging -> bf16 swizzled tile of the codes' values.  Every e4m3 value is
 // a bf16 value (3 of 7 mantissa bits, a narrower exponent range), so the copy
 // is exact; the token scale is applied to the scores and the weights instead.
@@ -416,10 +368,7 @@ __device__ __forceinline__ int scan_row_tiles(const int* __restrict__ seq_lens, 
 //   O^T (512 cols x 32 heads) += V^T (512 x 32) . P^T         [32 MFMA]
 // so softmax statistics stay inside the wave.  Q_w stays in VGPRs (its rotary
 // part in LDS on the bf16 path) and O^T in AGPRs for the whole loop.
-// F8S (fp8 cache only): the score product runs on the fp8 matrix cores, with
-// the cache codes as they are and the queries quantised to e4m3 with one scale
-// per (row, head); the value product stays bf16.
-template <bool FP8, bool F8S = false>
+template <bool FP8>
 __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const unsigned short* __restrict__ qbuf,      // [R][H][576] bf16
     const unsigned char* __restrict__ pool,       // [blocks][64][576] bf16 | fp8
@@ -432,10 +381,9 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     // fp8: one bf16 tile + two fp8 staging tiles with scales (rotary queries in VGPRs)
     constexpr bool QPE_LDS = !FP8;
     constexpr int QPE_BYTES = H * DR * 2;
-    static_assert(FP8 || !F8S, "fp8 scores need an fp8 cache");
-    constexpr int STAGE = (F8S ? F8SCODES : F8TILE) + 256;   // fp8 staging buffer: codes + scales
+    constexpr int STAGE = F8TILE + 256;                     // fp8 staging buffer: codes + scales
     constexpr int LDS_BYTES = FP8 ? (TILE + 2 * STAGE) : (2 * TILE + QPE_BYTES);
-    constexpr int NQ = F8S ? 1 : (QPE_LDS ? 32 : 36);   // bf16 query K-steps kept in VGPRs
+    constexpr int NQ = QPE_LDS ? 32 : 36;               // bf16 query K-steps kept in VGPRs
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[LDS_BYTES];
     lds_u8* smem = (lds_u8*)smem_raw;
 
@@ -526,9 +474,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         // asynchronous load of tile t into `dst` (a bf16 tile, or fp8 staging)
         auto issue = [&](int t, lds_u8* dst) {
             const size_t blk = (size_t)btab[t];
-            if constexpr (F8S) {
-                issue_tile_fp8_padded(pool + blk * F8TILE, pool_scale + blk * BS, dst, w, lane);
-            } else if constexpr (FP8) {
+            if constexpr (FP8) {
                 issue_tile_fp8(pool + blk * F8TILE, pool_scale + blk * BS, dst, w, lane);
             } else {
                 issue_tile_bf16(pool + blk * GTILE, dst, w, lane);
@@ -542,61 +488,10 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         // this wave's 32 query rows, as MFMA B fragments: lane (hf, l32) holds
         // channels 16 ks + 8 hf .. +8 of head 32 w + l32
         bf16x8 qf[NQ];
-        if constexpr (!F8S) {
+        {
             const unsigned short* qrow = qbuf + ((size_t)row * H + head) * D + hf * 8;
 #pragma unroll
             for (int ks = 0; ks < NQ; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
-        }
-        // fp8 scores: the fp8 B fragments of K-step s (64 channels) hold channels
-        // 64 s + 32 hf .. +32 of head 32 w + l32, divided by the head's scale
-        // 2^e, the smallest power of two with amax <= 448 * 2^e, and rounded to
-        // nearest even.  The division is exact, so the rounding sees the exact
-        // quotient; |q| / 2^e <= 448 never saturates.
-        [[maybe_unused]] i32x8 qc[F8S ? 9 : 1];
-        [[maybe_unused]] float qscale = 1.f;
-        if constexpr (F8S) {
-            const unsigned short* qrow = qbuf + ((size_t)row * H + head) * D + hf * 32;
-            u32x4 raw[9][4];
-            float amax = 0.f;
-#pragma unroll
-            for (int s8 = 0; s8 < 9; ++s8)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) raw[s8][j] = *reinterpret_cast<const u32x4*>(qrow + 64 * s8 + 8 * j);
-#pragma unroll
-            for (int s8 = 0; s8 < 9; ++s8)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const unsigned u = raw[s8][j][e];
-                        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32((unsigned short)u)),
-                                                 fabsf(bf16_bits_to_f32((unsigned short)(u >> 16)))));
-                    }
-            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-            // amax = f 2^E, 0.5 <= f < 1, and 448 = 0.875 2^9
-            int ex = 0;
-            const float fm = frexpf(amax, &ex);
-            const int qe = amax > 0.f ? (fm <= 0.875f ? ex - 9 : ex - 8) : 0;
-            qscale = ldexpf(1.0f, qe);
-            const float inv = ldexpf(1.0f, -qe);
-#pragma unroll
-            for (int s8 = 0; s8 < 9; ++s8)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    // 8 bf16 -> 8 e4m3 codes (2 dwords)
-                    const u32x4 u = raw[s8][j];
-                    int d0 = 0, d1 = 0;
-                    d0 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_bits_to_f32((unsigned short)u[0]) * inv,
-                                                         bf16_bits_to_f32((unsigned short)(u[0] >> 16)) * inv, d0, false);
-                    d0 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_bits_to_f32((unsigned short)u[1]) * inv,
-                                                         bf16_bits_to_f32((unsigned short)(u[1] >> 16)) * inv, d0, true);
-                    d1 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_bits_to_f32((unsigned short)u[2]) * inv,
-                                                         bf16_bits_to_f32((unsigned short)(u[2] >> 16)) * inv, d1, false);
-                    d1 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_bits_to_f32((unsigned short)u[3]) * inv,
-                                                         bf16_bits_to_f32((unsigned short)(u[3] >> 16)) * inv, d1, true);
-                    qc[s8][2 * j] = d0;
-                    qc[s8][2 * j + 1] = d1;
-                }
         }
         if constexpr (QPE_LDS) {
             // q_pe of all heads: head h's chunk c (8 channels) at h*128 + ((c ^ g(h)) << 4)
@@ -684,7 +579,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                 [[maybe_unused]] float tsc[16];
                 if constexpr (FP8) {
                     const MLA_LDS float* lsc =
-                        reinterpret_cast<const MLA_LDS float*>(stg + (F8S ? F8SCODES : F8TILE));
+                        reinterpret_cast<const MLA_LDS float*>(stg + F8TILE);
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const f32x4 ks4 = *reinterpret_cast<const MLA_LDS f32x4*>(lsc + hb * 32 + 8 * g + 4 * hf);
@@ -692,28 +587,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                         for (int j = 0; j < 4; ++j) tsc[4 * g + j] = ks4[j];
                     }
                 }
-                if constexpr (F8S) {
-                    // codes of rows 32 hb + l32, channels 64 s + 32 hf .. +32: two
-                    // consecutive 16-byte chunks of the padded staging row
-                    const lds_u8* srow = stg + ((hb * 32 + l32) * F8ROW + 2 * hf) * 16;
-                    auto kc = [&](int s8) {
-                        const u32x4 lo = *reinterpret_cast<const MLA_LDS u32x4*>(srow + s8 * 64);
-                        const u32x4 hi = *reinterpret_cast<const MLA_LDS u32x4*>(srow + s8 * 64 + 16);
-                        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                    };
-                    i32x8 a0 = kc(0), a1 = kc(1), a2;
-#pragma unroll
-                    for (int s8 = 0; s8 < 9; ++s8) {
-                        if (s8 + 2 < 9) a2 = kc(s8 + 2);
-                        // e4m3 x e4m3, unit block scales (e8m0 127 = 1.0)
-                        sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qc[s8], sacc, 0, 0, 0, 127, 0, 127);
-                        a0 = a1;
-                        a1 = a2;
-                    }
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) sv[i] = sacc[i] * qscale * tsc[i];
-                } else {
+                {
                     bf16x8 a0 = ka(0), a1 = ka(1), a2;
 #pragma unroll
                     for (int ks = 0; ks < 36; ++ks) {
@@ -807,11 +681,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                 if constexpr (FP8) {
                     lds_u8* st_cur = smem + TILE + cur * STAGE;
                     lds_u8* st_nxt = smem + TILE + (cur ^ 1) * STAGE;
-                    if constexpr (F8S) {
-                        convert_tile_fp8_latent(st_cur, smem, tid, valid_of(t));
-                    } else {
-                        convert_tile_fp8(st_cur, smem, tid, valid_of(t));
-                    }
+                    convert_tile_fp8(st_cur, smem, tid, valid_of(t));
                     __syncthreads();
                     run_tile(t, smem, st_nxt, st_cur, has_next);
                 } else {
@@ -875,6 +745,571 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
             const int hh = (i + rot) & 31;
             const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(ost + hh * OSTR + lane * 8);
             *reinterpret_cast<u32x4*>(po + hh * DC) = v;
+        }
+        if (hf == 0) lse_dst[head] = (m_ref + __builtin_log2f(l_run)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2b. split-KV over a bf16 cache: half-tile ring, software-pipelined
+// ---------------------------------------------------------------------------
+//
+// Same work partition, partial slots and results as split_kv_kernel, for a
+// bf16 cache.  The cache streams through a ring of four 32-row half-tiles
+// (4 x 36 KiB); the last 16 KiB of LDS pass softmax weights between waves.
+//
+// Two products per half-tile, split differently over the four waves:
+//  - scores: wave w owns heads 32w .. 32w+31 (its queries stay in VGPRs):
+//      S^T (32 tokens x 32 heads) = K_half (32 x 576) . Q_w^T      36 MFMA
+//    and forms those heads' softmax weights P;
+//  - values: wave w owns latent columns 128w .. 128w+127 of all 128 heads:
+//      O^T (128 cols x 128 heads) += V^T (128 x 32) . P^T          32 MFMA
+//    with every head block's weights read from LDS.  Each transposed value
+//    fragment then feeds four MFMAs (one per head block): the transposing
+//    LDS reads, which slow down sharply while the copies land in LDS, drop
+//    to a quarter of what the head split needs.
+// Loop iteration h (half h of the piece) runs, per wave:
+//   S_{h+1} (36 MFMA, with the copy of half h+3: 9 instructions)
+//   V_h     (32 MFMA, with the softmax of S_{h+1} threaded between them;
+//            its weights go to LDS for iteration h+1)
+// Every LDS operand is read well ahead of its use (four MFMAs for the score
+// operands): with a shorter lead an LDS-fed 32x32x16 MFMA waits for its
+// operand.  A scheduling barrier after every MFMA slot keeps this order;
+// left alone, the compiler moves each read next to its use and gathers the
+// vector work between the chains.  One barrier per half: half h+1 has landed
+// (each wave waits for its own copies, the barrier for the others'), the
+// weights P_h are in LDS, and every wave is done with half h-1, whose slot
+// the copy of h+3 reuses, and with the weights of h-1, whose buffer P_{h+1}
+// reuses.
+constexpr int HROWS = 32;                 // rows per half-tile
+constexpr int HALF = HROWS * ROWB;        // 36864 bytes
+constexpr int NRING = 4;                  // ring slots
+constexpr int PBUF = 4 * 2 * 1024;        // weights of one half: 4 head blocks x 2 K-steps x 1 KB
+
+// LDS position of chunk c of row t (< 32) in a half-tile slot: the tile
+// layout above with 256 positions per group of 8 chunks.
+__device__ __forceinline__ int hpos(int t, int c) {
+    return ((c >> 3) << 8) + (t << 3) + ((c & 7) ^ fswz(t));
+}
+
+// Copy instruction k (0..8) of wave w for one half-tile: instruction
+// i = 9 w + k = 4 cg + q fills positions 64 i .. 64 i + 63, i.e. rows
+// 8q .. 8q+7 of chunk group cg; lane l takes row 8q + l/8, slot l%8, i.e.
+// chunk 8 cg + ((l%8) ^ g(8q + l/8)), and g(8q + u) = g(u) ^ 2 (q & 1).
+__device__ __forceinline__ void issue_half_part(__amdgpu_buffer_rsrc_t rsrc, lds_u8* slot, int w,
+                                                int lane, int k) {
+    const int i = w * 9 + k, cg = i >> 2, q = i & 3;
+    const unsigned off0 = (lane >> 3) * ROWB + (((lane & 7) ^ fswz(lane >> 3)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(slot + i * 1024), 16,
+                                             (q & 1) ? (off0 ^ 32u) : off0, q * 8 * ROWB + cg * 128,
+                                             0, 0);
+}
+
+// Zero rows valid .. 31 of a half-tile slot (their cache slots hold no token).
+__device__ __forceinline__ void zero_half_rows(lds_u8* slot, int valid, int tid) {
+    for (int p = valid * NCH + tid; p < HROWS * NCH; p += 256) {
+        const int t = p / NCH, c = p - t * NCH;
+        *reinterpret_cast<MLA_LDS u32x4*>(slot + hpos(t, c) * 16) = u32x4{0, 0, 0, 0};
+    }
+}
+
+// Workgroup barrier after this wave's vector memory operations up to the 9
+// (18) most recent have completed, and its LDS operations.  __syncthreads()
+// would wait for every copy in flight (its fence drains the whole vector
+// memory counter).  The asm's memory clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void barrier_landed_but_9() {
+    asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void barrier_landed_but_18() {
+    asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Workgroup barrier after this wave's LDS operations (vector memory copies
+// may stay in flight).
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
+    const unsigned short* __restrict__ qbuf,      // [R][H][576] bf16
+    const unsigned char* __restrict__ pool,       // [blocks][64][576] bf16
+    const int* __restrict__ block_table, int max_blocks,
+    const int* __restrict__ seq_lens, int R, int q_len, int num_splits, float scale_log2,
+    unsigned short* __restrict__ part_o,          // [slots][H][512] fp16
+    float* __restrict__ part_lse) {               // [slots][H]
+    constexpr int P_OFF = NRING * HALF;
+    constexpr int LDS_BYTES = P_OFF + 2 * PBUF;           // 160 KiB
+    constexpr int DIST = 4;                               // score operand lead, in MFMAs
+    constexpr int NS = 36, NV = 32;                       // score / value MFMAs per half
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[LDS_BYTES];
+    lds_u8* smem = (lds_u8*)smem_raw;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in an SGPR
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int head = w * 32 + l32;
+
+    // ---- this workgroup's pieces: as in split_kv_kernel ----------------------------
+    int cur_row = 0, cur_rs = 0, rng_a = 0, rng_b = 0;
+    bool fixed_pending = num_splits > 0;
+    if (num_splits == 0) {
+        MLA_LDS int* sc = reinterpret_cast<MLA_LDS int*>(smem);
+        int excl, mine;
+        const int T = scan_row_tiles(seq_lens, q_len, R, sc, &excl, &mine);
+        const long long G = balanced_groups(gridDim.x, T);
+        if ((long long)blockIdx.x >= G) return;      // uniform: the whole workgroup leaves
+        rng_a = (int)((long long)blockIdx.x * T / G);
+        rng_b = (int)((long long)(blockIdx.x + 1) * T / G);
+        if (rng_a < rng_b && excl <= rng_a && rng_a < excl + mine) {
+            const int per = (R + 255) / 256;
+            int rs = excl;
+            for (int k = 0; k < per; ++k) {
+                const int r = tid * per + k;
+                const int nt = r < R ? row_tiles(seq_lens, q_len, r) : 0;
+                if (rng_a < rs + nt) {
+                    sc[260] = r;
+                    sc[261] = rs;
+                    break;
+                }
+                rs += nt;
+            }
+        }
+        __syncthreads();
+        if (rng_a < rng_b) {
+            cur_row = sc[260];
+            cur_rs = sc[261];
+        }
+        __syncthreads();                 // scratch read before the ring reuses it
+    }
+    auto next_piece = [&](int& row, int& t0, int& t1, int& slot) -> bool {
+        if (num_splits > 0) {
+            if (!fixed_pending) return false;
+            fixed_pending = false;
+            row = blockIdx.x / num_splits;
+            const int split = blockIdx.x - row * num_splits;
+            const int n_tiles = row_tiles(seq_lens, q_len, row);
+            const int tps = (n_tiles + num_splits - 1) / num_splits;
+            t0 = split * tps;
+            t1 = min(n_tiles, t0 + tps);
+            slot = blockIdx.x;
+            if (t0 >= t1) {              // nothing visible in this range
+                if (tid < H) part_lse[(size_t)slot * H + tid] = kNegInf;
+                return false;
+            }
+            return true;
+        }
+        while (cur_rs < rng_b && cur_row < R) {
+            const int r = cur_row, rs = cur_rs;
+            const int nt = row_tiles(seq_lens, q_len, r);
+            cur_row += 1;
+            cur_rs += nt;
+            const int lo = max(rng_a, rs) - rs, hi = min(rng_b, rs + nt) - rs;
+            if (hi > lo) {
+                row = r;
+                t0 = lo;
+                t1 = hi;
+                slot = blockIdx.x + r;
+                return true;
+            }
+        }
+        return false;
+    };
+
+    lds_u8* pbuf = smem + P_OFF;
+    int row, t0, t1, pslot;
+    for (int piece = 0; next_piece(row, t0, t1, pslot); ++piece) {
+        if (piece > 0) __syncthreads();      // the previous piece's epilogue is done with LDS
+        const int b = row / q_len, s = row - b * q_len;
+        const int n_vis = seq_lens[b] - q_len + s + 1;
+        float* lse_dst = part_lse + (size_t)pslot * H;
+        const int* btab = block_table + (size_t)b * max_blocks;
+        // halves hfirst .. hlast of the row hold the piece's visible tokens;
+        // only hlast can be partial
+        const int vis_end = min(n_vis, t1 * BS);
+        const int hfirst = 2 * t0, hlast = (vis_end - 1) / HROWS;
+        auto slot_of = [&](int h) { return smem + ((h - hfirst) & (NRING - 1)) * HALF; };
+        // slot and weight-buffer addresses as wave-uniform values, so that the
+        // copies' LDS addresses (M0) come from scalar arithmetic
+        auto slot_at = [&](int h) __attribute__((always_inline)) {
+            return smem + __builtin_amdgcn_readfirstlane((h - hfirst) & (NRING - 1)) * HALF;
+        };
+        auto pbuf_of = [&](int h) __attribute__((always_inline)) {
+            return pbuf + __builtin_amdgcn_readfirstlane((h - hfirst) & 1) * PBUF;
+        };
+        auto valid_half = [&](int h) { return min(HROWS, vis_end - h * HROWS); };
+        // buffer resource of half h; past the last half, one without records
+        // (its copies read nothing), so that every iteration issues 9 copies
+        auto half_rsrc = [&](int h) {
+            const bool real = h <= hlast;
+            const size_t blk = (size_t)btab[real ? (h >> 1) : (hlast >> 1)];
+            return make_rsrc(pool + blk * GTILE + (h & 1) * HALF, real ? HALF : 0);
+        };
+        auto issue_half = [&](int h) {
+            const __amdgpu_buffer_rsrc_t rs = half_rsrc(h);
+#pragma unroll
+            for (int k = 0; k < 9; ++k) issue_half_part(rs, slot_of(h), w, lane, k);
+        };
+        // A piece's start: the first half's copy, this wave's query rows, then
+        // the next two halves' copies, so that the first scores wait only for
+        // the first two groups of memory operations (vector memory operations
+        // complete in order).
+        issue_half(hfirst);
+        // this wave's 32 query rows, as MFMA B fragments: lane (hf, l32) holds
+        // channels 16 ks + 8 hf .. +8 of head 32 w + l32 (latent 0..31, rotary 32..35)
+        bf16x8 qf[36];
+        {
+            const unsigned short* qrow = qbuf + ((size_t)row * H + head) * D + hf * 8;
+#pragma unroll
+            for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+        }
+        issue_half(hfirst + 1);
+        issue_half(hfirst + 2);
+        bool first_in_flight = true;
+
+        // Per-lane LDS byte offsets.  Score operand (chunk 2 ks + hf of row
+        // l32): by ks % 4.  Transposed value reads (in a 16-lane group, lane
+        // 4r + b reads row 4 hf + r (+8), channels 4b .. 4b+3 of a 16-channel
+        // block): by cm % 2 and by the +8 row offset.
+        int qk_off[4], tr_off[2][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qk_off[j] = (l32 * 8 + ((2 * j + hf) ^ fswz(l32 & 15))) * 16;
+        {
+            const int r = (lane & 15) >> 2, g1 = (lane >> 4) & 1, b1 = (lane >> 1) & 1;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int t = 8 * e + 4 * hf + r;      // row within a 16-row group
+                    tr_off[j][e] = (t * 8 + ((4 * j + 2 * g1 + b1) ^ fswz(t))) * 16 + (lane & 1) * 8;
+                }
+        }
+        // score operand of K-step ks (rows l32 of the slot at sbase)
+        auto k_frag = [&](const lds_u8* sbase, int ks) __attribute__((always_inline)) -> bf16x8 {
+            return *reinterpret_cast<const MLA_LDS bf16x8*>(sbase + qk_off[ks & 3] + (ks >> 2) * 4096);
+        };
+        // value operand: V^T for latent columns 32 cm .. +32, K-step k2 (tokens
+        // 16 k2 + {0..3, 8..11} in lanes 0-31 and {4..7, 12..15} in lanes
+        // 32-63, the weights' layout)
+        auto v_frag = [&](const lds_u8* vbase, int cm, int k2) __attribute__((always_inline)) -> bf16x8 {
+            const lds_u8* vb = vbase + (cm >> 1) * 4096 + k2 * 16 * 128;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + tr_off[cm & 1][0]));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + tr_off[cm & 1][1]));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        // weights of head block hb, K-step k2, as the MFMA B operand: 1 KB,
+        // lane l at 16 l
+        auto p_frag = [&](const lds_u8* pb, int hb, int k2) __attribute__((always_inline)) -> bf16x8 {
+            return *reinterpret_cast<const MLA_LDS bf16x8*>(pb + (hb * 2 + k2) * 1024 + lane * 16);
+        };
+
+        // Softmax without rescaling the accumulators: every weight of a pass is
+        // exp2(s - m_ref) for one reference m_ref per head.  The first pass takes
+        // m_ref from the piece's first half-tile; if a later half-tile's maximum
+        // exceeds it by more than kMaxLead (weights stay below 2^64, far from
+        // fp32 overflow) the pass's result is discarded, one scan computes the
+        // exact maximum and a last pass runs with it.  (Scaling O inside the loop
+        // would force the 256 accumulators out of AGPRs.)  The waves vote after
+        // the loop, in LDS.
+        constexpr float kMaxLead = 64.0f;
+        // o[4 c + hb]: O^T for latent columns 32 (4 w + c) .. +32 and heads
+        // 32 hb .. +32
+        f32x16 o[16];
+        float m_ref = kNegInf, l_run = 0.f;
+        bool overflow = false;
+        int mode = 0;                        // 0: first-half reference, 1: max scan, 2: exact reference
+
+        // scores of one half, unscaled, in VGPRs: lane (hf, l32) holds head
+        // 32 w + l32, rows 8 (i/4) + 4 hf + (i%4) of the half
+        float sv[16];
+        bf16x8 pw[2];                        // this wave's weights of a half, per value K-step
+        float hmax = kNegInf, psum = 0.f;
+        int sv_valid = HROWS;                // rows of the half in sv that hold tokens
+        lds_u8* pw_dst = pbuf;               // where the weights of the half in sv go
+
+        // Softmax of the half held in sv as steps k = 0 .. 28, threaded between
+        // the MFMAs of another chain.  The instructions of one step do not
+        // depend on each other (a step's inputs come from earlier steps, at
+        // least one MFMA apart), so each step issues without stalling the
+        // wave: value i is scaled at step 8 + i, exponentiated at 9 + i and
+        // summed at 10 + i.  MASKED (a partial last half): rows past the
+        // sequence end are set to -inf in steps 0-3 and the rest follows four
+        // steps later.  SCAN: steps 1-7 only, raising m_ref to the half's
+        // maximum.  The weights end in LDS at pw_dst (this wave's head block).
+        float mx[6];
+        auto softmax_step = [&](auto kc, auto scan_c, auto mask_c) __attribute__((always_inline)) {
+            constexpr bool SCAN = decltype(scan_c)::value;
+            constexpr bool MASKED = decltype(mask_c)::value;
+            constexpr int k = decltype(kc)::value - (MASKED ? 4 : 0);
+            if constexpr (MASKED && k < 0) {
+                constexpr int g = k + 4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (8 * g + 4 * hf + j >= sv_valid) sv[4 * g + j] = kNegInf;
+            }
+            if constexpr (k == 1) {
+                mx[0] = max3f(sv[0], sv[1], sv[2]);
+                mx[1] = max3f(sv[3], sv[4], sv[5]);
+            }
+            if constexpr (k == 2) {
+                mx[2] = max3f(sv[6], sv[7], sv[8]);
+                mx[3] = max3f(sv[9], sv[10], sv[11]);
+            }
+            if constexpr (k == 3) {
+                mx[4] = max3f(sv[12], sv[13], sv[14]);
+                mx[5] = max3f(sv[15], mx[0], mx[1]);
+            }
+            if constexpr (k == 4) mx[0] = max3f(mx[2], mx[3], mx[4]);
+            if constexpr (k == 5) hmax = max3f(mx[0], mx[5], mx[5]);
+            // the log2-domain score is sv * scale_log2 (scale_log2 > 0, so maxima
+            // commute with the scaling).  Maxima and sums stay per lane; the two
+            // lanes of a head (hf = 0, 1) combine once per pass.
+            if constexpr (k == 6) hmax *= scale_log2;
+            if constexpr (k == 7) {
+                if constexpr (SCAN) {
+                    m_ref = fmaxf(m_ref, hmax);
+                } else {
+                    // (cannot hold in the exact-reference pass: the scan saw the
+                    // same maxima, so at most three passes run)
+                    overflow |= hmax > m_ref + kMaxLead;
+                }
+            }
+            if constexpr (!SCAN) {
+                if constexpr (k >= 8 && k < 24) sv[k - 8] = __builtin_fmaf(sv[k - 8], scale_log2, -m_ref);
+                if constexpr (k >= 9 && k < 25) sv[k - 9] = __builtin_amdgcn_exp2f(sv[k - 9]);
+                if constexpr (k >= 10 && k < 26) psum += sv[k - 10];
+                // weights 4 j .. 4 j + 3 as bf16 into pw (j = 0, 1 at steps 18, 19;
+                // j = 2, 3 at steps 25, 26)
+                if constexpr (k == 18 || k == 19 || k == 25 || k == 26) {
+                    constexpr int j = (k == 18) ? 0 : (k == 19) ? 1 : (k == 25) ? 2 : 3;
+                    u32x4 t = __builtin_bit_cast(u32x4, pw[j >> 1]);
+                    t[(j & 1) * 2] = pack_bf16x2(sv[4 * j], sv[4 * j + 1]);
+                    t[(j & 1) * 2 + 1] = pack_bf16x2(sv[4 * j + 2], sv[4 * j + 3]);
+                    pw[j >> 1] = __builtin_bit_cast(bf16x8, t);
+                }
+                if constexpr (k == 27) {
+                    l_run += psum;
+                    psum = 0.f;
+                }
+                if constexpr (k == 28) {
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2)
+                        *reinterpret_cast<MLA_LDS bf16x8*>(pw_dst + (w * 2 + k2) * 1024 + lane * 16) = pw[k2];
+                }
+            }
+        };
+
+        // The scores of half h into sv, plain (a piece's first half).
+        auto first_scores = [&](int h) __attribute__((always_inline)) {
+            const lds_u8* sb = slot_of(h);
+            bf16x8 ring[DIST];
+            f32x16 sacc = {};
+            static_for<0, DIST>([&](auto mc) { ring[decltype(mc)::value] = k_frag(sb, decltype(mc)::value); });
+            static_for<0, NS>([&](auto mc) __attribute__((always_inline)) {
+                constexpr int m = decltype(mc)::value;
+                const bf16x8 a = ring[m % DIST];
+                if constexpr (m + DIST < NS) ring[m % DIST] = k_frag(sb, m + DIST);
+                sacc = mfma32(a, qf[m], sacc);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
+        };
+        // The weights of the half in sv, plain (SCAN: m_ref only).
+        auto plain_softmax = [&](auto scan_c) __attribute__((always_inline)) {
+            if (sv_valid < HROWS) {
+                static_for<0, 33>([&](auto kc) { softmax_step(kc, scan_c, std::true_type{}); });
+            } else {
+                static_for<0, 29>([&](auto kc) { softmax_step(kc, scan_c, std::false_type{}); });
+            }
+        };
+
+        // V_h: O^T += V^T . P^T for this wave's 4 column blocks and all 4 head
+        // blocks.  Slot m = 16 k2 + 4 c + hb; the value fragment of (k2, c) is
+        // read one column block ahead, the weights of K-step k2 (four 1 KB reads)
+        // at the start of the previous K-step.  Step hook(m) runs after the
+        // MFMA of slot m.
+        auto values = [&](const lds_u8* __restrict__ vb, const lds_u8* __restrict__ pb, auto hook)
+                          __attribute__((always_inline)) {
+            bf16x8 va[2], pf[2][4];
+            va[0] = v_frag(vb, 4 * w, 0);
+            static_for<0, 4>([&](auto hc) { pf[0][decltype(hc)::value] = p_frag(pb, decltype(hc)::value, 0); });
+            static_for<0, NV>([&](auto mc) __attribute__((always_inline)) {
+                constexpr int m = decltype(mc)::value;
+                constexpr int k2 = m >> 4, c = (m >> 2) & 3, hb = m & 3;
+                if constexpr (hb == 0 && m + 4 < NV) {      // next column block's fragment
+                    constexpr int kn = (m + 4) >> 4, cn = ((m + 4) >> 2) & 3;
+                    va[((m >> 2) + 1) & 1] = v_frag(vb, 4 * w + cn, kn);
+                }
+                if constexpr (m == 0) {
+                    static_for<0, 4>([&](auto hc) { pf[1][decltype(hc)::value] = p_frag(pb, decltype(hc)::value, 1); });
+                }
+                o[4 * c + hb] = mfma32(va[(m >> 2) & 1], pf[k2][hb], o[4 * c + hb]);
+                hook(std::integral_constant<int, m>{});
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+
+        // One pipelined iteration: the scores S_{h+1} (into sv), with the copy
+        // of half h+3 spread over them; then, unless SCAN, V_h with the weights
+        // of h from LDS.  SOFT: the softmax of S_{h+1} is threaded between the
+        // V_h MFMAs (a partial S_{h+1}, the piece's last half, takes the plain
+        // masked softmax after the iteration instead).  SCAN: scores only.
+        auto iteration_body = [&](auto scan_c, auto soft_c, int h, const lds_u8* __restrict__ sb,
+                                  const lds_u8* __restrict__ vb, lds_u8* __restrict__ cb,
+                                  const lds_u8* __restrict__ pb) __attribute__((always_inline)) {
+            constexpr bool SCAN = decltype(scan_c)::value;
+            constexpr bool SOFT = decltype(soft_c)::value;
+            const __amdgpu_buffer_rsrc_t crs = half_rsrc(h + 3);
+            bf16x8 ring[DIST];
+            f32x16 sacc = {};
+            sv_valid = valid_half(h + 1);
+            static_for<0, DIST>([&](auto mc) { ring[decltype(mc)::value] = k_frag(sb, decltype(mc)::value); });
+            static_for<0, NS>([&](auto mc) __attribute__((always_inline)) {
+                constexpr int m = decltype(mc)::value;
+                const bf16x8 a = ring[m % DIST];
+                if constexpr (m + DIST < NS) ring[m % DIST] = k_frag(sb, m + DIST);
+                sacc = mfma32(a, qf[m], sacc);
+                if constexpr (m % 4 == 0) issue_half_part(crs, cb, w, lane, m / 4);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // the scores leave the accumulator
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
+            if constexpr (!SCAN) {
+                pw_dst = (lds_u8*)pbuf_of(h + 1);
+                values(vb, pb, [&](auto mc) __attribute__((always_inline)) {
+                    if constexpr (SOFT) softmax_step(mc, std::false_type{}, std::false_type{});
+                });
+            }
+        };
+        auto iteration = [&](auto scan_c, auto soft_c, int h) __attribute__((always_inline)) {
+            iteration_body(scan_c, soft_c, h, slot_at(h + 1), slot_at(h), slot_at(h + 3), pbuf_of(h));
+        };
+        // wait for half h and for every wave: h is a piece's first half (the
+        // two later halves' copies may stay in flight) or the half after the
+        // current one (one later half's copies may)
+        auto landed = [&](int h, bool first) {
+            if (first) barrier_landed_but_18();
+            else barrier_landed_but_9();
+            if (valid_half(h) < HROWS) {     // the last, partial half of the sequence
+                zero_half_rows((lds_u8*)slot_of(h), valid_half(h), tid);
+                __syncthreads();
+            }
+        };
+
+        for (;;) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[i] = f32x16{};
+            l_run = 0.f;
+            overflow = false;
+            if (!first_in_flight) {              // a later pass
+                issue_half(hfirst);
+                issue_half(hfirst + 1);
+                issue_half(hfirst + 2);
+            }
+            first_in_flight = false;
+            landed(hfirst, true);
+            first_scores(hfirst);
+            sv_valid = valid_half(hfirst);
+            pw_dst = (lds_u8*)pbuf_of(hfirst);
+            if (mode == 0) {
+                // the reference: the first half's maximum over both lanes of each
+                // head (rows past the sequence end excluded)
+                float mx0 = kNegInf;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if ((i >> 2) * 8 + 4 * hf + (i & 3) < sv_valid) mx0 = fmaxf(mx0, sv[i]);
+                mx0 *= scale_log2;
+                m_ref = fmaxf(mx0, __shfl_xor(mx0, 32, 64));
+            }
+            if (mode == 1) {
+                plain_softmax(std::true_type{});
+                for (int h = hfirst; h < hlast; ++h) {
+                    landed(h + 1, false);
+                    iteration(std::true_type{}, std::false_type{}, h);
+                    plain_softmax(std::true_type{});
+                }
+            } else {
+                plain_softmax(std::false_type{});
+                // every half but the last is full: their softmax runs inside the
+                // iteration that computes their scores
+                for (int h = hfirst; h < hlast - 1; ++h) {
+                    landed(h + 1, false);
+                    iteration(std::false_type{}, std::true_type{}, h);
+                }
+                if (hlast > hfirst) {
+                    landed(hlast, false);
+                    iteration(std::false_type{}, std::false_type{}, hlast - 1);
+                    pw_dst = (lds_u8*)pbuf_of(hlast);
+                    plain_softmax(std::false_type{});
+                }
+                barrier_lds();                   // the last half's weights are in LDS
+                values(slot_of(hlast), pbuf_of(hlast), [](auto) {});
+            }
+            // ---- vote: did any wave's weights run past the reference? ------------------
+            wait_vmem_all();                 // (record-less copies included)
+            __syncthreads();                 // all waves are done with the ring
+            MLA_LDS int* votes = reinterpret_cast<MLA_LDS int*>(smem);
+            if (lane == 0) votes[w] = __builtin_amdgcn_ballot_w64(overflow) != 0;
+            __syncthreads();
+            const bool redo = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+            __syncthreads();                 // votes read before the next pass reuses the ring
+            if (redo) {
+                mode = 1;
+                m_ref = kNegInf;
+                continue;
+            }
+            if (mode == 1) {             // the scan's maxima: both lanes of each head
+                m_ref = fmaxf(m_ref, __shfl_xor(m_ref, 32, 64));
+                mode = 2;
+                continue;
+            }
+            break;
+        }
+        l_run += __shfl_xor(l_run, 32, 64);  // the head's two lanes hold disjoint tokens
+
+        // ---- epilogue: normalised partial o_lat (fp16) and log-sum-exp ---------------
+        // The partial is a convex combination of latent rows: fp16 keeps it to
+        // 2^-11 relative and halves the bytes written (and read by the combine).
+        // Wave w holds columns 128w .. 128w+127 of all 128 heads; each head's
+        // sum of weights comes from the wave that owns the head's scores,
+        // through LDS.  The accumulator layout scatters a lane's values over 32
+        // column rows, so each wave transposes through its own LDS region (the
+        // ring is free after the vote barrier) and writes 256-byte pieces of the
+        // head rows.
+        if (hf == 0) reinterpret_cast<MLA_LDS float*>(pbuf)[head] = l_run;
+        barrier_lds();
+        float inv_l[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) inv_l[hb] = 1.0f / reinterpret_cast<const MLA_LDS float*>(pbuf)[hb * 32 + l32];
+        // staging: head row hh (0..127) of this wave at hh * OSTR halves, row
+        // stride 136 halves (272 bytes): the 8-byte writes of 16 consecutive
+        // lanes (16 head rows) fall on distinct banks
+        constexpr int OSTR = 136;
+        MLA_LDS unsigned short* ost = reinterpret_cast<MLA_LDS unsigned short*>(smem + w * (128 * OSTR * 2));
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u16x4 hv;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) hv[j] = f32_to_f16_bits(o[4 * c + hb][4 * g + j] * inv_l[hb]);
+                    *reinterpret_cast<MLA_LDS u16x4*>(ost + (hb * 32 + l32) * OSTR + c * 32 + g * 8 + 4 * hf) = hv;
+                }
+        // LDS operations of one wave complete in order: the reads see the writes.
+        // 128 head rows x 16 chunks of 16 bytes; lane l takes chunk l % 16 of
+        // rows 4 i + l / 16.  Waves start at different rows so that concurrent
+        // stores spread over memory channels.
+        // (a buffer resource over the slot's partial keeps the addresses 32-bit)
+        const __amdgpu_buffer_rsrc_t prs = make_rsrc(part_o + (size_t)pslot * H * DC, H * DC * 2);
+        const int rot = (blockIdx.x * 4 + w) & 31;
+#pragma unroll 4
+        for (int i = 0; i < 32; ++i) {
+            const int hh = 4 * ((i + rot) & 31) + (lane >> 4);
+            const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(ost + hh * OSTR + (lane & 15) * 8);
+            __builtin_amdgcn_raw_buffer_store_b128(v, prs, (hh * DC + w * 128 + (lane & 15) * 8) * 2, 0, 0);
         }
         if (hf == 0) lse_dst[head] = (m_ref + __builtin_log2f(l_run)) * kLn2;
     }
@@ -1086,20 +1521,15 @@ hipError_t launch_decode_mfma(const DecodeLaunch& a, unsigned stages) {
         // balanced scheduling: one workgroup per compute unit
         const int grid = a.num_splits > 0 ? R * a.num_splits : kNumCUs;
         const float scale_log2 = a.scale * kLog2e;
-        if (a.cache_dtype == MLA_FP8_E4M3 && a.fp8_scores) {
-            split_kv_kernel<true, true><<<grid, 256, 0, a.stream>>>(
-                qbuf, static_cast<const unsigned char*>(a.pool), a.pool_scale, a.block_table,
-                a.max_blocks, a.seq_lens, R, a.q_len, a.num_splits, scale_log2,
-                static_cast<unsigned short*>(a.part_o), a.part_lse);
-        } else if (a.cache_dtype == MLA_FP8_E4M3) {
+        if (a.cache_dtype == MLA_FP8_E4M3) {
             split_kv_kernel<true><<<grid, 256, 0, a.stream>>>(
                 qbuf, static_cast<const unsigned char*>(a.pool), a.pool_scale, a.block_table,
                 a.max_blocks, a.seq_lens, R, a.q_len, a.num_splits, scale_log2,
                 static_cast<unsigned short*>(a.part_o), a.part_lse);
         } else {
-            split_kv_kernel<false><<<grid, 256, 0, a.stream>>>(
-                qbuf, static_cast<const unsigned char*>(a.pool), nullptr, a.block_table,
-                a.max_blocks, a.seq_lens, R, a.q_len, a.num_splits, scale_log2,
+            split_kv_ring_kernel<<<grid, 256, 0, a.stream>>>(
+                qbuf, static_cast<const unsigned char*>(a.pool), a.block_table, a.max_blocks,
+                a.seq_lens, R, a.q_len, a.num_splits, scale_log2,
                 static_cast<unsigned short*>(a.part_o), a.part_lse);
         }
         hipError_t e = hipGetLastError();

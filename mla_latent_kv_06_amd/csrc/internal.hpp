@@ -19,7 +19,6 @@ struct DecodeLaunch {
     // shape
     int H, DC, DR, N, V, BS;
     int cache_dtype, act_dtype;
-    bool fp8_scores = false;     // fp8 cache: score product on fp8 matrix cores
     float scale;                 // softmax scale (natural units)
     int batch, q_len, num_splits;
     // tensors

@@ -77,15 +77,6 @@ __device__ __forceinline__ void p_stage_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// max(a, b, c) in one instruction.  (fmaxf on matrix-core results first
-// quiets each input in IEEE mode, one extra instruction per value; the
-// scores here are never NaN: masked ones are -inf.)
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-
 __device__ __forceinline__ int seq_len_of(const int* __restrict__ seq_lens, int b, int Tmax) {
     return min(max(seq_lens[b], 0), Tmax);
 }

@@ -95,9 +95,8 @@ class Case:
     def act_f64(self, name: str) -> np.ndarray:
         return act_to_f64(getattr(self, name), self.wl.act_dtype)
 
-    def oracle_decode(self, seqs=None, heads=None, pool=None, scale=None, fp8_queries=False):
-        """Oracle output for the listed sequences (all by default) and heads;
-        ``fp8_queries``: the decode whose score product takes e4m3 queries."""
+    def oracle_decode(self, seqs=None, heads=None, pool=None, scale=None):
+        """Oracle output for the listed sequences (all by default) and heads."""
         seqs = list(range(self.wl.batch)) if seqs is None else list(seqs)
         rows_all = self.pool_rows_f64(pool, scale)
         qn = self.act_f64("q_nope")[seqs]
@@ -109,8 +108,7 @@ class Case:
         rows = [oracle.gather_sequence(rows_all, self.block_table[b], int(self.seq_lens[b]),
                                        self.wl.block_size) for b in seqs]
         scale_ = oracle.default_softmax_scale(self.wl.qk_nope_dim, self.wl.qk_rope_dim)
-        fn = oracle.decode_fp8_queries if fp8_queries else oracle.decode_naive
-        return fn(qn, qp, wuk, wuv, rows, self.wl.q_len, scale_)
+        return oracle.decode_naive(qn, qp, wuk, wuv, rows, self.wl.q_len, scale_)
 
 
 def build_case(wl: synth.Workload, seed: int = 0, fill=None, seq_lens_override=None) -> Case:
