@@ -225,6 +225,32 @@ mla_status mla_decode_absorbed_stages(const mla_dims* dims, int32_t batch, int32
                                       size_t workspace_bytes, uint32_t stages,
                                       void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * mla_decode_absorbed with no workspace argument.  Its scratch is one
+ * statically sized device array inside the library (MLA_NOALLOC_SCRATCH_BYTES
+ * per GPU, held from the library's first use on that GPU until the process
+ * ends); the call allocates nothing.
+ *
+ * Arguments, results and requirements as mla_decode_absorbed, and the same
+ * kernels run.  The stream must belong to the current device.  A call whose
+ * workspace (mla_decode_workspace_size for the same arguments) exceeds
+ * MLA_NOALLOC_SCRATCH_BYTES returns MLA_ERR_WORKSPACE_TOO_SMALL and launches
+ * nothing; with the balanced schedule on the DeepSeek-V3 shape that admits
+ * batch * q_len up to 119.  Every call on one GPU uses the same array, which
+ * keeps what the last call left: calls that overlap on one GPU (on several
+ * streams, or on one stream from several host threads without ordering)
+ * race and their results are undefined. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+mla_status mla_decode_absorbed_noalloc(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                       const void* q_nope, const void* q_pe,
+                                       const void* w_uk, const void* w_uv,
+                                       const void* cache_pool, const float* cache_scale,
+                                       const int32_t* block_table,
+                                       int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, int32_t num_splits,
+                                       void* out, float* lse, void* stream);
+
 /* ---- query path ------------------------------------------------------------
  *
  * The decode's query inputs from the layer input ("DeepSeek-V2: MLA

@@ -38,7 +38,8 @@ EXPORTED = ("mla_status_string", "mla_last_error", "mla_cache_row_bytes",
             "mla_cache_block_bytes", "mla_cache_append_workspace_size", "mla_cache_append",
             "mla_decode_default_splits", "mla_decode_workspace_size", "mla_decode_absorbed",
             "mla_decode_absorbed_stages", "mla_query_workspace_size", "mla_query_project",
-            "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_stages")
+            "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_stages",
+            "mla_decode_absorbed_noalloc")
 
 
 class Dims(ctypes.Structure):
@@ -88,6 +89,9 @@ _lib.mla_decode_workspace_size.argtypes = [_DP, _I, _I, _I, ctypes.POINTER(_SZ)]
 _lib.mla_decode_absorbed.restype = ctypes.c_int
 _lib.mla_decode_absorbed.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I,
                                      _P, _P, _P, _SZ, _P]
+_lib.mla_decode_absorbed_noalloc.restype = ctypes.c_int
+_lib.mla_decode_absorbed_noalloc.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I,
+                                             _P, _P, _P]
 _lib.mla_query_workspace_size.restype = ctypes.c_int
 _lib.mla_query_workspace_size.argtypes = [_DP, _I, _I, _I, _I, ctypes.POINTER(_SZ)]
 _lib.mla_query_project.restype = ctypes.c_int
@@ -191,15 +195,9 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def decode(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_table, seq_lens,
-           num_splits: int = 0, out=None, lse=None, workspace=None,
-           stages: int = STAGE_ALL, want_lse: bool = True):
-    """One absorbed-MLA decode step (mla_decode_absorbed[_stages]).
-
-    q_nope [B, Sq, H, N], q_pe [B, Sq, H, R] (act dtype); w_uk [H, N, d_c],
-    w_uv [H, V, d_c]; cache_pool [num_blocks, block_size, d_c + R] (cache dtype);
-    cache_scale [num_blocks, block_size] float32 (fp8 only); block_table
-    [B, max_blocks] int32; seq_lens [B] int32.  Returns (out, lse)."""
+def _decode_tensors(dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_table,
+                    seq_lens, out, lse, want_lse):
+    """Check the decode's tensors; create out (and lse) when not given."""
     act = _TORCH_OF[dims.act_dtype]
     B, Sq = q_nope.shape[0], q_nope.shape[1]
     H, N, R = dims.n_heads, dims.qk_nope_dim, dims.qk_rope_dim
@@ -225,6 +223,20 @@ def decode(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_
         lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
     if lse is not None:
         _need(lse, "lse", (torch.float32,), (B, Sq, H), dev)
+    return B, Sq, dev, out, lse
+
+
+def decode(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_table, seq_lens,
+           num_splits: int = 0, out=None, lse=None, workspace=None,
+           stages: int = STAGE_ALL, want_lse: bool = True):
+    """One absorbed-MLA decode step (mla_decode_absorbed[_stages]).
+
+    q_nope [B, Sq, H, N], q_pe [B, Sq, H, R] (act dtype); w_uk [H, N, d_c],
+    w_uv [H, V, d_c]; cache_pool [num_blocks, block_size, d_c + R] (cache dtype);
+    cache_scale [num_blocks, block_size] float32 (fp8 only); block_table
+    [B, max_blocks] int32; seq_lens [B] int32.  Returns (out, lse)."""
+    B, Sq, dev, out, lse = _decode_tensors(dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                                           block_table, seq_lens, out, lse, want_lse)
     ws_bytes = decode_workspace_size(dims, B, Sq, num_splits)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -235,6 +247,23 @@ def decode(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_
         _ptr(seq_lens), num_splits, _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel(), stages, _stream(dev))
     _check(st, "mla_decode_absorbed_stages")
+    return out, lse
+
+
+def decode_noalloc(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_table,
+                   seq_lens, out, lse=None, num_splits: int = 0):
+    """mla_decode_absorbed_noalloc: the decode on the library's static scratch.
+    Arguments as for ``decode``; out (and lse, if wanted) must be given, so
+    that nothing is allocated.  Returns (out, lse)."""
+    if out is None:
+        raise ValueError("out is required (this call allocates nothing)")
+    B, Sq, dev, out, lse = _decode_tensors(dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                                           block_table, seq_lens, out, lse, False)
+    st = _lib.mla_decode_absorbed_noalloc(
+        ctypes.byref(dims), B, Sq, _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+        _ptr(cache_pool), _ptr(cache_scale), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), num_splits, _ptr(out), _ptr(lse), _stream(dev))
+    _check(st, "mla_decode_absorbed_noalloc")
     return out, lse
 
 

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "internal.hpp"
 #include "prefill.hpp"
@@ -338,6 +339,35 @@ mla_status prefill_impl(const mla_dims* dims, int32_t batch, int32_t q_len, cons
     return ok();
 }
 
+// Scratch of mla_decode_absorbed_noalloc: one array per GPU (each device
+// holds its own copy), placed by the code object, never allocated by a call.
+// In host code `scratch` names a host-side stand-in; the device address comes
+// from hipGetSymbolAddress, once per device with that device current.
+__device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+mla_status noalloc_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MLA_ERR_UNSUPPORTED, "device %d: at most %d devices are supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -474,6 +504,31 @@ mla_status mla_decode_absorbed_stages(const mla_dims* dims, int32_t batch, int32
     return decode_impl(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
                        block_table, max_blocks_per_seq, seq_lens, num_splits, out, lse, workspace,
                        workspace_bytes, stages, stream);
+}
+
+mla_status mla_decode_absorbed_noalloc(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                       const void* q_nope, const void* q_pe, const void* w_uk,
+                                       const void* w_uv, const void* cache_pool,
+                                       const float* cache_scale, const int32_t* block_table,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                       int32_t num_splits, void* out, float* lse, void* stream) {
+    if (mla_status st = check_dims(dims); st != MLA_OK) return st;
+    if (batch < 0 || q_len < 1 || q_len > 1024)
+        return fail(MLA_ERR_BAD_SHAPE, "batch=%d must be >= 0 and q_len=%d in [1, 1024]", batch, q_len);
+    if (num_splits < 0 || num_splits > mla::kMaxSplits)
+        return fail(MLA_ERR_BAD_SHAPE, "num_splits=%d outside [0, %d]", num_splits, mla::kMaxSplits);
+    if (batch == 0) return ok();
+    const size_t need = decode_ws(*dims, batch, q_len, num_splits).total;
+    if (need > MLA_NOALLOC_SCRATCH_BYTES)
+        return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                    "this decode needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(use mla_decode_absorbed with a workspace)", need,
+                    (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (mla_status st = noalloc_scratch(&ws); st != MLA_OK) return st;
+    return decode_impl(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                       block_table, max_blocks_per_seq, seq_lens, num_splits, out, lse, ws,
+                       MLA_NOALLOC_SCRATCH_BYTES, MLA_STAGE_ALL, stream);
 }
 
 mla_status mla_query_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
