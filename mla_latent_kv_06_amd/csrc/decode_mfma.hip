@@ -851,15 +851,23 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
 
     // ---- this workgroup's pieces: as in split_kv_kernel ----------------------------
     int cur_row = 0, cur_rs = 0, rng_a = 0, rng_b = 0;
+    int grp = blockIdx.x;                // this workgroup's range of the balanced schedule
     bool fixed_pending = num_splits > 0;
     if (num_splits == 0) {
         MLA_LDS int* sc = reinterpret_cast<MLA_LDS int*>(smem);
         int excl, mine;
         const int T = scan_row_tiles(seq_lens, q_len, R, sc, &excl, &mine);
         const long long G = balanced_groups(gridDim.x, T);
-        if ((long long)blockIdx.x >= G) return;      // uniform: the whole workgroup leaves
-        rng_a = (int)((long long)blockIdx.x * T / G);
-        rng_b = (int)((long long)(blockIdx.x + 1) * T / G);
+        // Range L of the balanced schedule runs on workgroup id b with
+        // L = (b % 8) * per + b / 8, per = ceil(G / 8): workgroups share an XCD
+        // (XCD = id % 8 on this grid of 256) in runs of consecutive ranges, so
+        // the workgroups of one query row read its queries through one L2.
+        const int per = (int)((G + 7) / 8);
+        const int bx = blockIdx.x & 7, bk = blockIdx.x >> 3;
+        grp = bk < per ? bx * per + bk : (int)G;
+        if ((long long)grp >= G) return;             // uniform: the whole workgroup leaves
+        rng_a = (int)((long long)grp * T / G);
+        rng_b = (int)((long long)(grp + 1) * T / G);
         if (rng_a < rng_b && excl <= rng_a && rng_a < excl + mine) {
             const int per = (R + 255) / 256;
             int rs = excl;
@@ -908,7 +916,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
                 row = r;
                 t0 = lo;
                 t1 = hi;
-                slot = blockIdx.x + r;
+                slot = grp + r;
                 return true;
             }
         }
