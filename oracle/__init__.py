@@ -13,6 +13,8 @@ Parity status of each public function (what pins it is listed in
 ``tests/test_oracle_pins.py``):
 
 * ``decode_naive``           pinned (associativity, brute force, special cases)
+* ``decode_absorbed``        pinned (equals ``decode_naive`` to 1e-12 relative,
+                             and the pure-Python brute force)
 * ``round_to_bf16``          pinned (vs torch.bfloat16 on binary32 inputs, ties)
 * ``append_rows``            pinned (brute force, RMSNorm / RoPE invariants)
 * ``query_rows``             pinned (head-block layout, query/key relative
@@ -34,6 +36,7 @@ from .mla_ref import (  # noqa: F401
     slot_index,
     gather_sequence,
     decode_naive,
+    decode_absorbed,
     default_softmax_scale,
     round_to_bf16,
 )

@@ -212,3 +212,54 @@ def decode_naive(q_nope, q_pe, w_uk, w_uv, seq_rows, q_len, softmax_scale=None):
                 out[b, s, i] = (e / tot) @ v_full[:n_vis]
                 lse[b, s, i] = m + math.log(tot)
     return out, lse
+
+
+def decode_absorbed(q_nope, q_pe, w_uk, w_uv, seq_rows, q_len, softmax_scale=None):
+    """MLA decode in the weight-absorbed form, float64.
+
+    "DeepSeek-V2: MLA Explained", "Optimization Note": W_UK moves onto the
+    query side and W_UV onto the output by associativity, so per sequence b,
+    query row s and head i
+
+      q_lat_i = W_UK[i]^T q^C_i                       (d_c values)
+      s_j     = (q_lat_i . c_j + q^R_i . k^R_j) * scale
+      o_lat_i = sum_j softmax_j(s) c_j
+      o_i     = W_UV[i] o_lat_i
+
+    over the tokens row s may see.  Equal to ``decode_naive`` up to rounding
+    (matrix associativity); it costs 2 (d_c + R + d_c) flops per visible
+    token and head instead of the naive form's decompression, which makes
+    whole-workload checks of the large configurations affordable.
+    Arguments and results as ``decode_naive``."""
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    q_pe = np.asarray(q_pe, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    B, Sq, H, N = q_nope.shape
+    R = q_pe.shape[-1]
+    d_c = w_uk.shape[-1]
+    V = w_uv.shape[1]
+    if Sq != q_len:
+        raise ValueError("q_len does not match q_nope")
+    scale = default_softmax_scale(N, R) if softmax_scale is None else float(softmax_scale)
+    out = np.zeros((B, Sq, H, V))
+    lse = np.full((B, Sq, H), -np.inf)
+    for b in range(B):
+        rows = np.asarray(seq_rows[b], dtype=np.float64)
+        L = rows.shape[0]
+        c = rows[:, :d_c]
+        kr = rows[:, d_c:]
+        for s in range(Sq):
+            n_vis = L - Sq + s + 1
+            if n_vis <= 0:
+                continue
+            q_lat = np.stack([w_uk[i].T @ q_nope[b, s, i] for i in range(H)])   # [H, d_c]
+            sc = (q_lat @ c[:n_vis].T + q_pe[b, s] @ kr[:n_vis].T) * scale       # [H, n_vis]
+            m = sc.max(axis=1)
+            e = np.exp(sc - m[:, None])
+            tot = e.sum(axis=1)
+            o_lat = (e / tot[:, None]) @ c[:n_vis]                               # [H, d_c]
+            out[b, s] = np.stack([w_uv[i] @ o_lat[i] for i in range(H)])
+            lse[b, s] = m + np.log(tot)
+    return out, lse
+

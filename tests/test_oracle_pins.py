@@ -135,6 +135,10 @@ def test_p2_associativity_small(Sq):
     o2, l2 = _absorbed(qn, qp, wuk, wuv, rows, Sq, scale)
     assert np.max(np.abs(o1 - o2)) <= 1e-12 * max(1.0, np.max(np.abs(o1)))
     assert np.max(np.abs(l1 - l2)) <= 1e-12
+    # the oracle's own absorbed form (used for whole-workload GPU checks)
+    o3, l3 = oracle.decode_absorbed(qn, qp, wuk, wuv, rows, Sq, scale)
+    assert np.max(np.abs(o1 - o3)) <= 1e-12 * max(1.0, np.max(np.abs(o1)))
+    assert np.max(np.abs(l1 - l3)) <= 1e-12
 
 
 def test_p2_associativity_v3_heads():
@@ -152,6 +156,28 @@ def test_p2_associativity_v3_heads():
     rel = np.max(np.abs(o1 - o2)) / np.max(np.abs(o1))
     assert rel <= 1e-10
     assert np.max(np.abs(l1 - l2)) <= 1e-10
+    o3, l3 = oracle.decode_absorbed(qn, qp, wuk, wuv, rows, 1)
+    assert np.max(np.abs(o1 - o3)) / np.max(np.abs(o1)) <= 1e-10
+    assert np.max(np.abs(l1 - l3)) <= 1e-10
+
+
+def test_p2_absorbed_oracle_rows_that_see_nothing_and_planted_mistakes():
+    """Rows with no visible token give zeros and -inf, as the naive form; and
+    the absorbed oracle is not trivially equal to the naive one: a transposed
+    W_UV, a dropped rotary term or a wrong scale each break the agreement."""
+    rng = np.random.default_rng(12)
+    qn, qp, wuk, wuv, rows = _rand_problem(rng, B=2, Sq=2, L=(1, 6))
+    o1, l1 = oracle.decode_naive(qn, qp, wuk, wuv, rows, 2, 0.3)
+    o3, l3 = oracle.decode_absorbed(qn, qp, wuk, wuv, rows, 2, 0.3)
+    assert np.isneginf(l1[0, 0]).all() and np.isneginf(l3[0, 0]).all()
+    assert np.all(o3[0, 0] == 0)
+    fin = np.isfinite(l1)
+    assert np.max(np.abs(o1 - o3)) <= 1e-12 and np.max(np.abs(l1[fin] - l3[fin])) <= 1e-12
+    bad_pe = np.zeros_like(qp)
+    o4, _ = oracle.decode_absorbed(qn, bad_pe, wuk, wuv, rows, 2, 0.3)
+    assert np.max(np.abs(o4 - o1)) > 1e-3
+    o5, _ = oracle.decode_absorbed(qn, qp, wuk, wuv, rows, 2, 0.31)
+    assert np.max(np.abs(o5 - o1)) > 1e-4
 
 
 # --------------------------------------------------------------------------
@@ -207,6 +233,11 @@ def test_p3_brute_force_tiny_workload():
                                  rows, wl.q_len)
     assert np.max(np.abs(got - exp)) <= 1e-12
     assert np.max(np.abs(got_lse - exp_lse)) <= 1e-12
+    ab, ab_lse = oracle.decode_absorbed(case.act_f64("q_nope"), case.act_f64("q_pe"),
+                                        case.act_f64("w_uk"), case.act_f64("w_uv"),
+                                        [case.seq_rows(0)], wl.q_len)
+    assert np.max(np.abs(ab - exp)) <= 1e-12
+    assert np.max(np.abs(ab_lse - exp_lse)) <= 1e-12
 
 
 def test_p3_brute_force_two_queries():
