@@ -14,6 +14,7 @@ reads outside the visible tokens shows it.
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 
 import numpy as np
@@ -133,7 +134,7 @@ def build_case(wl: synth.Workload, seed: int = 0, fill=None, seq_lens_override=N
     flat = pool.reshape(-1, D)
     flat_scale = None if scale is None else scale.reshape(-1)
     fill = list(range(wl.batch)) if fill is None else list(fill)
-    for b in fill:
+    def write(b):
         # rows the cache already holds before the step: all decode tokens for
         # decode-only workloads, the cached prefix when the append writes the rest
         n_rows = int(cached[b]) if wl.append else int(seq_lens[b])
@@ -148,6 +149,10 @@ def build_case(wl: synth.Workload, seed: int = 0, fill=None, seq_lens_override=N
             flat_scale[phys] = sc
         else:
             flat[phys] = rows.astype(np.float32)
+
+    # sequences own disjoint slots, and numpy drops the GIL in the heavy steps
+    with concurrent.futures.ThreadPoolExecutor(min(8, max(1, len(fill)))) as ex:
+        list(ex.map(write, fill))
     case = Case(
         wl=wl, seed=seed, cached=cached, seq_lens=seq_lens, block_table=table,
         num_blocks=num_blocks, pool=pool, scale=scale,

@@ -1,0 +1,220 @@
+"""Whole-workload GPU parity at the full sizes of the stated configurations:
+every sequence, every query row and every head against the float64 oracle.
+
+* v3_b64_ctx1k8k_paged_bf16: the one-token append for all 64 sequences
+  (appended rows against ``oracle.append_rows``; every other byte of the pool
+  unchanged), then the decode on the pool read back from the device, against
+  ``oracle.decode_naive``.
+* v3_b4_ctx128k_split32_bf16: the decode with 32 partitions per row, all
+  heads against ``oracle.decode_absorbed`` and 16 against ``oracle.decode_naive``.
+* v3_b128_ctx8k32k_fp8_q2: the fp8 decode (two causal query rows), all heads
+  against ``oracle.decode_absorbed`` and 8 heads against ``oracle.decode_naive``.
+* v3_b64_ctx8k_paged_bf16 (the measured point): the decode, against
+  ``oracle.decode_absorbed`` (pinned to the naive form to 1e-12 relative).
+
+Bars as in test_gpu_decode.py (bf16: max-abs 2e-2 and rel-L2 5e-3 over the
+output tensor; fp8 cache: max-abs 6e-2, and here rel-L2 5e-3 as well, since
+the oracle reads the same dequantised codes; lse 1e-2).  The naive oracle needs
+about 34 MFLOP per cached token for all heads, the absorbed one about 0.3;
+these tests take minutes.
+
+Also: a pool larger than 4 GiB whose sequences use its topmost blocks (block
+byte offsets beyond 2^32), for the decode and the append, bf16 and fp8.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_06_amd import synth
+from tests import casebuild
+from tests.casebuild import build_case, error_stats
+
+pytestmark = pytest.mark.gpu
+W = synth.WORKLOADS
+BARS = {"bf16": (2e-2, 5e-3), "fp8": (6e-2, 5e-3)}
+
+
+def announce(*what):
+    print("[gpu-case]", *what, flush=True)
+
+
+def G():
+    from tests import gpu_util
+    return gpu_util
+
+
+def seq_rows_f64(case, b, pool, scale):
+    """float64 rows of sequence b (its visible tokens) from raw pool bytes,
+    converting only the rows the sequence uses."""
+    wl = case.wl
+    D, bs = wl.row_width, wl.block_size
+    L = int(case.seq_lens[b])
+    j = np.arange(L)
+    phys = case.block_table[b, j // bs].astype(np.int64) * bs + j % bs
+    raw = pool.reshape(-1, D)[phys]
+    if wl.cache_dtype == "bf16":
+        return oracle.bf16_bits_to_f64(raw)
+    return oracle.dequantize_rows_fp8(raw, scale.reshape(-1)[phys])
+
+
+def oracle_all(case, pool, scale, fn, heads=None):
+    """Oracle over every sequence, one sequence at a time (bounded memory);
+    ``heads`` restricts it to those heads."""
+    wl = case.wl
+    qn, qp = case.act_f64("q_nope"), case.act_f64("q_pe")
+    wuk, wuv = case.act_f64("w_uk"), case.act_f64("w_uv")
+    if heads is not None:
+        qn, qp, wuk, wuv = qn[:, :, heads], qp[:, :, heads], wuk[heads], wuv[heads]
+    sm = oracle.default_softmax_scale(wl.qk_nope_dim, wl.qk_rope_dim)
+    outs, lses = [], []
+    for b in range(wl.batch):
+        o, l = fn(qn[b:b + 1], qp[b:b + 1], wuk, wuv, [seq_rows_f64(case, b, pool, scale)],
+                  wl.q_len, sm)
+        outs.append(o)
+        lses.append(l)
+        if (b + 1) % 16 == 0 or b + 1 == wl.batch:
+            print(f"  oracle {fn.__name__}: {b + 1}/{wl.batch} sequences", flush=True)
+    return np.concatenate(outs), np.concatenate(lses)
+
+
+def check(got, ref, got_lse, ref_lse, cache_dtype, tag):
+    vis = np.isfinite(ref_lse)
+    max_abs, rel = error_stats(got[vis], ref[vis])
+    d_lse = float(np.max(np.abs(got_lse[vis] - ref_lse[vis])))
+    print(f"{tag}: max-abs {max_abs:.3e} rel-L2 {rel:.3e} lse {d_lse:.3e} "
+          f"({int(vis.sum())} rows x heads)", flush=True)
+    bar_abs, bar_rel = BARS[cache_dtype]
+    assert np.isfinite(got).all(), tag
+    assert max_abs <= bar_abs, (tag, max_abs)
+    if bar_rel is not None:
+        assert rel <= bar_rel, (tag, rel)
+    assert d_lse <= 1e-2, (tag, "lse", d_lse)
+    assert np.all(got[~vis] == 0)
+
+
+def test_full_batch64_append_then_decode_all_sequences():
+    from tests.test_gpu_append import check_untouched, expected_rows
+    wl = W["v3_b64_ctx1k8k_paged_bf16"]
+    announce(wl.name, "full: append + decode, all sequences and heads")
+    case = build_case(wl)
+    dc = G().DeviceCase(case)
+    before = case.pool.copy()
+    dc.append()
+    out, lse = dc.decode()
+    out, lse = G().to_np(out), G().to_np(lse)
+    after, _ = dc.pool_host()
+    rows, slots = expected_rows(case)
+    got_rows = oracle.bf16_bits_to_f64(check_untouched(before, after, slots, wl.row_width))
+    ma, rl = error_stats(got_rows, rows)
+    print(f"{wl.name} append (all {len(slots)} rows): max-abs {ma:.3e} rel-L2 {rl:.3e}", flush=True)
+    assert ma <= 2e-2 and rl <= 5e-3
+    ref, ref_lse = oracle_all(case, after, None, oracle.decode_naive)
+    check(out, ref, lse, ref_lse, "bf16", wl.name + " decode")
+
+
+def decode_full(wl):
+    case = build_case(wl)
+    dc = G().DeviceCase(case)
+    out, lse = dc.decode()
+    out, lse = G().to_np(out), G().to_np(lse)
+    del dc
+    torch.cuda.empty_cache()
+    return case, out, lse
+
+
+def test_full_batch4_128k_split32_all_sequences():
+    """All 4 sequences: every head against the absorbed form, 16 heads
+    spread over the 128 against the naive form."""
+    wl = W["v3_b4_ctx128k_split32_bf16"].replace(append=False)
+    announce(wl.name, "full: decode, all sequences, splits", wl.num_splits)
+    case, out, lse = decode_full(wl)
+    ref, ref_lse = oracle_all(case, case.pool, case.scale, oracle.decode_absorbed)
+    check(out, ref, lse, ref_lse, "bf16", wl.name + " (absorbed oracle, all heads)")
+    heads = list(range(0, 128, 8))
+    ref, ref_lse = oracle_all(case, case.pool, case.scale, oracle.decode_naive, heads)
+    check(out[:, :, heads], ref, lse[:, :, heads], ref_lse, "bf16",
+          wl.name + " (naive oracle, 16 heads)")
+
+
+def test_full_fp8_q2_all_sequences():
+    """All 128 sequences, both query rows: every head against the absorbed
+    form, and 8 heads spread over the 128 against the naive form."""
+    wl = W["v3_b128_ctx8k32k_fp8_q2"].replace(append=False)
+    announce(wl.name, "full: decode, all sequences, both query rows")
+    case, out, lse = decode_full(wl)
+    ref, ref_lse = oracle_all(case, case.pool, case.scale, oracle.decode_absorbed)
+    check(out, ref, lse, ref_lse, "fp8", wl.name + " (absorbed oracle, all heads)")
+    heads = [0, 17, 38, 63, 64, 90, 111, 127]
+    ref, ref_lse = oracle_all(case, case.pool, case.scale, oracle.decode_naive, heads)
+    check(out[:, :, heads], ref, lse[:, :, heads], ref_lse, "fp8",
+          wl.name + " (naive oracle, 8 heads)")
+
+
+def test_full_headline_point_all_sequences():
+    wl = W["v3_b64_ctx8k_paged_bf16"].replace(append=False)
+    announce(wl.name, "full: decode, all sequences and heads (absorbed-form oracle)")
+    case, out, lse = decode_full(wl)
+    ref, ref_lse = oracle_all(case, case.pool, case.scale, oracle.decode_absorbed)
+    check(out, ref, lse, ref_lse, "bf16", wl.name)
+
+
+# ---------------------------------------------------------------------------
+# a pool larger than 4 GiB
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8"])
+def test_pool_beyond_4gib(cache_dtype):
+    """The sequences' blocks are moved to the top of a pool of more than
+    4 GiB (every used block starts beyond byte 2^32); the decode and the
+    append must give what they give on the small pool, and the append must
+    write exactly its slots there."""
+    from mla_latent_kv_06_amd import binding as b
+    wl = W["v3_b64_ctx1k8k_paged_bf16"].replace(name="v3_big_pool", batch=3, ctx_lo=70,
+                                                ctx_hi=300, cache_dtype=cache_dtype)
+    case = build_case(wl)
+    dc = G().DeviceCase(case)
+    blk_bytes = wl.block_size * wl.row_width * (2 if cache_dtype == "bf16" else 1)
+    first = (1 << 32) // blk_bytes + 7                # first used block: past byte 2^32
+    total = first + case.num_blocks + 5
+    announce("big pool", cache_dtype, total, "blocks,", total * blk_bytes / 2**30, "GiB")
+    assert total * blk_bytes > (1 << 32) + case.num_blocks * blk_bytes
+    dev = G().DEV
+    big = torch.empty((total,) + tuple(dc.pool.shape[1:]), dtype=dc.pool.dtype, device=dev)
+    big.view(torch.uint8).fill_(0x7F)                   # NaN in bf16 (0x7F7F) and fp8 (0x7F)
+    big[first:first + case.num_blocks] = dc.pool
+    big_scale = None
+    if cache_dtype == "fp8":
+        big_scale = torch.full((total, wl.block_size), float("nan"), device=dev)
+        big_scale[first:first + case.num_blocks] = dc.scale
+    table = case.block_table.astype(np.int64)
+    table = np.where(table >= 0, table + first, table).astype(np.int32)
+    big_table = torch.from_numpy(table).to(dev)
+    # the append on both pools, then the decode on both
+    dc.append()
+    b.append(dc.dims, dc.h, dc.w_kv_a, dc.gamma, big_table, dc.start_pos, big, big_scale,
+             rms_eps=casebuild.RMS_EPS, rope_base=casebuild.ROPE_BASE)
+    torch.cuda.synchronize()
+    assert torch.equal(big[first:first + case.num_blocks].view(torch.uint8),
+                       dc.pool.view(torch.uint8))
+    if cache_dtype == "fp8":
+        assert torch.equal(big_scale[first:first + case.num_blocks].view(torch.int32),
+                           dc.scale.view(torch.int32))
+    assert bool((big[:first].view(torch.uint8) == 0x7F).all())
+    assert bool((big[first + case.num_blocks:].view(torch.uint8) == 0x7F).all())
+    o_small, l_small = dc.decode(num_splits=0)
+    o_big, l_big = b.decode(dc.dims, dc.q_nope, dc.q_pe, dc.w_uk, dc.w_uv, big, big_scale,
+                            big_table, dc.seq_lens, num_splits=0)
+    assert torch.equal(o_big.view(torch.int16), o_small.view(torch.int16))
+    assert torch.equal(l_big.view(torch.int32), l_small.view(torch.int32))
+    o_big, l_big = b.decode(dc.dims, dc.q_nope, dc.q_pe, dc.w_uk, dc.w_uv, big, big_scale,
+                            big_table, dc.seq_lens, num_splits=3)
+    out = G().to_np(o_big)
+    after, after_scale = dc.pool_host()
+    ref, ref_lse = case.oracle_decode(pool=after, scale=after_scale)
+    check(out, ref, G().to_np(l_big), ref_lse, cache_dtype, f"big pool {cache_dtype}")
+    del big, big_scale
+    torch.cuda.empty_cache()

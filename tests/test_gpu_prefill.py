@@ -10,12 +10,13 @@ concatenated outputs must equal causal attention over the whole prompt:
 (``append_rows``) and queries (``query_rows``), all from the same seeded
 draws.  No expected value comes from the device.
 
-Bars.  The decode-only tests give the scores one bf16 rounding (q_lat); here
-they carry four (c_Q, q, q_lat and the cache rows), each moving a score by
-up to ~2^-9 of its size, and the first rows of a prompt see one or two
-tokens, so nothing averages out.  Hence lse <= 2e-2 and output max-abs <=
-3e-2 (twice and 1.5 times the decode's bars); rel-L2 keeps the decode's
-5e-3.  Measured: lse 9.7e-3, max-abs 1.7e-2, rel-L2 3.7e-3.
+Bars.  The cache holds bf16 rows, so the oracle attends over its own rows
+rounded to bf16 (``round_to_bf16``), as the decode-only tests read back the
+stored bf16 rows.  The scores then still carry three roundings the decode-only
+tests do not (c_Q, q and q_lat), each moving a score by up to ~2^-9 of its
+size, and the first rows of a prompt see one or two tokens, so nothing
+averages out.  The bars are the decode's: output max-abs <= 2e-2, rel-L2 <=
+5e-3, lse <= 1e-2.
 """
 
 from __future__ import annotations
@@ -108,7 +109,8 @@ def test_chunked_prefill(L, C, attn):
 
     # ---- oracle: the whole prompt at once ----------------------------------------
     pos = np.arange(L)
-    rows = [oracle.append_rows(h[i], wkva, g_kv, casebuild.RMS_EPS, pos, dc, casebuild.ROPE_BASE)
+    rows = [oracle.round_to_bf16(oracle.append_rows(h[i], wkva, g_kv, casebuild.RMS_EPS, pos, dc,
+                                                    casebuild.ROPE_BASE))
             for i in range(B)]
     qn_r, qp_r = [], []
     for i in range(B):
@@ -121,4 +123,4 @@ def test_chunked_prefill(L, C, attn):
     print(f"chunked prefill L={L} C={C}: max-abs {max_abs:.3e} rel-L2 {rel:.3e} lse {d_lse:.3e}",
           flush=True)
     assert np.isfinite(out).all()
-    assert max_abs <= 3e-2 and rel <= 5e-3 and d_lse <= 2e-2, (max_abs, rel, d_lse)
+    assert max_abs <= 2e-2 and rel <= 5e-3 and d_lse <= 1e-2, (max_abs, rel, d_lse)
