@@ -36,6 +36,7 @@ import numpy as np
 
 METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak) at bs64, ctx 8k"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+EVENT_STRIDE = 3               # timed steps per kernel-event sample
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("decode_mfma.hip", "common.hpp", "internal.hpp")
@@ -44,6 +45,46 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "split_kv_kernel_v3_b64_ctx8k_b
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+class KernelEvent:
+    """A HIP event for timing kernels inside the timed loop, created with
+    hipEventDisableSystemFence: recording it does not write back and
+    invalidate the caches.  (A default event's system-scope release flushes
+    the L2's dirty lines when it is recorded: after a kernel that wrote tens
+    of MB, such as the split-KV partials, that puts several microseconds
+    between the kernel and the next one.)  Elapsed times are read after a
+    device synchronisation, as with any event."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if KernelEvent._hip is None:
+            # the HIP runtime torch has already loaded (same soname)
+            KernelEvent._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        self._check(KernelEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev),
+                                                             ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)))
+
+    @staticmethod
+    def _check(err):
+        if err != 0:
+            raise RuntimeError(f"HIP event call failed with error {err}")
+
+    def record(self, stream):
+        self._check(KernelEvent._hip.hipEventRecord(self.ev, self._ct.c_void_p(stream.cuda_stream)))
+
+    def elapsed_time(self, end):
+        ms = self._ct.c_float()
+        self._check(KernelEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self.ev, end.ev))
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
 
 
 def kernel_source_digest():
@@ -249,10 +290,13 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    qevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(args.steps)]
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    # Kernel events on every EVENT_STRIDE-th step of the timed region: a
+    # recorded event is a queue packet of its own that holds the next kernel
+    # back by about 5 us on this GPU, so instrumenting every step would add
+    # ~10 us to each; the sampled steps are spread over the whole region.
+    sampled = [i % EVENT_STRIDE == 0 for i in range(K)]
+    qevs = [(KernelEvent(), KernelEvent()) if sampled[i] else None for i in range(K)] if args.query_path else []
+    evs = [(KernelEvent(), KernelEvent()) if sampled[i] else None for i in range(K)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     if torch.distributed.is_available() and torch.distributed.is_initialized():
@@ -265,8 +309,8 @@ def main():
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / K
-    k_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
-    q_ms = np.array([e0.elapsed_time(e1) for e0, e1 in qevs]) if args.query_path else None
+    k_ms = np.array([e[0].elapsed_time(e[1]) for e in evs if e is not None])
+    q_ms = np.array([e[0].elapsed_time(e[1]) for e in qevs if e is not None]) if args.query_path else None
     k_avg_s = float(k_ms.mean()) / 1e3
 
     tokens_per_step = B * Sq
@@ -325,6 +369,7 @@ def main():
             "traffic": profiled_traffic(wl.name), "traffic_unit": "bytes per launch",
             "algorithmic_bytes": cache_bytes,
             "avg_launch_us": round(k_avg_s * 1e6, 2),
+            "launches_timed": int(len(k_ms)),
             "mfma_tflops": round(flops / k_avg_s / 1e12, 1),
             "mfma_frac": round(flops / k_avg_s / 1e12 / mfma_peak, 4),
         },
@@ -421,7 +466,7 @@ def prefill_main(args, torch, synth, b, dev):
         step(layers[i % n_layers])
     torch.cuda.synchronize()
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    evs = [[KernelEvent() for _ in range(4)] for _ in range(K)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -520,6 +565,7 @@ def prefill_cpu_baseline(wl, L, torch, n_q=8192, heads=tuple(range(16))):
     log(f"cpu oracle: {n_q} queries x {len(hs)} heads in {dt:.1f}s on {threads} threads; "
         f"GPU vs oracle max-abs {err:.2e}")
     return {"value": round(n_q * len(hs) / wl.n_heads / dt, 4), "unit": "tokens/s", "cores": threads,
+            "host_cpus": os.cpu_count(),
             "kind": "oracle",
             "sample": f"first {n_q} of {wl.q_len} queries of prompt 0, heads {hs[0]}-{hs[-1]} of "
                       f"{wl.n_heads}, naive float64 attention, {dt:.1f}s; rate scaled to all heads",
@@ -570,7 +616,7 @@ def cpu_baseline(args, wl, L, torch):
     err = float(np.max(np.abs(got - ref)))
     log(f"cpu oracle: {n} sequences in {dt:.1f}s on {threads} threads; GPU vs oracle max-abs {err:.2e}")
     return {"value": round(n * wl.q_len / dt, 4), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"{n} of {wl.batch} sequences ({tot} cached tokens, {wl.q_len} query "
                       f"row(s) each, all {wl.n_heads} heads), naive float64 decode, {dt:.1f}s",
             "gpu_vs_oracle_max_abs": err}

@@ -128,15 +128,14 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
                                      q_nope + ((size_t)r * H + h) * 128 + ks * 16 + hf * 8)
                                : bf16x8{};
         }
-    // q_pe rides along in the workgroups of column block 0
-    if (cb == 0) {
-        for (int i = tid; i < 64 * 8; i += 256) {       // 64 rows x 8 chunks of 8
-            const int r = rb * 64 + (i >> 3), c8 = i & 7;
-            if (r < R) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(q_pe + ((size_t)r * H + h) * DR + c8 * 8);
-                *reinterpret_cast<u32x4*>(qbuf + ((size_t)r * H + h) * D + DC + c8 * 8) = v;
-            }
-        }
+    // q_pe rides along in the workgroups of column block 0: 64 rows x 8
+    // chunks of 16 bytes, two per thread, loaded here with everything else
+    // (unconditionally, at clamped rows) and stored at the end
+    u32x4 pe[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int i = k * 256 + tid, r = min(rb * 64 + (i >> 3), R - 1), c8 = i & 7;
+        pe[k] = *reinterpret_cast<const u32x4*>(q_pe + ((size_t)r * H + h) * DR + c8 * 8);
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -186,6 +185,13 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
         if (r < R)
             *reinterpret_cast<u32x4*>(qbuf + ((size_t)r * H + h) * D + cb * 128 + c * 8) =
                 *reinterpret_cast<const u32x4*>(wt + rl * OROWB + c * 16);
+    }
+    if (cb == 0) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int i = k * 256 + tid, r = rb * 64 + (i >> 3), c8 = i & 7;
+            if (r < R) *reinterpret_cast<u32x4*>(qbuf + ((size_t)r * H + h) * D + DC + c8 * 8) = pe[k];
+        }
     }
 }
 
@@ -1052,7 +1058,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
                 constexpr int g = k + 4;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (8 * g + 4 * hf + j >= sv_valid) sv[4 * g + j] = kNegInf;
+                    if (8 * g + j >= sv_valid - 4 * hf) sv[4 * g + j] = kNegInf;
             }
             if constexpr (k == 1) {
                 mx[0] = max3f(sv[0], sv[1], sv[2]);
@@ -1223,10 +1229,13 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
             if (mode == 0) {
                 // the reference: the first half's maximum over both lanes of each
                 // head (rows past the sequence end excluded)
+                // (row 8 (i/4) + 4 hf + i%4 of the half: a constant against a
+                // per-lane limit, so no per-element row index stays live)
                 float mx0 = kNegInf;
+                const int lim = sv_valid - 4 * hf;
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if ((i >> 2) * 8 + 4 * hf + (i & 3) < sv_valid) mx0 = fmaxf(mx0, sv[i]);
+                    if ((i >> 2) * 8 + (i & 3) < lim) mx0 = fmaxf(mx0, sv[i]);
                 mx0 *= scale_log2;
                 m_ref = fmaxf(mx0, __shfl_xor(mx0, 32, 64));
             }
@@ -1327,178 +1336,324 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
 // 3. log-sum-exp combine of partitions, then out = W_UV o_lat
 // ---------------------------------------------------------------------------
 
-// grid: H * ceil(R / 32) workgroups (h fastest, so one head's row blocks share
-// an XCD and its W_UV slice in L2).  Workgroup (h, rb) handles rows rb*32 ..
-// +32 of head h; wave w combines rows 8w .. 8w+7, then computes
-// out^T[32w .. +32][rows] = W_UV[h] o_lat^T.  Every phase issues its global
-// loads together (partition weights, then all partitions of 8 rows, then the
-// whole W_UV slice) so each costs about one memory round trip.
-__global__ __launch_bounds__(256) void combine_kernel(
+// grid: H * ceil(R / 32) workgroups of 512 threads (h fastest, so one head's
+// row blocks share an XCD and its W_UV slice in L2).  Workgroup (h, rb)
+// handles rows rb*32 .. +32 of head h.  Its memory traffic is three
+// independent reads issued up front -- this head's W_UV slice (as MFMA
+// operands, wave w taking output values 16w .. 16w+15), the sequence lengths
+// (to locate each row's partials), then every partial and log-sum-exp of the
+// wave's 4 rows together -- so the kernel costs about two memory round trips.
+//  1. merge: wave w merges rows 4w .. 4w+3 online over their partials (lane
+//     holds latent columns 8 lane .. +8): o_lat = sum_p e^{lse_p} o_p / sum_p
+//     e^{lse_p}, lse = log sum_p e^{lse_p};
+//  2. out^T[16w .. +16][rows] = W_UV[h][16w .. +16] o_lat^T with o_lat from
+//     LDS as a bf16 hi + lo pair (16x16x32 MFMA, 32 K-steps of 16 per pair).
+constexpr int CMB_THREADS = 512;
+constexpr int CMB_CHUNK = 4;                    // partials per row loaded together
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(CMB_THREADS) void combine_kernel(
     const unsigned short* __restrict__ part_o,  // [slots][H][512] fp16
     const float* __restrict__ part_lse,         // [slots][H]
     const int* __restrict__ seq_lens, int q_len, int R, int num_splits, int groups,
     const unsigned short* __restrict__ w_uv,    // [H][128][512]
     unsigned short* __restrict__ out,           // [R][H][128] bf16
     float* __restrict__ lse_out) {              // [R][H] or null
-    __shared__ __attribute__((aligned(16))) unsigned char ol[2][32 * 1024];   // hi, lo bf16
-    __shared__ float wts[32][kMaxSplits];       // normalised partition weights per local row
+    // merged o_lat of the 32 rows, hi and lo bf16: row rl at rl * 1024 bytes,
+    // 16-byte chunk c at position c ^ (rl & 7)
+    __shared__ __attribute__((aligned(16))) unsigned char ol[2][32 * 1024];
+    __shared__ int pbase[32], pcnt[32], red[2][CMB_THREADS / 64];
+    __shared__ float xacc[CMB_THREADS / 64][512], xml[CMB_THREADS / 64][2];   // form B's wave results
     const int h = blockIdx.x % H;
-    const int rb = blockIdx.x / H;
+    const int rb = blockIdx.x / H, r0 = rb * 32;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in an SGPR
-    const int l32 = lane & 31, hf = lane >> 5;
-    __shared__ int pbase[32], pcnt[32];         // partial slots of each local row
 
-    // ---- where each row's partials are (see the split-KV work partition)
-    if (num_splits > 0) {
-        if (tid < 32) {
-            const bool in = rb * 32 + tid < R;
-            pbase[tid] = in ? (rb * 32 + tid) * num_splits : 0;
-            pcnt[tid] = in ? num_splits : 0;
+    // ---- sequence lengths first (their wait then leaves the W_UV loads in
+    // flight): thread tid reads the length behind row tid (and, past 512
+    // rows, every 512th after it); lanes 0..31 of wave 0 read this block's rows.
+    const bool balanced = num_splits == 0;
+    const int len_main = seq_lens[min(tid, R - 1) / q_len];
+    const int len_blk = seq_lens[min(r0 + (lane & 31), R - 1) / q_len];
+    // tiles of a row from its sequence length
+    auto tiles_of = [&](int r, int len) {
+        const int n_vis = len - q_len + (r - (r / q_len) * q_len) + 1;
+        return n_vis > 0 ? (n_vis + BS - 1) / BS : 0;
+    };
+    // (keeps the compiler from hoisting the W_UV loads above these: vector
+    // memory loads complete in order, so the lengths would wait for W_UV)
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- W_UV[h] rows 16w + (lane % 16), K-step ks: latent columns
+    // 32 ks + 8 (lane / 16) .. +8 (the A operand of the 16x16x32 MFMA)
+    bf16x8 wa[16];
+    {
+        const unsigned short* wrow = w_uv + ((size_t)h * 128 + 16 * w + (lane & 15)) * DC + (lane >> 4) * 8;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) wa[ks] = *reinterpret_cast<const bf16x8*>(wrow + ks * 32);
+    }
+
+    // ---- where each row's partials are (see the split-KV work partition).
+    // The balanced schedule's table is computed whatever the schedule (the
+    // branch-free form keeps the length loads ahead of W_UV's); a fixed
+    // partition overrides it.
+    {
+        // tiles of all rows (T) and of the rows before this block's
+        int total = 0, before = 0;
+        {
+            const int nt = tiles_of(tid, len_main) * (tid < R ? 1 : 0);
+            total = nt;
+            before = tid < r0 ? nt : 0;
         }
-    } else {
-        int* sc = reinterpret_cast<int*>(&wts[0][0]);
-        int excl, mine;
-        const int T = scan_row_tiles(seq_lens, q_len, R, sc, &excl, &mine);
-        const int per = (R + 255) / 256;
-        int rs = excl;
-        for (int k = 0; k < per; ++k) {
-            const int r = tid * per + k;
-            if (r >= R) break;
+        for (int r = tid + CMB_THREADS; r < R; r += CMB_THREADS) {
             const int nt = row_tiles(seq_lens, q_len, r);
-            if (r >= rb * 32 && r < rb * 32 + 32) {
-                const int G = (int)balanced_groups(groups, T);
-                const int f = nt > 0 ? group_of_tile(rs, T, G) : 0;
-                const int l = nt > 0 ? group_of_tile(rs + nt - 1, T, G) : -1;
-                pbase[r - rb * 32] = f + r;
-                pcnt[r - rb * 32] = l - f + 1;
-            }
-            rs += nt;
+            total += nt;
+            before += r < r0 ? nt : 0;
         }
-        if (tid < 32 && rb * 32 + tid >= R) {
-            pbase[tid] = 0;
-            pcnt[tid] = 0;
+#pragma unroll
+        for (int d = 32; d > 0; d >>= 1) {
+            total += __shfl_xor(total, d, 64);
+            before += __shfl_xor(before, d, 64);
+        }
+        if (lane == 0) {
+            red[0][w] = total;
+            red[1][w] = before;
+        }
+        __syncthreads();
+        if (w == 0) {
+            int T = 0, rs = 0;
+#pragma unroll
+            for (int k = 0; k < CMB_THREADS / 64; ++k) {
+                T += red[0][k];
+                rs += red[1][k];
+            }
+            // lanes 0..31: the block's rows, an exclusive scan of their tiles
+            const int r = r0 + (lane & 31);
+            const int nt = tiles_of(r, len_blk) * ((lane < 32 && r < R) ? 1 : 0);
+            int incl = nt;
+#pragma unroll
+            for (int d = 1; d < 32; d <<= 1) {
+                const int y = __shfl_up(incl, d, 64);
+                if ((lane & 31) >= d) incl += y;
+            }
+            rs += incl - nt;
+            if (lane < 32) {
+                if (balanced) {
+                    const int G = (int)balanced_groups(groups, T);
+                    const int f = nt > 0 ? group_of_tile(rs, T, G) : 0;
+                    const int l = nt > 0 ? group_of_tile(rs + nt - 1, T, G) : -1;
+                    pbase[lane] = f + r;
+                    pcnt[lane] = nt > 0 ? l - f + 1 : 0;
+                } else {
+                    pbase[lane] = r < R ? r * num_splits : 0;
+                    pcnt[lane] = r < R ? num_splits : 0;
+                }
+            }
         }
     }
     __syncthreads();
 
-    // ---- partition weights exp(lse_s - max) / sum and the merged lse; lanes
-    // run over partitions (at most 256 = 4 x 64)
-    int S = 0;                                  // most partials of this wave's rows
-    {
-        float lv[8][4];
+    // ---- 1. merge.  A partial whose piece saw no token has log-sum-exp -inf
+    // and unwritten memory: its weight is selected away, never multiplied, so
+    // whatever that memory holds cannot leak in.  Two forms:
+    //  A. (at most CMB_CHUNK partials per row, or many rows) wave w merges
+    //     rows 4w .. 4w+3 itself, CMB_CHUNK partials per row at a time;
+    //  B. (more partials, at most 8 rows) the waves split each row's
+    //     partials (8 / rows waves per row, 16 partials each at a time) and
+    //     the row's first wave merges their results through LDS, so that a
+    //     long row costs one memory round trip instead of one per CMB_CHUNK.
+    int S_blk = 0;
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int base = pbase[w * 8 + rr], cnt = pcnt[w * 8 + rr];
-            S = max(S, cnt);
+    for (int k = 0; k < 32; ++k) S_blk = max(S_blk, pcnt[k]);
+    const int rows_b = min(32, R - r0);
+    // per-lane merge of n partials into (m, l, acc): online log-sum-exp
+    auto merge_into = [&](float& m_run, float& l_run, float (&acc)[8], const u32x4* v, const float* lv,
+                          auto n_c) __attribute__((always_inline)) {
+        constexpr int n = decltype(n_c)::value;
+        float m_new = m_run;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int sp = lane + 64 * j;
-                lv[rr][j] = sp < cnt ? part_lse[((size_t)base + sp) * H + h] : kNegInf;
+        for (int j = 0; j < n; ++j) m_new = fmaxf(m_new, lv[j]);
+        if (m_new == kNegInf) return;                 // nothing visible yet
+        const float keep = m_run == kNegInf ? 0.f : __expf(m_run - m_new);
+        float e[n], esum = 0.f;
+#pragma unroll
+        for (int j = 0; j < n; ++j) {
+            e[j] = lv[j] == kNegInf ? 0.f : __expf(lv[j] - m_new);
+            esum += e[j];
+        }
+        l_run = l_run * keep + esum;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float a = acc[c] * keep;
+#pragma unroll
+            for (int j = 0; j < n; ++j) {
+                const float x = f16_bits_to_f32((unsigned short)(v[j][c >> 1] >> (16 * (c & 1))));
+                a += e[j] != 0.f ? e[j] * x : 0.f;
             }
+            acc[c] = a;
         }
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int rl = w * 8 + rr, r = rb * 32 + rl;
-            const float mx = wave_max(fmaxf(fmaxf(lv[rr][0], lv[rr][1]), fmaxf(lv[rr][2], lv[rr][3])));
-            float e[4], tot = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                e[j] = lv[rr][j] == kNegInf ? 0.f : __expf(lv[rr][j] - mx);
-                tot += e[j];
-            }
-            tot = wave_sum(tot);
-            const float inv = tot > 0.f ? 1.0f / tot : 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (lane + 64 * j < kMaxSplits) wts[rl][lane + 64 * j] = e[j] * inv;
-            if (lse_out != nullptr && lane == 0 && r < R)
-                lse_out[(size_t)r * H + h] = (mx == kNegInf) ? kNegInf : mx + __logf(tot);
-        }
-    }
-    // (each wave reads back only its own rows' weights: LDS operations of one
-    // wave complete in order)
-
-    // ---- o_lat of rows 8w .. 8w+7: lane holds columns 8 lane .. 8 lane + 7.
-    // A partition with no visible token has weight 0 and an unwritten partial:
-    // select, never multiply, so whatever that memory holds cannot leak in.
-    float acc[8][8];
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[rr][j] = 0.f;
-    const unsigned short* pcol = part_o + (size_t)h * DC + lane * 8;
-#pragma unroll 2
-    for (int sp = 0; sp < S; ++sp) {
-        u32x4 v[8];
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            // past a row's last partial the weight is 0: read its first one
-            const int sl = pbase[w * 8 + rr] + (sp < pcnt[w * 8 + rr] ? sp : 0);
-            v[rr] = *reinterpret_cast<const u32x4*>(pcol + (size_t)sl * H * DC);
-        }
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const float wt = wts[w * 8 + rr][sp];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float x = f16_bits_to_f32((unsigned short)(v[rr][j >> 1] >> (16 * (j & 1))));
-                acc[rr][j] += wt != 0.f ? wt * x : 0.f;
-            }
-        }
-    }
-    // W_UV slice of this wave's 32 output rows: all 32 fragments at once
-    bf16x8 wa[32];
-    {
-        const unsigned short* wrow = w_uv + ((size_t)h * 128 + w * 32 + l32) * DC + hf * 8;
-#pragma unroll
-        for (int ks = 0; ks < 32; ++ks) wa[ks] = *reinterpret_cast<const bf16x8*>(wrow + ks * 16);
-    }
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-        const int rl = w * 8 + rr;
+        m_run = m_new;
+    };
+    // merged row rl of the block into LDS as bf16 hi + lo, and its lse
+    auto emit_row = [&](int rl, float m_run, float l_run, const float (&acc)[8]) __attribute__((always_inline)) {
+        const int r = r0 + rl;
+        const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
         u16x8 hi, lo;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float v = acc[rr][j];
-            hi[j] = f32_to_bf16_bits(v);
-            lo[j] = f32_to_bf16_bits(v - bf16_bits_to_f32(hi[j]));
+        for (int c = 0; c < 8; ++c) {
+            const float x = acc[c] * inv;
+            hi[c] = f32_to_bf16_bits(x);
+            lo[c] = f32_to_bf16_bits(x - bf16_bits_to_f32(hi[c]));
         }
-        const int off = rl * 1024 + ((lane ^ (rl & 7)) << 4);   // chunk = lane (8 cols)
+        const int off = rl * 1024 + ((lane ^ (rl & 7)) << 4);   // chunk = lane (8 columns)
         *reinterpret_cast<u16x8*>(&ol[0][off]) = hi;
         *reinterpret_cast<u16x8*>(&ol[1][off]) = lo;
+        if (lse_out != nullptr && lane == 0 && r < R)
+            lse_out[(size_t)r * H + h] = l_run > 0.f ? m_run + __logf(l_run) : kNegInf;
+    };
+    if (S_blk > CMB_CHUNK && rows_b <= 8) {
+        // ---- form B
+        constexpr int NB = 16;
+        const int wpr = rows_b == 1 ? 8 : rows_b == 2 ? 4 : rows_b <= 4 ? 2 : 1;
+        const int rl = w / wpr, sub = w - rl * wpr;
+        float m_run = kNegInf, l_run = 0.f, acc[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+        if (rl < rows_b) {
+            const int base = pbase[rl], cnt = pcnt[rl];
+            const __amdgpu_buffer_rsrc_t prs = make_rsrc(part_o + (size_t)base * H * DC, cnt * H * DC * 2);
+            const __amdgpu_buffer_rsrc_t lrs = make_rsrc(part_lse + (size_t)base * H, cnt * H * 4);
+            for (int p0 = sub; p0 < cnt; p0 += NB * wpr) {
+                u32x4 v[NB];
+                float lv[NB];
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int sp = p0 + j * wpr;
+                    v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        prs, lane * 16, sp * (H * DC * 2) + h * (DC * 2), 0));
+                    lv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                         lrs, 0, sp * (H * 4) + h * 4, 0));
+                }
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    if (p0 + j * wpr >= cnt) lv[j] = kNegInf;
+                merge_into(m_run, l_run, acc, v, lv, std::integral_constant<int, NB>{});
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) xacc[w][lane * 8 + c] = acc[c];
+        if (lane == 0) {
+            xml[w][0] = m_run;
+            xml[w][1] = l_run;
+        }
+        __syncthreads();
+        if (sub == 0 && rl < rows_b) {
+            float M = kNegInf;
+            for (int k = 0; k < wpr; ++k) M = fmaxf(M, xml[w + k][0]);
+            float L = 0.f, a[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) a[c] = 0.f;
+            if (M != kNegInf) {
+                for (int k = 0; k < wpr; ++k) {
+                    const float mk = xml[w + k][0];
+                    const float f = mk == kNegInf ? 0.f : __expf(mk - M);
+                    L += f * xml[w + k][1];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) a[c] += f != 0.f ? f * xacc[w + k][lane * 8 + c] : 0.f;
+                }
+            }
+            emit_row(rl, M, L, a);
+        }
+    } else {
+        // ---- form A
+        int base[4], cnt[4], S = 0;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            base[rr] = pbase[4 * w + rr];
+            cnt[rr] = pcnt[4 * w + rr];
+            S = max(S, cnt[rr]);
+        }
+        float acc[4][8], m_run[4], l_run[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            m_run[rr] = kNegInf;
+            l_run[rr] = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[rr][j] = 0.f;
+        }
+        // Per-row buffer resources over the row's partials and log-sum-exps: the
+        // offsets stay 32-bit and wave-uniform, and a piece past the row's count
+        // reads outside the range (zeros; its weight is selected away below).
+        __amdgpu_buffer_rsrc_t prs[4], lrs[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            prs[rr] = make_rsrc(part_o + (size_t)base[rr] * H * DC, cnt[rr] * H * DC * 2);
+            lrs[rr] = make_rsrc(part_lse + (size_t)base[rr] * H, cnt[rr] * H * 4);
+        }
+        for (int p0 = 0; p0 < S; p0 += CMB_CHUNK) {
+            u32x4 v[4][CMB_CHUNK];
+            float lv[4][CMB_CHUNK];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                for (int j = 0; j < CMB_CHUNK; ++j) {
+                    const int sp = p0 + j;
+                    v[rr][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             prs[rr], lane * 16, sp * (H * DC * 2) + h * (DC * 2), 0));
+                    lv[rr][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                              lrs[rr], 0, sp * (H * 4) + h * 4, 0));
+                }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                for (int j = 0; j < CMB_CHUNK; ++j)
+                    if (p0 + j >= cnt[rr]) lv[rr][j] = kNegInf;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                merge_into(m_run[rr], l_run[rr], acc[rr], v[rr], lv[rr], std::integral_constant<int, CMB_CHUNK>{});
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) emit_row(4 * w + rr, m_run[rr], l_run[rr], acc[rr]);
     }
     __syncthreads();
 
-    f32x16 oacc = {};
+    // ---- 2. out^T (16 values x 32 rows) of this wave: N-block nb = rows
+    // 16 nb .. +16; the B operand of K-step ks is row 16 nb + (lane % 16),
+    // latent columns 32 ks + 8 (lane / 16) .. +8, i.e. chunk 4 ks + lane / 16
+    f32x4 oacc[2] = {};
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) {
-        const int ch = 2 * ks + hf;
-        const int off = l32 * 1024 + ((ch ^ (l32 & 7)) << 4);
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&ol[0][off]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&ol[1][off]);
-        oacc = mfma32(wa[ks], bh, oacc);
-        oacc = mfma32(wa[ks], bl, oacc);
-    }
+    for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int rl = 16 * nb + (lane & 15), ch = 4 * ks + (lane >> 4);
+            const int off = rl * 1024 + ((ch ^ (rl & 7)) << 4);
+            const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&ol[0][off]);
+            const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&ol[1][off]);
+            oacc[nb] = mfma16(wa[ks], bh, oacc[nb]);
+            oacc[nb] = mfma16(wa[ks], bl, oacc[nb]);
+        }
     // out rows (32 rows x 128 values of head h) through LDS, so that each
-    // row's 256-byte segment is one contiguous store (a lane holds 8-byte
-    // pieces of 32 different rows)
+    // row's 256-byte segment is written by contiguous 16-byte stores: lane
+    // (g, n) holds values 16 w + 4 g .. +4 of row 16 nb + n
     constexpr int OROWB = 272;                  // bytes per staged output row
     __syncthreads();                            // every wave is done reading o_lat
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int nb = 0; nb < 2; ++nb) {
         const unsigned long long pk =
-            (unsigned long long)f32_to_bf16_bits(oacc[4 * g + 0]) |
-            ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 1]) << 16) |
-            ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 2]) << 32) |
-            ((unsigned long long)f32_to_bf16_bits(oacc[4 * g + 3]) << 48);
-        *reinterpret_cast<unsigned long long*>(&ol[0][l32 * OROWB + (w * 32 + 8 * g + 4 * hf) * 2]) = pk;
+            (unsigned long long)f32_to_bf16_bits(oacc[nb][0]) |
+            ((unsigned long long)f32_to_bf16_bits(oacc[nb][1]) << 16) |
+            ((unsigned long long)f32_to_bf16_bits(oacc[nb][2]) << 32) |
+            ((unsigned long long)f32_to_bf16_bits(oacc[nb][3]) << 48);
+        *reinterpret_cast<unsigned long long*>(
+            &ol[0][(16 * nb + (lane & 15)) * OROWB + (16 * w + 4 * (lane >> 4)) * 2]) = pk;
     }
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {               // 32 rows x 16 chunks, 2 per thread
-        const int i = k * 256 + tid, rl = i >> 4, c = i & 15;
-        const int r = rb * 32 + rl;
+    {                                           // 32 rows x 16 chunks, one per thread
+        const int rl = tid >> 4, c = tid & 15;
+        const int r = r0 + rl;
         if (r < R)
             *reinterpret_cast<u32x4*>(out + ((size_t)r * H + h) * 128 + c * 8) =
                 *reinterpret_cast<const u32x4*>(&ol[0][rl * OROWB + c * 16]);
@@ -1545,7 +1700,7 @@ hipError_t launch_decode_mfma(const DecodeLaunch& a, unsigned stages) {
     }
     if (stages & MLA_STAGE_COMBINE) {
         const int grid = H * ((R + 31) / 32);
-        combine_kernel<<<grid, 256, 0, a.stream>>>(static_cast<const unsigned short*>(a.part_o),
+        combine_kernel<<<grid, CMB_THREADS, 0, a.stream>>>(static_cast<const unsigned short*>(a.part_o),
                                                    a.part_lse, a.seq_lens, a.q_len, R, a.num_splits,
                                                    kNumCUs,
                                                    static_cast<const unsigned short*>(a.w_uv),
