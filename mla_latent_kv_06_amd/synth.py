@@ -33,7 +33,7 @@ import math
 import numpy as np
 
 # stream tags
-_LENGTHS, _BLOCKS, _CACHE, _QNOPE, _QPE, _WUK, _WUV, _H, _WKVA, _WDQ, _WUQ, _WQR, _QG = range(13)
+_LENGTHS, _BLOCKS, _CACHE, _QNOPE, _QPE, _WUK, _WUV, _H, _WKVA, _WDQ, _WUQ, _WQR, _QG, _WO = range(14)
 
 # query compression width of the DeepSeek-V3 shape (0 = full-rank queries)
 Q_LORA_RANK_V3 = 1536
@@ -212,6 +212,13 @@ def w_qr(wl: Workload, q_lora_rank: int, seed: int = 0) -> np.ndarray:
     """Query rotary projection [H * R, d_q] (or [H * R, d] at d_q = 0)."""
     f = _q_fan_in(wl, q_lora_rank)
     w = _normal(_rng(seed, _WQR), (wl.n_heads * wl.qk_rope_dim, f))
+    return w * np.float32(1.0 / math.sqrt(f))
+
+
+def w_o(wl: Workload, seed: int = 0) -> np.ndarray:
+    """Output projection [d, H * V]: column block h * V .. +V acts on head h."""
+    f = wl.n_heads * wl.v_head_dim
+    w = _normal(_rng(seed, _WO), (wl.d_model, f))
     return w * np.float32(1.0 / math.sqrt(f))
 
 

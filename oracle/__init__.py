@@ -15,6 +15,8 @@ Parity status of each public function (what pins it is listed in
 * ``decode_naive``           pinned (associativity, brute force, special cases)
 * ``decode_absorbed``        pinned (equals ``decode_naive`` to 1e-12 relative,
                              and the pure-Python brute force)
+* ``output_rows``            pinned (head-block selector, brute force, the
+                             merged W_O W_UV form of the same product)
 * ``round_to_bf16``          pinned (vs torch.bfloat16 on binary32 inputs, ties)
 * ``append_rows``            pinned (brute force, RMSNorm / RoPE invariants)
 * ``query_rows``             pinned (head-block layout, query/key relative
@@ -37,6 +39,7 @@ from .mla_ref import (  # noqa: F401
     gather_sequence,
     decode_naive,
     decode_absorbed,
+    output_rows,
     default_softmax_scale,
     round_to_bf16,
 )

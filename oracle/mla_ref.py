@@ -14,6 +14,9 @@ Sources, by page title and section:
 * "KV Compression -- DeepSeek-V3" (AI Engineer Exhaustive), "How it works":
   one linear map emits 512 latent channels followed by the 64-channel rotary
   key before rotation; the latent is RMS-normalised before it is cached.
+* "DeepSeek-V2: MLA Explained", "MLA Full Formulas", section 3 (last
+  equation): the heads' outputs, concatenated head after head, go through
+  one output projection W_O.
 * "HuggingFace version does NOT use efficient MLA caching" (DeepSeek-R1
   discussion), list item 2: cache the latent and the rotary key, rebuild full
   per-head keys and values at every step.  That "decompress" form is what
@@ -263,3 +266,21 @@ def decode_absorbed(q_nope, q_pe, w_uk, w_uv, seq_rows, q_len, softmax_scale=Non
             lse[b, s] = m + np.log(tot)
     return out, lse
 
+
+
+def output_rows(o, w_o):
+    """Output projection in float64: u = W_O [o_1; ...; o_H].
+
+    "DeepSeek-V2: MLA Explained", "MLA Full Formulas", section 3: per query
+    row, the H heads' outputs are concatenated head after head (a vector of
+    H * V values) and multiplied by W_O.
+
+    o [B, Sq, H, V] (a decode's output), w_o [d_model, H * V] whose columns
+    h * V .. (h + 1) * V act on head h.  Returns u [B, Sq, d_model]."""
+    o = np.asarray(o, dtype=np.float64)
+    w_o = np.asarray(w_o, dtype=np.float64)
+    B, Sq, H, V = o.shape
+    if w_o.ndim != 2 or w_o.shape[1] != H * V:
+        raise ValueError("w_o must be [d_model, H * V]")
+    concat = o.reshape(B, Sq, H * V)            # [o_1; ...; o_H] for every row
+    return concat @ w_o.T

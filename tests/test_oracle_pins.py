@@ -591,3 +591,61 @@ def test_query_rows_full_rank_is_the_direct_projection():
     pre = (h @ w_qr.T).reshape(T, H, R // 2, 2)
     np.testing.assert_allclose(np.linalg.norm(q_pe.reshape(T, H, R // 2, 2), axis=-1),
                                np.linalg.norm(pre, axis=-1), rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P8: the output projection u = W_O [o_1; ...; o_H]
+# --------------------------------------------------------------------------
+
+def test_p8_output_projection_block_selector_returns_one_head():
+    """W_O = [0 .. I_V .. 0] with the identity in head j's column block
+    gives back that head's output: the concatenation is head after head."""
+    rng = np.random.default_rng(41)
+    B, Sq, H, V = 2, 3, 4, 5
+    o = rng.standard_normal((B, Sq, H, V))
+    for j in range(H):
+        w = np.zeros((V, H * V))
+        w[:, j * V:(j + 1) * V] = np.eye(V)
+        np.testing.assert_array_equal(oracle.output_rows(o, w), o[:, :, j, :])
+
+
+def test_p8_output_projection_brute_force():
+    rng = np.random.default_rng(42)
+    B, Sq, H, V, d = 2, 2, 3, 4, 5
+    o = rng.standard_normal((B, Sq, H, V))
+    w = rng.standard_normal((d, H * V))
+    got = oracle.output_rows(o, w)
+    for b in range(B):
+        for s in range(Sq):
+            for k in range(d):
+                want = sum(w[k][h * V + v] * o[b][s][h][v] for h in range(H) for v in range(V))
+                assert abs(got[b, s, k] - want) < 1e-12
+
+
+def test_p8_output_projection_merged_weights_give_the_same_rows():
+    """The pages' merged form: W_UV folds into W_O, W_OV[:, h] = W_O[:, h] W_UV[h],
+    applied to the heads' attention-weighted latents.  The latents come from
+    the naive decode with identity value weights (V = d_c)."""
+    rng = np.random.default_rng(43)
+    qn, qp, wuk, wuv, rows = _rand_problem(rng, B=2, Sq=2, H=3, N=4, R=2, dc=6, V=5, L=(7, 9))
+    H, V, dc = wuv.shape
+    d = 8
+    w_o = rng.standard_normal((d, H * V))
+    o, _ = oracle.decode_naive(qn, qp, wuk, wuv, rows, 2)
+    u = oracle.output_rows(o, w_o)
+    eye = np.broadcast_to(np.eye(dc), (H, dc, dc))
+    o_lat, _ = oracle.decode_naive(qn, qp, wuk, eye, rows, 2)        # [B, Sq, H, dc]
+    w_ov = np.concatenate([w_o[:, h * V:(h + 1) * V] @ wuv[h] for h in range(H)], axis=1)
+    merged = o_lat.reshape(2, 2, H * dc) @ w_ov.T
+    np.testing.assert_allclose(u, merged, rtol=1e-12, atol=1e-12)
+
+
+def test_p8_output_projection_planted_mistakes_fail():
+    """A value-major concatenation (v outer, h inner) changes the rows."""
+    rng = np.random.default_rng(44)
+    B, Sq, H, V, d = 1, 2, 3, 4, 12
+    o = rng.standard_normal((B, Sq, H, V))
+    w = rng.standard_normal((d, H * V))
+    u = oracle.output_rows(o, w)
+    wrong_order = o.transpose(0, 1, 3, 2).reshape(B, Sq, H * V) @ w.T
+    assert np.max(np.abs(u - wrong_order)) > 1e-3
