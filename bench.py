@@ -153,6 +153,10 @@ def parse():
                         "prefill workload, e.g. v3_prefill_b2_8k_bf16, instead of the decode step")
     p.add_argument("--cpu-tokens", type=int, default=262144,
                    help="CPU-baseline sample: first sequences of layer 0 up to this many cached tokens")
+    p.add_argument("--output-study", action="store_true",
+                   help="instead: time the output side of the layer at the workload's rows: "
+                        "u = W_O o (W_O [d_model, H V]) against the merged-weight form "
+                        "u = (W_O W_UV) o_lat ([d_model, H d_c]), and the decode through W_O")
     p.add_argument("--report", default=None)
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="instead: copy a buffer of this many bytes 5 times (calibrates "
@@ -237,6 +241,9 @@ def main():
         return
     if args.prefill:
         prefill_main(args, torch, synth, b, dev)
+        return
+    if args.output_study:
+        output_study(args, torch, synth, b, dev)
         return
     wl = synth.WORKLOADS[args.workload]
     if wl.act_dtype != "bf16" or wl.cache_dtype not in ("bf16", "fp8"):
@@ -396,6 +403,71 @@ def main():
     if args.report:
         with open(args.report, "w") as f:
             json.dump(result, f, indent=1)
+
+
+def output_study(args, torch, synth, b, dev):
+    """The layer's output side at the workload's rows R = batch * q_len:
+      factored  u = W_O o,           W_O   [d_model, H V]   (mla_output_project)
+      merged    u = (W_O W_UV) o_lat, W_OV [d_model, H d_c] (the same GEMM, K = H d_c)
+    and one decode through W_O (mla_decode_output) against the decode alone.
+    Weights are random bf16 (timing does not depend on values); two W_O
+    copies alternate so that the 235 MB weight does not stay in the 256 MB
+    last-level cache.  One JSON line."""
+    wl = synth.WORKLOADS[args.workload]
+    R, H, V, dc, d = wl.batch * wl.q_len, wl.n_heads, wl.v_head_dim, wl.kv_lora_rank, wl.d_model
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    rnd = lambda *shape: (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * 0.01).to(bf)
+    w_o = [rnd(d, H * V) for _ in range(2)]
+    w_ov = rnd(d, H * dc)
+    o = rnd(R, H * V)
+    lat = rnd(R, H * dc)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, K):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(K):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / K / 1e3
+
+    K = max(4, args.steps)
+    ws = torch.empty(max(b.output_workspace_size(R, H * dc, d), b.output_workspace_size(R, H * V, d)),
+                     dtype=torch.uint8, device=dev)
+    outb = torch.empty(R, d, dtype=bf, device=dev)
+    fact_s = timed(lambda i: b.output_project(o, w_o[i & 1], out=outb, workspace=ws), K)
+    merged_s = timed(lambda i: b.output_project(lat, w_ov, out=outb, workspace=ws), max(4, K // 4))
+    fact_bytes = d * H * V * 2 + R * H * V * 2 + R * d * 2
+    merged_bytes = d * H * dc * 2 + R * H * dc * 2 + R * d * 2
+    # the decode alone against the decode through W_O, on one layer
+    layer = Layer(wl, 0, b.Dims.from_workload(wl), dev, torch, synth, b)
+    dims = b.Dims.from_workload(wl)
+    common = (dims, layer.q_nope, layer.q_pe, layer.w_uk, layer.w_uv, layer.pool, layer.scale,
+              layer.block_table, layer.seq_lens)
+    ws_d = torch.empty(b.decode_output_workspace_size(dims, wl.batch, wl.q_len, 0, d), dtype=torch.uint8,
+                       device=dev)
+    u = torch.empty(wl.batch, wl.q_len, d, dtype=bf, device=dev)
+    dec_s = timed(lambda i: b.decode(*common, out=layer.out, lse=layer.lse, workspace=ws_d), K)
+    dec_out_s = timed(lambda i: b.decode_output(*common, w_o[i & 1], u=u, lse=layer.lse, workspace=ws_d), K)
+    res = {
+        "study": "output side", "workload": wl.name, "rows": R, "d_model": d,
+        "factored_w_o": {"k": H * V, "bytes": fact_bytes, "us": round(fact_s * 1e6, 2),
+                         "gbs": round(fact_bytes / fact_s / 1e9, 1)},
+        "merged_w_ov": {"k": H * dc, "bytes": merged_bytes, "us": round(merged_s * 1e6, 2),
+                        "gbs": round(merged_bytes / merged_s / 1e9, 1)},
+        "decode_us": round(dec_s * 1e6, 2), "decode_through_w_o_us": round(dec_out_s * 1e6, 2),
+    }
+    log(f"W_O GEMM {fact_s * 1e6:.1f} us ({fact_bytes / 1e6:.0f} MB, {fact_bytes / fact_s / 1e9:.0f} GB/s); "
+        f"merged W_OV GEMM {merged_s * 1e6:.1f} us ({merged_bytes / 1e6:.0f} MB, "
+        f"{merged_bytes / merged_s / 1e9:.0f} GB/s); decode {dec_s * 1e6:.1f} us, "
+        f"decode through W_O {dec_out_s * 1e6:.1f} us")
+    print(json.dumps(res), flush=True)
 
 
 class PrefillLayer:

@@ -251,6 +251,51 @@ mla_status mla_decode_absorbed_noalloc(const mla_dims* dims, int32_t batch, int3
                                        const int32_t* seq_lens, int32_t num_splits,
                                        void* out, float* lse, void* stream);
 
+/* ---- output projection -----------------------------------------------------
+ *
+ * The layer's output side ("DeepSeek-V2: MLA Explained", "MLA Full Formulas",
+ * section 3): the heads' outputs of a query row, concatenated head after head,
+ * times W_O:  u = W_O [o_1; ...; o_H].
+ *
+ * mla_output_project: out[t][j] = sum_k w[j][k] x[t][k] for t < rows, j < n,
+ * bf16 operands, fp32 accumulation, bf16 result.  With x the decode's output
+ * [rows][n_heads][v_head_dim] read as [rows][n_heads * v_head_dim] and w = W_O
+ * [d_model][n_heads * v_head_dim] this is u.  (Any bf16 product of this form
+ * runs: e.g. the merged weights W_O W_UV [d_model][n_heads * kv_lora_rank]
+ * applied to the heads' attention-weighted latents.)
+ *  rows         0 .. 65536;  k a positive multiple of 64;  n a positive
+ *               multiple of 32;  rows * k * 2 and n * k * 2 below 2^31
+ *  x [rows][k], w [n][k], out [rows][n]: bf16, device, 16-byte aligned
+ *  workspace    device scratch of at least mla_output_workspace_size bytes
+ *               (fp32 partial sums of the depth-split product), 16-byte aligned
+ * The partial sums are added in a fixed order: results do not depend on
+ * scheduling.  Errors: MLA_ERR_BAD_SHAPE, MLA_ERR_NULL_POINTER,
+ * MLA_ERR_ALIGNMENT, MLA_ERR_WORKSPACE_TOO_SMALL; nothing is launched then. */
+mla_status mla_output_workspace_size(int32_t rows, int32_t k, int32_t n, size_t* bytes);
+mla_status mla_output_project(int32_t rows, int32_t k, int32_t n, const void* x, const void* w,
+                              void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step through the output projection: mla_decode_absorbed, whose
+ * output o [batch][q_len][n_heads][v_head_dim] stays in the workspace, then
+ * u = W_O [o_1; ...; o_H] as mla_output_project.
+ *  w_o   [d_model][n_heads * v_head_dim] bf16 (columns h * v_head_dim .. +
+ *        v_head_dim act on head h)
+ *  u     [batch][q_len][d_model] bf16
+ *  lse   as mla_decode_absorbed (or NULL)
+ * Other arguments as mla_decode_absorbed; act_dtype must be MLA_BF16,
+ * n_heads * v_head_dim a multiple of 64 and d_model a multiple of 32.
+ * workspace: at least mla_decode_output_workspace_size bytes. */
+mla_status mla_decode_output_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                            int32_t num_splits, int32_t d_model, size_t* bytes);
+mla_status mla_decode_output(const mla_dims* dims, int32_t batch, int32_t q_len,
+                             const void* q_nope, const void* q_pe,
+                             const void* w_uk, const void* w_uv,
+                             const void* cache_pool, const float* cache_scale,
+                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                             const int32_t* seq_lens, int32_t num_splits, int32_t d_model,
+                             const void* w_o, void* u, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* ---- query path ------------------------------------------------------------
  *
  * The decode's query inputs from the layer input ("DeepSeek-V2: MLA

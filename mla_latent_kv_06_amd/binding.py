@@ -39,7 +39,8 @@ EXPORTED = ("mla_status_string", "mla_last_error", "mla_cache_row_bytes",
             "mla_decode_default_splits", "mla_decode_workspace_size", "mla_decode_absorbed",
             "mla_decode_absorbed_stages", "mla_query_workspace_size", "mla_query_project",
             "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_stages",
-            "mla_decode_absorbed_noalloc")
+            "mla_decode_absorbed_noalloc", "mla_output_workspace_size", "mla_output_project",
+            "mla_decode_output_workspace_size", "mla_decode_output")
 
 
 class Dims(ctypes.Structure):
@@ -100,6 +101,15 @@ _lib.mla_query_project.argtypes = [_DP, _I, _I, _I, _I, _P, _P, _P, ctypes.c_flo
 _lib.mla_decode_absorbed_stages.restype = ctypes.c_int
 _lib.mla_decode_absorbed_stages.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I,
                                             _P, _P, _P, _SZ, ctypes.c_uint32, _P]
+_lib.mla_output_workspace_size.restype = ctypes.c_int
+_lib.mla_output_workspace_size.argtypes = [_I, _I, _I, ctypes.POINTER(_SZ)]
+_lib.mla_output_project.restype = ctypes.c_int
+_lib.mla_output_project.argtypes = [_I, _I, _I, _P, _P, _P, _P, _SZ, _P]
+_lib.mla_decode_output_workspace_size.restype = ctypes.c_int
+_lib.mla_decode_output_workspace_size.argtypes = [_DP, _I, _I, _I, _I, ctypes.POINTER(_SZ)]
+_lib.mla_decode_output.restype = ctypes.c_int
+_lib.mla_decode_output.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P,
+                                   _P, _P, _SZ, _P]
 
 _lib.mla_prefill_workspace_size.restype = ctypes.c_int
 _lib.mla_prefill_workspace_size.argtypes = [_DP, _I, _I, _I, ctypes.POINTER(_SZ)]
@@ -196,8 +206,9 @@ def _stream(device):
 
 
 def _decode_tensors(dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_table,
-                    seq_lens, out, lse, want_lse):
-    """Check the decode's tensors; create out (and lse) when not given."""
+                    seq_lens, out, lse, want_lse, need_out=True):
+    """Check the decode's tensors; create out (and lse) when not given
+    (need_out False: no out tensor at all)."""
     act = _TORCH_OF[dims.act_dtype]
     B, Sq = q_nope.shape[0], q_nope.shape[1]
     H, N, R = dims.n_heads, dims.qk_nope_dim, dims.qk_rope_dim
@@ -216,9 +227,10 @@ def _decode_tensors(dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, blo
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError(f"block_table shape {tuple(block_table.shape)}")
     _need(seq_lens, "seq_lens", (torch.int32,), (B,), dev)
-    if out is None:
-        out = torch.empty((B, Sq, H, V), dtype=act[0], device=dev)
-    _need(out, "out", act, (B, Sq, H, V), dev)
+    if need_out:
+        if out is None:
+            out = torch.empty((B, Sq, H, V), dtype=act[0], device=dev)
+        _need(out, "out", act, (B, Sq, H, V), dev)
     if lse is None and want_lse:
         lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
     if lse is not None:
@@ -265,6 +277,73 @@ def decode_noalloc(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale
         _ptr(seq_lens), num_splits, _ptr(out), _ptr(lse), _stream(dev))
     _check(st, "mla_decode_absorbed_noalloc")
     return out, lse
+
+
+def output_workspace_size(rows: int, k: int, n: int) -> int:
+    b = _SZ(0)
+    _check(_lib.mla_output_workspace_size(rows, k, n, ctypes.byref(b)), "mla_output_workspace_size")
+    return b.value
+
+
+def output_project(x, w, out=None, workspace=None):
+    """out = x W^T (mla_output_project): x [rows, k] and w [n, k] bf16 (x may
+    carry more leading axes, flattened to rows; its last axis is k).
+    Returns out [..., n] bf16."""
+    if x is None or w is None:
+        raise ValueError("x and w are required")
+    k = x.shape[-1]
+    rows = x.numel() // k if k else 0
+    n = w.shape[0]
+    dev = x.device
+    _need(x, "x", (torch.bfloat16,), None, dev)
+    _need(w, "w", (torch.bfloat16,), (n, k), dev)
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", (torch.bfloat16,), tuple(x.shape[:-1]) + (n,), dev)
+    ws_bytes = output_workspace_size(rows, k, n)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), None, dev)
+    _check(_lib.mla_output_project(rows, k, n, _ptr(x), _ptr(w), _ptr(out), _ptr(workspace),
+                                   workspace.numel(), _stream(dev)), "mla_output_project")
+    return out
+
+
+def decode_output_workspace_size(dims: Dims, batch: int, q_len: int, num_splits: int,
+                                 d_model: int) -> int:
+    b = _SZ(0)
+    _check(_lib.mla_decode_output_workspace_size(ctypes.byref(dims), batch, q_len, num_splits,
+                                                 d_model, ctypes.byref(b)),
+           "mla_decode_output_workspace_size")
+    return b.value
+
+
+def decode_output(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_table,
+                  seq_lens, w_o, num_splits: int = 0, u=None, lse=None, workspace=None,
+                  want_lse: bool = True):
+    """Decode then output projection (mla_decode_output): the decode's
+    arguments as for ``decode``, w_o [d_model, H * V] bf16.  Returns
+    (u [B, Sq, d_model] bf16, lse)."""
+    B, Sq, dev, _, lse = _decode_tensors(dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                                         block_table, seq_lens, None, lse, want_lse, need_out=False)
+    _need(w_o, "w_o", (torch.bfloat16,), None, dev)
+    if w_o.dim() != 2 or w_o.shape[1] != dims.n_heads * dims.v_head_dim:
+        raise ValueError(f"w_o shape {tuple(w_o.shape)}")
+    d_model = w_o.shape[0]
+    if u is None:
+        u = torch.empty((B, Sq, d_model), dtype=torch.bfloat16, device=dev)
+    _need(u, "u", (torch.bfloat16,), (B, Sq, d_model), dev)
+    ws_bytes = decode_output_workspace_size(dims, B, Sq, num_splits, d_model)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), None, dev)
+    st = _lib.mla_decode_output(
+        ctypes.byref(dims), B, Sq, _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+        _ptr(cache_pool), _ptr(cache_scale), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), num_splits, d_model, _ptr(w_o), _ptr(u), _ptr(lse), _ptr(workspace),
+        workspace.numel(), _stream(dev))
+    _check(st, "mla_decode_output")
+    return u, lse
 
 
 def prefill(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_table, seq_lens,

@@ -2,6 +2,7 @@
 // dispatch to the MFMA or portable kernels.  Every check runs on the host
 // before anything is enqueued.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -9,6 +10,7 @@
 #include <mutex>
 
 #include "internal.hpp"
+#include "output.hpp"
 #include "prefill.hpp"
 #include "query.hpp"
 
@@ -339,6 +341,80 @@ mla_status prefill_impl(const mla_dims* dims, int32_t batch, int32_t q_len, cons
     return ok();
 }
 
+// Output projection: shape checks shared by the sizing call and the entry point.
+mla_status check_output_shape(int32_t rows, int32_t k, int32_t n) {
+    if (rows < 0 || rows > 65536)
+        return fail(MLA_ERR_BAD_SHAPE, "rows=%d outside [0, 65536]", rows);
+    if (k < 64 || k % 64)
+        return fail(MLA_ERR_BAD_SHAPE, "k=%d must be a positive multiple of 64", k);
+    if (n < 32 || n % 32)
+        return fail(MLA_ERR_BAD_SHAPE, "n=%d must be a positive multiple of 32", n);
+    if ((long long)rows * k * 2 >= (1ll << 31) || (long long)n * k * 2 >= (1ll << 31))
+        return fail(MLA_ERR_BAD_SHAPE, "an output-projection operand exceeds 2 GiB");
+    return MLA_OK;
+}
+
+size_t output_ws_bytes(int32_t rows, int32_t k, int32_t n) {
+    const int kc = mla::output_splits(n, k, rows);
+    return align_up((size_t)kc * rows * n * 4, 256);
+}
+
+mla_status output_impl(int32_t rows, int32_t k, int32_t n, const void* x, const void* w, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (mla_status st = check_output_shape(rows, k, n); st != MLA_OK) return st;
+    if (rows == 0) return ok();
+    if (!x || !w || !out || !workspace)
+        return fail(MLA_ERR_NULL_POINTER, "x, w, out and workspace are required");
+    const void* ptrs[] = {x, w, out, workspace};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(MLA_ERR_ALIGNMENT, "tensor at %p is not 16-byte aligned", p);
+    const size_t need = output_ws_bytes(rows, k, n);
+    if (workspace_bytes < need)
+        return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu", workspace_bytes, need);
+    mla::OutputLaunch a;
+    a.T = rows;
+    a.K = k;
+    a.N = n;
+    a.x = x;
+    a.w = w;
+    a.out = out;
+    a.part = static_cast<float*>(workspace);
+    a.kc = mla::output_splits(n, k, rows);
+    a.stream = static_cast<hipStream_t>(stream);
+    const hipError_t e = mla::launch_output(a);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// Decode followed by the output projection: the decode's output o stays in
+// the workspace, after the decode's own scratch.
+struct DecodeOutputWs {
+    size_t decode, o, part, total;
+};
+
+DecodeOutputWs decode_output_ws(const mla_dims& d, int batch, int q_len, int num_splits, int d_model) {
+    DecodeOutputWs w;
+    const size_t R = (size_t)batch * q_len;
+    w.decode = 0;
+    w.o = align_up(decode_ws(d, batch, q_len, num_splits).total, 256);
+    w.part = w.o + align_up(R * d.n_heads * d.v_head_dim * 2, 256);
+    w.total = w.part + output_ws_bytes((int32_t)R, d.n_heads * d.v_head_dim, d_model);
+    return w;
+}
+
+mla_status check_decode_output_shape(const mla_dims* dims, int32_t batch, int32_t q_len, int32_t num_splits,
+                                     int32_t d_model) {
+    if (mla_status st = check_dims(dims); st != MLA_OK) return st;
+    if (dims->act_dtype != MLA_BF16)
+        return fail(MLA_ERR_UNSUPPORTED, "the output projection needs act_dtype MLA_BF16");
+    if (batch < 0 || q_len < 1 || q_len > 1024)
+        return fail(MLA_ERR_BAD_SHAPE, "batch=%d must be >= 0 and q_len=%d in [1, 1024]", batch, q_len);
+    if (num_splits < 0 || num_splits > mla::kMaxSplits)
+        return fail(MLA_ERR_BAD_SHAPE, "num_splits=%d outside [0, %d]", num_splits, mla::kMaxSplits);
+    return check_output_shape((int32_t)std::min<long long>((long long)batch * q_len, 65537),
+                              dims->n_heads * dims->v_head_dim, d_model);
+}
+
 // Scratch of mla_decode_absorbed_noalloc: one array per GPU (each device
 // holds its own copy), placed by the code object, never allocated by a call.
 // In host code `scratch` names a host-side stand-in; the device address comes
@@ -529,6 +605,52 @@ mla_status mla_decode_absorbed_noalloc(const mla_dims* dims, int32_t batch, int3
     return decode_impl(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
                        block_table, max_blocks_per_seq, seq_lens, num_splits, out, lse, ws,
                        MLA_NOALLOC_SCRATCH_BYTES, MLA_STAGE_ALL, stream);
+}
+
+mla_status mla_output_workspace_size(int32_t rows, int32_t k, int32_t n, size_t* bytes) {
+    if (mla_status st = check_output_shape(rows, k, n); st != MLA_OK) return st;
+    if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes is NULL");
+    *bytes = output_ws_bytes(rows, k, n);
+    return ok();
+}
+
+mla_status mla_output_project(int32_t rows, int32_t k, int32_t n, const void* x, const void* w, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    return output_impl(rows, k, n, x, w, out, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_decode_output_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                            int32_t num_splits, int32_t d_model, size_t* bytes) {
+    if (mla_status st = check_decode_output_shape(dims, batch, q_len, num_splits, d_model); st != MLA_OK)
+        return st;
+    if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes is NULL");
+    *bytes = decode_output_ws(*dims, batch, q_len, num_splits, d_model).total;
+    return ok();
+}
+
+mla_status mla_decode_output(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
+                             const void* q_pe, const void* w_uk, const void* w_uv, const void* cache_pool,
+                             const float* cache_scale, const int32_t* block_table,
+                             int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_splits,
+                             int32_t d_model, const void* w_o, void* u, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (mla_status st = check_decode_output_shape(dims, batch, q_len, num_splits, d_model); st != MLA_OK)
+        return st;
+    if (batch == 0) return ok();
+    if (!w_o || !u || !workspace) return fail(MLA_ERR_NULL_POINTER, "w_o, u and workspace are required");
+    const DecodeOutputWs ws = decode_output_ws(*dims, batch, q_len, num_splits, d_model);
+    if (workspace_bytes < ws.total)
+        return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu", workspace_bytes, ws.total);
+    char* base = static_cast<char*>(workspace);
+    void* o = base + ws.o;
+    if (mla_status st = decode_impl(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                                    block_table, max_blocks_per_seq, seq_lens, num_splits, o, lse,
+                                    base + ws.decode, ws.o - ws.decode, MLA_STAGE_ALL, stream);
+        st != MLA_OK)
+        return st;
+    const int32_t R = batch * q_len;
+    return output_impl(R, dims->n_heads * dims->v_head_dim, d_model, o, w_o, u, base + ws.part,
+                       ws.total - ws.part, stream);
 }
 
 mla_status mla_query_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,

@@ -218,3 +218,47 @@ def test_prefill_validation_rejects_before_launch(b):
     assert call(dims=b.Dims.make(64, 512, 64, 128, 128, 64, "bf16", "bf16")) == 3
     assert call(dims=b.Dims.make(128, 512, 64, 128, 128, 64, "fp8", "bf16", flags=1), scale=16) == 3
     assert call(batch=0) == 0
+
+
+def test_output_workspace_sizes(b):
+    # few rows: weight-streaming GEMM, depth split over 3 workgroups per output
+    # block for the V3 output projection (75 blocks of 96 outputs)
+    assert b.output_workspace_size(64, 16384, 7168) == 3 * 64 * 7168 * 4
+    # a prompt's rows: tile form, one slice
+    assert b.output_workspace_size(4096, 16384, 7168) == 4096 * 7168 * 4
+    d = v3_dims(b)
+    n = b.decode_output_workspace_size(d, 64, 1, 0, 7168)
+    dec = b.decode_workspace_size(d, 64, 1, 0)
+    assert n == dec + 64 * 16384 * 2 + 3 * 64 * 7168 * 4
+
+
+def test_output_validation_rejects_before_launch(b):
+    lib = b.lib()
+    P = ctypes.c_void_p
+    sz = ctypes.c_size_t(0)
+    assert lib.mla_output_workspace_size(4, 100, 64, ctypes.byref(sz)) == 2     # k % 64
+    assert lib.mla_output_workspace_size(4, 128, 48, ctypes.byref(sz)) == 2     # n % 32
+    assert lib.mla_output_workspace_size(-1, 128, 64, ctypes.byref(sz)) == 2
+    assert lib.mla_output_workspace_size(4, 1 << 16, 1 << 15, ctypes.byref(sz)) == 2   # > 2 GiB
+    assert lib.mla_output_workspace_size(4, 128, 64, None) == 1
+    ok = dict(rows=4, k=128, n=64, x=16, w=16, out=16, ws=16, ws_bytes=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        Pn = lambda v: None if v is None else P(v)
+        return lib.mla_output_project(a["rows"], a["k"], a["n"], Pn(a["x"]), Pn(a["w"]), Pn(a["out"]),
+                                      Pn(a["ws"]), a["ws_bytes"], None)
+    assert call(x=None) == 1
+    assert call(w=24) == 4
+    assert call(ws_bytes=8) == 5
+    assert call(rows=0, x=None) == 0                              # nothing to do
+    d = v3_dims(b)
+    assert lib.mla_decode_output_workspace_size(ctypes.byref(d), 64, 1, 0, 7000,
+                                                ctypes.byref(sz)) == 2     # d_model % 32
+    f32 = b.Dims.make(128, 512, 64, 128, 128, 64, "bf16", "f32")
+    assert lib.mla_decode_output_workspace_size(ctypes.byref(f32), 64, 1, 0, 7168,
+                                                ctypes.byref(sz)) == 3     # bf16 only
+    Pn = lambda v: None if v is None else P(v)
+    args = [ctypes.byref(d), 2, 1] + [Pn(16)] * 5 + [None, Pn(16), 4, Pn(16), 0, 7168]
+    assert lib.mla_decode_output(*args, None, Pn(16), None, Pn(16), 1 << 40, None) == 1   # no w_o
+    assert lib.mla_decode_output(*args, Pn(16), Pn(16), None, Pn(16), 10, None) == 5
