@@ -609,6 +609,7 @@ def prefill_cpu_baseline(wl, L, torch, n_q=8192, heads=tuple(range(16))):
     query seeing its causal prefix; the rate is scaled to whole prompt tokens
     (all heads).  Also checks the GPU output on that sample."""
     import oracle
+    from mla_latent_kv_06_amd import layout
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -618,7 +619,7 @@ def prefill_cpu_baseline(wl, L, torch, n_q=8192, heads=tuple(range(16))):
     f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
     nb = (n_q + wl.block_size - 1) // wl.block_size
     ids = torch.from_numpy(L.table_host[0, :nb].astype(np.int64)).to(L.pool.device)
-    blocks = L.pool.index_select(0, ids).view(-1, wl.row_width)
+    blocks = layout.pool_rows(L.pool.index_select(0, ids), wl.cache_dtype)     # token rows
     if wl.cache_dtype == "fp8":
         rows64 = oracle.dequantize_rows_fp8(blocks.cpu().numpy(),
                                             L.scale.index_select(0, ids).reshape(-1).cpu().numpy())
@@ -649,6 +650,7 @@ def cpu_baseline(args, wl, L, torch):
     workload: the first sequences of layer 0 up to --cpu-tokens cached tokens, all heads, read back
     from the device.  Also checks the GPU output for those sequences."""
     import oracle
+    from mla_latent_kv_06_amd import layout
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -669,7 +671,7 @@ def cpu_baseline(args, wl, L, torch):
         # oracle's own gather over a compact table
         nb = (int(L.seq_lens_host[i]) + wl.block_size - 1) // wl.block_size
         ids = torch.from_numpy(L.table_host[i, :nb].astype(np.int64)).to(L.pool.device)
-        blocks = L.pool.index_select(0, ids).view(-1, D)
+        blocks = layout.pool_rows(L.pool.index_select(0, ids), wl.cache_dtype)  # token rows
         if wl.cache_dtype == "fp8":
             codes = blocks.cpu().numpy()
             sc = L.scale.index_select(0, ids).reshape(-1).cpu().numpy()

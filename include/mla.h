@@ -34,7 +34,8 @@
  *
  * Conventions for every entry point:
  *
- *  - All tensors are dense, row-major, in device memory owned by the caller.
+ *  - All tensors are dense, row-major (the cache pool's blocks: see
+ *    mla_cache_block_bytes), in device memory owned by the caller.
  *    The library allocates nothing and keeps no state between calls; every
  *    call is reentrant.  Buffers must stay alive until `stream` passes the
  *    enqueued work.
@@ -114,7 +115,16 @@ const char* mla_last_error(void);
 size_t mla_cache_row_bytes(const mla_dims* dims);
 
 /* Bytes of one cache block: block_size * mla_cache_row_bytes(dims).  The pool
- * is an array of these, [num_blocks][block_size][kv_lora_rank + qk_rope_dim].
+ * is an array of these, num_blocks blocks of block_size * D elements
+ * (D = kv_lora_rank + qk_rope_dim).  Inside a block:
+ *  - FP8_E4M3 and F32 caches are token-major: token t's row at t * D;
+ *  - BF16 caches hold sub-blocks of sub = 32 tokens (sub = block_size when
+ *    block_size is not a multiple of 32), each channel-major: element
+ *    (token t, channel c) at ((t / sub) * D + c) * sub + t % sub.  The
+ *    decode's value product then reads 8 consecutive tokens of one latent
+ *    channel as one 16-byte unit.
+ * Only the library's own calls (mla_cache_append) need to write a pool; the
+ * layout matters to callers that fill or read pools themselves.
  * With FP8_E4M3 the per-token fp32 scales live in a separate array
  * cache_scale[num_blocks][block_size]. */
 size_t mla_cache_block_bytes(const mla_dims* dims);
@@ -133,7 +143,8 @@ mla_status mla_cache_append_workspace_size(const mla_dims* dims, int32_t batch,
  *  rope_base     RoPE base (10000 for DeepSeek)
  *  block_table   [batch][max_blocks_per_seq] int32, device
  *  start_pos     [batch] int32, device: position of sequence b's first new token
- *  cache_pool    [num_blocks][block_size][kv_lora_rank + qk_rope_dim] cache_dtype
+ *  cache_pool    [num_blocks][block_size * (kv_lora_rank + qk_rope_dim)] cache_dtype
+ *                (block layout: see mla_cache_block_bytes)
  *  cache_scale   [num_blocks][block_size] float, FP8_E4M3 only (else NULL):
  *                receives amax/448 of each written row; the row holds
  *                round-to-nearest-even(x / scale), saturated to +-448
@@ -175,7 +186,8 @@ enum {
  *  q_pe         [batch][q_len][n_heads][qk_rope_dim] act_dtype, already rotated
  *  w_uk         [n_heads][qk_nope_dim][kv_lora_rank] act_dtype (k^C = W_UK[i] c^)
  *  w_uv         [n_heads][v_head_dim][kv_lora_rank]  act_dtype (v^C = W_UV[i] c^)
- *  cache_pool   [num_blocks][block_size][kv_lora_rank + qk_rope_dim] cache_dtype
+ *  cache_pool   [num_blocks][block_size * (kv_lora_rank + qk_rope_dim)] cache_dtype
+ *               (block layout: see mla_cache_block_bytes)
  *  cache_scale  [num_blocks][block_size] float (FP8_E4M3 only, else NULL):
  *               a cached value is float(code) * scale of its token
  *  block_table  [batch][max_blocks_per_seq] int32, device

@@ -197,7 +197,12 @@ __global__ __launch_bounds__(256) void append_finalize(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int o = tid + 256 * u;
-            if (o < Dout) store_act<CDT>(pool, phys * Dout + o, yo[u]);
+            if (o < Dout) {
+                if constexpr (CDT == MLA_BF16)
+                    store_act<CDT>(pool, bf16_cache_offset(phys, o, Dout, BSZ), yo[u]);
+                else
+                    store_act<CDT>(pool, phys * Dout + o, yo[u]);
+            }
         }
     }
 }

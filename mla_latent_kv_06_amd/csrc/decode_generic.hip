@@ -17,12 +17,12 @@ constexpr int MAX_PER_THREAD = 4;     // latent columns per thread (d_c <= 1024)
 
 template <int CDT>
 __device__ __forceinline__ float cache_val(const void* pool, const float* pscale, size_t phys,
-                                           int D, int c) {
+                                           int D, int c, int bs) {
     if constexpr (CDT == MLA_FP8_E4M3) {
         const unsigned char code = static_cast<const unsigned char*>(pool)[phys * D + c];
         return e4m3_to_f32(code) * pscale[phys];
     } else if constexpr (CDT == MLA_BF16) {
-        return bf16_bits_to_f32(static_cast<const unsigned short*>(pool)[phys * D + c]);
+        return bf16_bits_to_f32(static_cast<const unsigned short*>(pool)[bf16_cache_offset(phys, c, D, bs)]);
     } else {
         return static_cast<const float*>(pool)[phys * D + c];
     }
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(NT) void g_split(
             const size_t phys = (size_t)btab[j / BSZ] * BSZ + (size_t)(j % BSZ);
             prow[threadIdx.x] = (long long)phys;
             float dot = 0.f;
-            for (int c = 0; c < D; ++c) dot += q[c] * cache_val<CDT>(pool, pscale, phys, D, c);
+            for (int c = 0; c < D; ++c) dot += q[c] * cache_val<CDT>(pool, pscale, phys, D, c, BSZ);
             sc = dot * scale;
         }
         const float cmax = block_max(sc, red);
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(NT) void g_split(
 #pragma unroll
             for (int k = 0; k < MAX_PER_THREAD; ++k) {
                 const int c = threadIdx.x + k * NT;
-                if (c < DC) acc[k] += pj * cache_val<CDT>(pool, pscale, phys, D, c);
+                if (c < DC) acc[k] += pj * cache_val<CDT>(pool, pscale, phys, D, c, BSZ);
             }
         }
         __syncthreads();

@@ -385,6 +385,10 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const int* __restrict__ seq_lens, int R, int q_len, int num_splits, float scale_log2,
     unsigned short* __restrict__ part_o,          // [slots][H][512] fp16
     float* __restrict__ part_lse) {               // [slots][H]
+    // Only the fp8 cache runs here: a bf16 cache runs on split_kv_ring_kernel,
+    // which reads the channel-major bf16 blocks.  (The FP8 = false branches
+    // below, which read token-major bf16 tiles, are never instantiated.)
+    static_assert(FP8, "split_kv_kernel serves the fp8 cache");
     // bf16: two tiles + the rotary queries of all heads (16 KB) = 160 KiB;
     // fp8: one bf16 tile + two fp8 staging tiles with scales (rotary queries in VGPRs)
     constexpr bool QPE_LDS = !FP8;
@@ -772,10 +776,16 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
 //    and forms those heads' softmax weights P;
 //  - values: wave w owns latent columns 128w .. 128w+127 of all 128 heads:
 //      O^T (128 cols x 128 heads) += V^T (128 x 32) . P^T          32 MFMA
-//    with every head block's weights read from LDS.  Each transposed value
-//    fragment then feeds four MFMAs (one per head block): the transposing
-//    LDS reads, which slow down sharply while the copies land in LDS, drop
-//    to a quarter of what the head split needs.
+//    with every head block's weights read from LDS.  Each value fragment
+//    then feeds four MFMAs (one per head block).
+// The cache's bf16 blocks are channel-major in sub-blocks of 32 tokens (one
+// half-tile: 576 channel rows of 64 bytes), so the value operand -- 8
+// consecutive tokens of one latent channel -- is one 16-byte LDS read, and
+// the score operand -- 8 channels of one token -- comes from the transposing
+// 8-byte reads.  Measured on MI355X, 8-byte LDS reads (transposing or not)
+// run at about half speed while buffer-to-LDS copies land, 16-byte reads
+// barely slow down; the copies issued during S land during V, so V, which
+// has the most LDS reads per MFMA, gets the 16-byte ones.
 // Loop iteration h (half h of the piece) runs, per wave:
 //   S_{h+1} (36 MFMA, with the copy of half h+3: 9 instructions)
 //   V_h     (32 MFMA, with the softmax of S_{h+1} threaded between them;
@@ -789,35 +799,46 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
 // weights P_h are in LDS, and every wave is done with half h-1, whose slot
 // the copy of h+3 reuses, and with the weights of h-1, whose buffer P_{h+1}
 // reuses.
-constexpr int HROWS = 32;                 // rows per half-tile
+constexpr int HROWS = 32;                 // tokens per half-tile (= the cache's sub-block)
 constexpr int HALF = HROWS * ROWB;        // 36864 bytes
 constexpr int NRING = 4;                  // ring slots
 constexpr int PBUF = 4 * 2 * 1024;        // weights of one half: 4 head blocks x 2 K-steps x 1 KB
+static_assert(HROWS == kCacheSub, "a half-tile is one channel-major sub-block of the cache");
 
-// LDS position of chunk c of row t (< 32) in a half-tile slot: the tile
-// layout above with 256 positions per group of 8 chunks.
-__device__ __forceinline__ int hpos(int t, int c) {
-    return ((c >> 3) << 8) + (t << 3) + ((c & 7) ^ fswz(t));
-}
+// Half-tile layout in LDS.  Channel row ch (64 bytes: 4 chunks of 8 tokens)
+// keeps its chunk c at 16-byte slot 4 ch + (c ^ hswz(ch)), hswz(ch) =
+// bit2(ch) | bit1(ch) << 1.  With 32 or 64 banks, the value operand's 16-byte
+// reads (8 consecutive rows, one chunk) and the score operand's transposing
+// 8-byte reads (16 lanes: 4 consecutive rows x 4 groups of 4 tokens) fall on
+// distinct banks; each copy instruction still moves 1 KB that is contiguous
+// in memory (16 channel rows).
+__device__ __forceinline__ int hswz(int ch) { return ((ch >> 2) & 1) | (((ch >> 1) & 1) << 1); }
 
 // Copy instruction k (0..8) of wave w for one half-tile: instruction
-// i = 9 w + k = 4 cg + q fills positions 64 i .. 64 i + 63, i.e. rows
-// 8q .. 8q+7 of chunk group cg; lane l takes row 8q + l/8, slot l%8, i.e.
-// chunk 8 cg + ((l%8) ^ g(8q + l/8)), and g(8q + u) = g(u) ^ 2 (q & 1).
+// i = 9 w + k fills slots 64 i .. 64 i + 63, i.e. channel rows 16 i .. +16;
+// lane l takes row 16 i + l/4, slot l%4, i.e. chunk (l%4) ^ hswz(l/4) of it
+// (16 i leaves bits 1 and 2 of the row to l/4), at byte 1024 i + 64 (l/4) +
+// 16 chunk of the sub-block.
 __device__ __forceinline__ void issue_half_part(__amdgpu_buffer_rsrc_t rsrc, lds_u8* slot, int w,
                                                 int lane, int k) {
-    const int i = w * 9 + k, cg = i >> 2, q = i & 3;
-    const unsigned off0 = (lane >> 3) * ROWB + (((lane & 7) ^ fswz(lane >> 3)) << 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(slot + i * 1024), 16,
-                                             (q & 1) ? (off0 ^ 32u) : off0, q * 8 * ROWB + cg * 128,
+    const int i = w * 9 + k;
+    const unsigned off = (lane >> 2) * 64 + (((lane & 3) ^ hswz(lane >> 2)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(slot + i * 1024), 16, off, i * 1024,
                                              0, 0);
 }
 
-// Zero rows valid .. 31 of a half-tile slot (their cache slots hold no token).
-__device__ __forceinline__ void zero_half_rows(lds_u8* slot, int valid, int tid) {
-    for (int p = valid * NCH + tid; p < HROWS * NCH; p += 256) {
-        const int t = p / NCH, c = p - t * NCH;
-        *reinterpret_cast<MLA_LDS u32x4*>(slot + hpos(t, c) * 16) = u32x4{0, 0, 0, 0};
+// Zero tokens valid .. 31 of a half-tile slot's latent rows (their cache
+// slots hold no token; the value product must not meet NaN there).
+__device__ __forceinline__ void zero_half_tokens(lds_u8* slot, int valid, int tid) {
+    for (int p = tid; p < DC * 4; p += 256) {
+        const int ch = p >> 2, c = p & 3;
+        if (8 * c + 8 <= valid) continue;
+        MLA_LDS u16x8* q = reinterpret_cast<MLA_LDS u16x8*>(slot + (4 * ch + (c ^ hswz(ch))) * 16);
+        u16x8 v = *q;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (8 * c + e >= valid) v[e] = 0;
+        *q = v;
     }
 }
 
@@ -982,35 +1003,38 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
         issue_half(hfirst + 2);
         bool first_in_flight = true;
 
-        // Per-lane LDS byte offsets.  Score operand (chunk 2 ks + hf of row
-        // l32): by ks % 4.  Transposed value reads (in a 16-lane group, lane
-        // 4r + b reads row 4 hf + r (+8), channels 4b .. 4b+3 of a 16-channel
-        // block): by cm % 2 and by the +8 row offset.
-        int qk_off[4], tr_off[2][2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) qk_off[j] = (l32 * 8 + ((2 * j + hf) ^ fswz(l32 & 15))) * 16;
+        // Per-lane LDS byte offsets.
+        // Score operand of K-step ks (channels 16 ks + 8 hf .. +8 of one token
+        // per lane), two transposing reads (channels +0..3, +4..7): in
+        // 16-lane group g, lane j = 4 r + b points at channel row
+        // 16 ks + 8 hf + 4 e + r and 4 tokens 16 (g & 1) + 4 perm(b), and
+        // receives token 16 (g & 1) + 4 perm(j / 4) + j % 4 -- the MFMA row
+        // l32 with bits 2 and 3 exchanged (perm(b) exchanges b's two bits).
+        // So the scores' accumulator row m holds token m with bits 2 and 3
+        // exchanged: lane (hf, l32) ends up with tokens 16 (i/8) + 8 hf + i%8
+        // in sv[i], the order in which the value operand reads them.
+        int s_off[2], v_off[2];
         {
-            const int r = (lane & 15) >> 2, g1 = (lane >> 4) & 1, b1 = (lane >> 1) & 1;
+            const int j = lane & 15, r = j >> 2, b = j & 3;
+            const int tq = 4 * ((lane >> 4) & 1) + (((b & 1) << 1) | (b >> 1));   // 4-token group
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int t = 8 * e + 4 * hf + r;      // row within a 16-row group
-                    tr_off[j][e] = (t * 8 + ((4 * j + 2 * g1 + b1) ^ fswz(t))) * 16 + (lane & 1) * 8;
-                }
+            for (int e = 0; e < 2; ++e) {
+                const int row = 8 * hf + 4 * e + r;
+                s_off[e] = row * 64 + (((tq >> 1) ^ hswz(row)) << 4) + (tq & 1) * 8;
+            }
         }
-        // score operand of K-step ks (rows l32 of the slot at sbase)
+        // Value operand: V^T for latent channels 32 cm + l32, K-step k2:
+        // tokens 16 k2 + 8 hf .. +8, one chunk of the channel row.
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) v_off[k2] = l32 * 64 + (((2 * k2 + hf) ^ hswz(l32)) << 4);
         auto k_frag = [&](const lds_u8* sbase, int ks) __attribute__((always_inline)) -> bf16x8 {
-            return *reinterpret_cast<const MLA_LDS bf16x8*>(sbase + qk_off[ks & 3] + (ks >> 2) * 4096);
-        };
-        // value operand: V^T for latent columns 32 cm .. +32, K-step k2 (tokens
-        // 16 k2 + {0..3, 8..11} in lanes 0-31 and {4..7, 12..15} in lanes
-        // 32-63, the weights' layout)
-        auto v_frag = [&](const lds_u8* vbase, int cm, int k2) __attribute__((always_inline)) -> bf16x8 {
-            const lds_u8* vb = vbase + (cm >> 1) * 4096 + k2 * 16 * 128;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + tr_off[cm & 1][0]));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + tr_off[cm & 1][1]));
+            const lds_u8* kb = sbase + ks * 1024;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(kb + s_off[0]));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(kb + s_off[1]));
             return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        auto v_frag = [&](const lds_u8* vbase, int cm, int k2) __attribute__((always_inline)) -> bf16x8 {
+            return *reinterpret_cast<const MLA_LDS bf16x8*>(vbase + cm * 2048 + v_off[k2]);
         };
         // weights of head block hb, K-step k2, as the MFMA B operand: 1 KB,
         // lane l at 16 l
@@ -1035,7 +1059,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
         int mode = 0;                        // 0: first-half reference, 1: max scan, 2: exact reference
 
         // scores of one half, unscaled, in VGPRs: lane (hf, l32) holds head
-        // 32 w + l32, rows 8 (i/4) + 4 hf + (i%4) of the half
+        // 32 w + l32, tokens 16 (i/8) + 8 hf + i%8 of the half in sv[i]
         float sv[16];
         bf16x8 pw[2];                        // this wave's weights of a half, per value K-step
         float hmax = kNegInf, psum = 0.f;
@@ -1060,7 +1084,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
                 constexpr int g = k + 4;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (8 * g + j >= sv_valid - 4 * hf) sv[4 * g + j] = kNegInf;
+                    if (16 * (g >> 1) + 4 * (g & 1) + j >= sv_valid - 8 * hf) sv[4 * g + j] = kNegInf;
             }
             if constexpr (k == 1) {
                 mx[0] = max3f(sv[0], sv[1], sv[2]);
@@ -1208,7 +1232,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
             if (first) barrier_landed_but_18();
             else barrier_landed_but_9();
             if (valid_half(h) < HROWS) {     // the last, partial half of the sequence
-                zero_half_rows((lds_u8*)slot_of(h), valid_half(h), tid);
+                zero_half_tokens((lds_u8*)slot_of(h), valid_half(h), tid);
                 __syncthreads();
             }
         };
@@ -1231,13 +1255,13 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
             if (mode == 0) {
                 // the reference: the first half's maximum over both lanes of each
                 // head (rows past the sequence end excluded)
-                // (row 8 (i/4) + 4 hf + i%4 of the half: a constant against a
-                // per-lane limit, so no per-element row index stays live)
+                // (token 16 (i/8) + 8 hf + i%8 of the half: a constant against a
+                // per-lane limit, so no per-element token index stays live)
                 float mx0 = kNegInf;
-                const int lim = sv_valid - 4 * hf;
+                const int lim = sv_valid - 8 * hf;
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if ((i >> 2) * 8 + (i & 3) < lim) mx0 = fmaxf(mx0, sv[i]);
+                    if ((i >> 3) * 16 + (i & 7) < lim) mx0 = fmaxf(mx0, sv[i]);
                 mx0 *= scale_log2;
                 m_ref = fmaxf(mx0, __shfl_xor(mx0, 32, 64));
             }

@@ -101,14 +101,20 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(
     const size_t row0 = (size_t)b * Tpad + (size_t)k * PBS;
     const int tid = threadIdx.x;
     if (!fp8) {
-        const unsigned char* src = pool + (size_t)blk * PBS * (PDC + PDR) * 2;
-        for (int p = tid; p < PBS * 72; p += 256) {          // 72 16-byte chunks per row
-            const int r = p / 72, c = p - r * 72;
+        // The block's two 32-token sub-blocks are channel-major (channel rows
+        // of 32 tokens): thread p takes token r = p % 64 and 8 channels
+        // 8 c .. +8, so the 2-byte reads of consecutive threads are adjacent
+        // tokens of one channel row, and writes token r's 16 bytes.
+        const unsigned short* src = reinterpret_cast<const unsigned short*>(pool) + (size_t)blk * PBS * (PDC + PDR);
+        for (int p = tid; p < PBS * 72; p += 256) {          // 72 chunks of 8 channels per token
+            const int r = p & (PBS - 1), c = p / PBS;
             const int t = k * PBS + r;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (t < len) v = *reinterpret_cast<const u32x4*>(src + ((size_t)r * 72 + c) * 16);
+            const unsigned short* col = src + ((size_t)(r / kCacheSub) * (PDC + PDR) + c * 8) * kCacheSub + r % kCacheSub;
+            u16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = t < len ? col[e * kCacheSub] : (unsigned short)0;
             unsigned short* dst = c < 64 ? x + (row0 + r) * PDC + c * 8 : kr + (row0 + r) * PDR + (c - 64) * 8;
-            *reinterpret_cast<u32x4*>(dst) = v;
+            *reinterpret_cast<u16x8*>(dst) = v;
         }
         return;
     }

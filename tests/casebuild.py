@@ -9,7 +9,9 @@ the oracle's float64 functions, then stored in the cache dtype:
 * f32:  float32.
 
 Unused pool slots and spare blocks are poisoned with NaN so a kernel that
-reads outside the visible tokens shows it.
+reads outside the visible tokens shows it.  Pools are held in the library's
+layout (``mla_latent_kv_06_amd.layout``: bf16 blocks channel-major in
+sub-blocks of 32 tokens); ``Case.rows`` gives token rows.
 """
 
 from __future__ import annotations
@@ -21,7 +23,7 @@ import numpy as np
 import torch
 
 import oracle
-from mla_latent_kv_06_amd import synth
+from mla_latent_kv_06_amd import layout, synth
 
 RMS_EPS = 1e-6
 ROPE_BASE = 10000.0
@@ -66,7 +68,7 @@ class Case:
     seq_lens: np.ndarray        # [B] int32 decode lengths (cached + q_len)
     block_table: np.ndarray     # [B, max_blocks] int32
     num_blocks: int
-    pool: np.ndarray            # [num_blocks, bs, D] uint16 (bf16) | uint8 (fp8) | float32
+    pool: np.ndarray            # [num_blocks, bs, D] uint16 (bf16) | uint8 (fp8) | float32, library layout
     scale: np.ndarray | None    # [num_blocks, bs] float32 (fp8 only)
     q_nope: np.ndarray          # stored dtype
     q_pe: np.ndarray
@@ -78,15 +80,18 @@ class Case:
     gamma: np.ndarray | None = None
 
     # ---- float64 views of what the device holds -------------------------
+    def rows(self, pool=None) -> np.ndarray:
+        """Token rows [num_blocks * bs, D] of a pool in the library layout."""
+        return layout.pool_rows(self.pool if pool is None else pool, self.wl.cache_dtype)
+
     def pool_rows_f64(self, pool=None, scale=None) -> np.ndarray:
-        pool = self.pool if pool is None else pool
         scale = self.scale if scale is None else scale
-        D = self.wl.row_width
+        raw = self.rows(pool)
         if self.wl.cache_dtype == "bf16":
-            return oracle.bf16_bits_to_f64(pool.reshape(-1, D))
+            return oracle.bf16_bits_to_f64(raw)
         if self.wl.cache_dtype == "fp8":
-            return oracle.dequantize_rows_fp8(pool.reshape(-1, D), scale.reshape(-1))
-        return pool.reshape(-1, D).astype(np.float64)
+            return oracle.dequantize_rows_fp8(raw, scale.reshape(-1))
+        return raw.astype(np.float64)
 
     def seq_rows(self, b: int, pool=None, scale=None, length=None) -> np.ndarray:
         rows = self.pool_rows_f64(pool, scale)
@@ -153,6 +158,7 @@ def build_case(wl: synth.Workload, seed: int = 0, fill=None, seq_lens_override=N
     # sequences own disjoint slots, and numpy drops the GIL in the heavy steps
     with concurrent.futures.ThreadPoolExecutor(min(8, max(1, len(fill)))) as ex:
         list(ex.map(write, fill))
+    pool = layout.rows_to_pool(flat, bs, wl.cache_dtype)      # token rows -> library layout
     case = Case(
         wl=wl, seed=seed, cached=cached, seq_lens=seq_lens, block_table=table,
         num_blocks=num_blocks, pool=pool, scale=scale,

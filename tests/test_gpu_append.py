@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from mla_latent_kv_06_amd import synth
+from mla_latent_kv_06_amd import layout, synth
 from tests import casebuild
 from tests.casebuild import build_case, error_stats
 
@@ -55,8 +55,11 @@ def run_append(case):
 
 
 def check_untouched(before, after, slots, D):
-    b = before.reshape(-1, D)
-    a = after.reshape(-1, D)
+    """Token rows of the pools (library layout: uint16 pools are bf16) equal
+    except at ``slots``; returns the rows at ``slots`` after."""
+    kind = "bf16" if before.dtype == np.uint16 else "token-major"
+    b = layout.pool_rows(before, kind).reshape(-1, D)
+    a = layout.pool_rows(after, kind).reshape(-1, D)
     mask = np.ones(len(b), dtype=bool)
     mask[slots] = False
     assert np.array_equal(a[mask].view(np.uint8), b[mask].view(np.uint8))

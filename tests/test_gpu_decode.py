@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 import torch
 
-from mla_latent_kv_06_amd import synth
+from mla_latent_kv_06_amd import layout, synth
 from tests import casebuild
 from tests.casebuild import build_case, error_stats
 
@@ -184,7 +184,7 @@ def _restart_case(cache_dtype):
     wl = MID.replace(name="v3_restart", batch=2, ctx_lo=300, ctx_hi=300, cache_dtype=cache_dtype)
     case = build_case(wl)
     D, dc = wl.row_width, wl.kv_lora_rank
-    flat = case.pool.reshape(-1, D)
+    flat = np.array(case.rows())                    # token rows (a copy), written back below
     sflat = None if case.scale is None else case.scale.reshape(-1)
     for b in range(wl.batch):
         L = int(case.seq_lens[b])
@@ -198,6 +198,7 @@ def _restart_case(cache_dtype):
                 row[dc:] *= 60.0
                 codes, sc = casebuild.oracle.quantize_rows_fp8(row[None])
                 flat[p], sflat[p] = codes[0], sc[0]
+    case.pool[...] = layout.rows_to_pool(flat, wl.block_size, cache_dtype)
     return case
 
 

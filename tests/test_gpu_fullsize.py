@@ -55,7 +55,7 @@ def seq_rows_f64(case, b, pool, scale):
     L = int(case.seq_lens[b])
     j = np.arange(L)
     phys = case.block_table[b, j // bs].astype(np.int64) * bs + j % bs
-    raw = pool.reshape(-1, D)[phys]
+    raw = case.rows(pool)[phys]
     if wl.cache_dtype == "bf16":
         return oracle.bf16_bits_to_f64(raw)
     return oracle.dequantize_rows_fp8(raw, scale.reshape(-1)[phys])
