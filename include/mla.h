@@ -67,7 +67,9 @@ typedef enum {
     MLA_ERR_UNSUPPORTED = 3,         /* dims / dtype combination not built    */
     MLA_ERR_ALIGNMENT = 4,           /* a pointer is not 16-byte aligned      */
     MLA_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < the size query      */
-    MLA_ERR_HIP = 6                  /* a HIP launch or runtime call failed   */
+    MLA_ERR_HIP = 6,                 /* a HIP launch or runtime call failed   */
+    MLA_STATUS_MAX_ = 0x7fffffff     /* not a status: keeps the enum int-wide, so
+                                        mla_status_string may be given any value */
 } mla_status;
 
 typedef enum {

@@ -43,6 +43,29 @@ def _run(cmd, verbose):
         print(out)
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for the C ABI's
+# validation code (device code is built as usual: each sanitizer flag is
+# restricted to the host pass).  The result loads only with clang's ASan
+# runtime preloaded (see tests/test_abi_sanitized.py).
+SAN_FLAGS = ["-g", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
+SAN_LIB = os.path.join(BUILD, "san", "libmla_san.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    d = os.path.join(BUILD, "san")
+    os.makedirs(d, exist_ok=True)
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    objs = [os.path.join(d, f[:-4] + ".o") for f in srcs]
+    cmds = [[HIPCC, *FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(srcs, objs)]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+          "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+          "-shared-libsan", *objs, "-o", SAN_LIB], verbose)
+    return SAN_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))

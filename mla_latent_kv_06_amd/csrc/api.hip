@@ -457,6 +457,7 @@ const char* mla_status_string(mla_status s) {
         case MLA_ERR_ALIGNMENT: return "MLA_ERR_ALIGNMENT";
         case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
         case MLA_ERR_HIP: return "MLA_ERR_HIP";
+        default: break;
     }
     return "MLA_ERR_UNKNOWN";
 }
