@@ -265,6 +265,22 @@ mla_status mla_decode_absorbed_noalloc(const mla_dims* dims, int32_t batch, int3
                                        const int32_t* seq_lens, int32_t num_splits,
                                        void* out, float* lse, void* stream);
 
+/* ---- debug check of the device-side contract --------------------------------
+ *
+ * The decode and the append read block_table and seq_lens on the device
+ * without checking them.  This call checks them, on the device: for every
+ * sequence b, 0 <= seq_lens[b] <= max_blocks_per_seq * block_size, and every
+ * block id block_table[b][k], k < ceil(seq_lens[b] / block_size), lies in
+ * [0, num_blocks).  It writes report[0] = the number of violations,
+ * report[1], report[2] = the first one (smallest b, then k; k = -1 for a
+ * length), or -1, -1.  report: 3 int32 in device memory, valid once `stream`
+ * has passed the call.  One workgroup walks batch * (max_blocks_per_seq + 1)
+ * entries: a debugging aid, not for every step.
+ * Errors (nothing launched): MLA_ERR_BAD_SHAPE, MLA_ERR_NULL_POINTER. */
+mla_status mla_check_block_table(const mla_dims* dims, int32_t batch, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                 int32_t num_blocks, int32_t* report, void* stream);
+
 /* ---- output projection -----------------------------------------------------
  *
  * The layer's output side ("DeepSeek-V2: MLA Explained", "MLA Full Formulas",

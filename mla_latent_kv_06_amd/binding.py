@@ -43,7 +43,7 @@ EXPORTED = ("mla_status_string", "mla_last_error", "mla_cache_row_bytes",
             "mla_decode_absorbed_stages", "mla_query_workspace_size", "mla_query_project",
             "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_stages",
             "mla_decode_absorbed_noalloc", "mla_output_workspace_size", "mla_output_project",
-            "mla_decode_output_workspace_size", "mla_decode_output")
+            "mla_decode_output_workspace_size", "mla_decode_output", "mla_check_block_table")
 
 
 class Dims(ctypes.Structure):
@@ -113,6 +113,8 @@ _lib.mla_decode_output_workspace_size.argtypes = [_DP, _I, _I, _I, _I, ctypes.PO
 _lib.mla_decode_output.restype = ctypes.c_int
 _lib.mla_decode_output.argtypes = [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P,
                                    _P, _P, _SZ, _P]
+_lib.mla_check_block_table.restype = ctypes.c_int
+_lib.mla_check_block_table.argtypes = [_DP, _I, _P, _I, _P, _I, _P, _P]
 
 _lib.mla_prefill_workspace_size.restype = ctypes.c_int
 _lib.mla_prefill_workspace_size.argtypes = [_DP, _I, _I, _I, ctypes.POINTER(_SZ)]
@@ -280,6 +282,20 @@ def decode_noalloc(dims: Dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale
         _ptr(seq_lens), num_splits, _ptr(out), _ptr(lse), _stream(dev))
     _check(st, "mla_decode_absorbed_noalloc")
     return out, lse
+
+
+def check_block_table(dims: Dims, block_table, seq_lens, num_blocks: int):
+    """mla_check_block_table: returns (violations, first b, first k) after a
+    device synchronisation (k = -1 for a bad length)."""
+    dev = block_table.device
+    _need(block_table, "block_table", (torch.int32,), None, dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), (block_table.shape[0],), dev)
+    report = torch.full((3,), -7, dtype=torch.int32, device=dev)
+    _check(_lib.mla_check_block_table(ctypes.byref(dims), block_table.shape[0], _ptr(block_table),
+                                      block_table.shape[1], _ptr(seq_lens), num_blocks, _ptr(report),
+                                      _stream(dev)), "mla_check_block_table")
+    r = report.cpu().tolist()
+    return r[0], r[1], r[2]
 
 
 def output_workspace_size(rows: int, k: int, n: int) -> int:

@@ -608,6 +608,23 @@ mla_status mla_decode_absorbed_noalloc(const mla_dims* dims, int32_t batch, int3
                        MLA_NOALLOC_SCRATCH_BYTES, MLA_STAGE_ALL, stream);
 }
 
+mla_status mla_check_block_table(const mla_dims* dims, int32_t batch, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_blocks,
+                                 int32_t* report, void* stream) {
+    if (mla_status st = check_dims(dims); st != MLA_OK) return st;
+    if (batch < 0 || max_blocks_per_seq < 1 || num_blocks < 0)
+        return fail(MLA_ERR_BAD_SHAPE, "batch=%d max_blocks_per_seq=%d num_blocks=%d", batch,
+                    max_blocks_per_seq, num_blocks);
+    if (!report) return fail(MLA_ERR_NULL_POINTER, "report is NULL");
+    if (batch > 0 && (!block_table || !seq_lens))
+        return fail(MLA_ERR_NULL_POINTER, "block_table and seq_lens are required");
+    const hipError_t e = mla::launch_check_block_table(block_table, batch, max_blocks_per_seq, seq_lens,
+                                                       dims->block_size, num_blocks, report,
+                                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 mla_status mla_output_workspace_size(int32_t rows, int32_t k, int32_t n, size_t* bytes) {
     if (mla_status st = check_output_shape(rows, k, n); st != MLA_OK) return st;
     if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes is NULL");

@@ -65,5 +65,7 @@ bool is_v3_shape(const mla_dims& d);
 hipError_t launch_decode_mfma(const DecodeLaunch& a, unsigned stages);
 hipError_t launch_decode_generic(const DecodeLaunch& a, unsigned stages);
 hipError_t launch_append(const AppendLaunch& a, bool mfma_gemm);
+hipError_t launch_check_block_table(const int* block_table, int batch, int max_blocks, const int* seq_lens,
+                                    int block_size, int num_blocks, int* report, hipStream_t stream);
 
 }  // namespace mla
