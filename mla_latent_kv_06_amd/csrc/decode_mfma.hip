@@ -807,17 +807,20 @@ static_assert(HROWS == kCacheSub, "a half-tile is one channel-major sub-block of
 
 // Half-tile layout in LDS.  Channel row ch (64 bytes: 4 chunks of 8 tokens)
 // keeps its chunk c at 16-byte slot 4 ch + (c ^ hswz(ch)), hswz(ch) =
-// bit2(ch) | bit1(ch) << 1.  With 32 or 64 banks, the value operand's 16-byte
-// reads (8 consecutive rows, one chunk) and the score operand's transposing
-// 8-byte reads (16 lanes: 4 consecutive rows x 4 groups of 4 tokens) fall on
-// distinct banks; each copy instruction still moves 1 KB that is contiguous
-// in memory (16 channel rows).
-__device__ __forceinline__ int hswz(int ch) { return ((ch >> 2) & 1) | (((ch >> 1) & 1) << 1); }
+// bit2(ch) | (bit1(ch) ^ bit3(ch)) << 1.  The value operand's 16-byte reads
+// (one chunk of consecutive rows) then fall on distinct banks for any 8
+// (32 banks) or 16 (64 banks) aligned rows -- hswz is one-to-one in
+// (bit1, bit2) for a fixed bit3 and in (bit2, bit3) for a fixed bit1 --
+// and so do the score operand's transposing 8-byte reads (16 lanes: 4
+// consecutive rows x 4 groups of 4 tokens; rows 2 apart differ in hswz's
+// high bit).  Each copy instruction still moves 1 KB contiguous in memory
+// (16 channel rows).
+__device__ __forceinline__ int hswz(int ch) { return ((ch >> 2) & 1) | ((((ch >> 1) ^ (ch >> 3)) & 1) << 1); }
 
 // Copy instruction k (0..8) of wave w for one half-tile: instruction
 // i = 9 w + k fills slots 64 i .. 64 i + 63, i.e. channel rows 16 i .. +16;
 // lane l takes row 16 i + l/4, slot l%4, i.e. chunk (l%4) ^ hswz(l/4) of it
-// (16 i leaves bits 1 and 2 of the row to l/4), at byte 1024 i + 64 (l/4) +
+// (16 i leaves bits 0..3 of the row to l/4), at byte 1024 i + 64 (l/4) +
 // 16 chunk of the sub-block.
 __device__ __forceinline__ void issue_half_part(__amdgpu_buffer_rsrc_t rsrc, lds_u8* slot, int w,
                                                 int lane, int k) {
