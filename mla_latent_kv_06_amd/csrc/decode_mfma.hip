@@ -1168,35 +1168,58 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
 
         // V_h: O^T += V^T . P^T for this wave's 4 column blocks and all 4 head
         // blocks.  Slot m = 16 k2 + 4 c + hb; the value fragment of (k2, c) is
-        // read one column block ahead, the weights of K-step k2 (four 1 KB reads)
-        // at the start of the previous K-step.  Step hook(m) runs after the
-        // MFMA of slot m.
-        auto values = [&](const lds_u8* __restrict__ vb, const lds_u8* __restrict__ pb, auto hook)
-                          __attribute__((always_inline)) {
-            bf16x8 va[2], pf[2][4];
-            va[0] = v_frag(vb, 4 * w, 0);
-            static_for<0, 4>([&](auto hc) { pf[0][decltype(hc)::value] = p_frag(pb, decltype(hc)::value, 0); });
+        // read one column block ahead; the weights of head block hb, K-step 1
+        // replace those of K-step 0 right after their last use (slot 12 + hb),
+        // four MFMAs ahead of their first.  The first value fragment and the
+        // K-step-0 weights (VPre) are read before the chain starts, inside the
+        // score chain when there is one.  Step hook(m) runs after the MFMA of
+        // slot m.
+        struct VPre {
+            bf16x8 va;
+            bf16x8 pf[4];
+        };
+        auto v_prologue = [&](const lds_u8* __restrict__ vb, const lds_u8* __restrict__ pb)
+                              __attribute__((always_inline)) {
+            VPre p;
+            p.va = v_frag(vb, 4 * w, 0);
+            static_for<0, 4>([&](auto hc) { p.pf[decltype(hc)::value] = p_frag(pb, decltype(hc)::value, 0); });
+            return p;
+        };
+        auto values_from = [&](const lds_u8* __restrict__ vb, const lds_u8* __restrict__ pb, const VPre& pre,
+                               auto hook) __attribute__((always_inline)) {
+            bf16x8 va[2], pf[4];
+            va[0] = pre.va;
+            static_for<0, 4>([&](auto hc) { pf[decltype(hc)::value] = pre.pf[decltype(hc)::value]; });
             static_for<0, NV>([&](auto mc) __attribute__((always_inline)) {
                 constexpr int m = decltype(mc)::value;
-                constexpr int k2 = m >> 4, c = (m >> 2) & 3, hb = m & 3;
-                if constexpr (hb == 0 && m + 4 < NV) {      // next column block's fragment
+                // head blocks in the order 1, 2, 3, 0 within a column block: the
+                // chain starts away from accumulator 0, whose registers the
+                // scores' accumulator borrows during the score chain
+                constexpr int c = (m >> 2) & 3, hb = (m + 1) & 3;
+                if constexpr ((m & 3) == 0 && m + 4 < NV) {      // next column block's fragment
                     constexpr int kn = (m + 4) >> 4, cn = ((m + 4) >> 2) & 3;
                     va[((m >> 2) + 1) & 1] = v_frag(vb, 4 * w + cn, kn);
                 }
-                if constexpr (m == 0) {
-                    static_for<0, 4>([&](auto hc) { pf[1][decltype(hc)::value] = p_frag(pb, decltype(hc)::value, 1); });
-                }
-                o[4 * c + hb] = mfma32(va[(m >> 2) & 1], pf[k2][hb], o[4 * c + hb]);
+                o[4 * c + hb] = mfma32(va[(m >> 2) & 1], pf[hb], o[4 * c + hb]);
+                if constexpr (m >= 12 && m < 16) pf[hb] = p_frag(pb, hb, 1);
                 hook(std::integral_constant<int, m>{});
                 __builtin_amdgcn_sched_barrier(0);
             });
+        };
+        auto values = [&](const lds_u8* __restrict__ vb, const lds_u8* __restrict__ pb, auto hook)
+                          __attribute__((always_inline)) {
+            values_from(vb, pb, v_prologue(vb, pb), hook);
         };
 
         // One pipelined iteration: the scores S_{h+1} (into sv), with the copy
         // of half h+3 spread over them; then, unless SCAN, V_h with the weights
         // of h from LDS.  SOFT: the softmax of S_{h+1} is threaded between the
-        // V_h MFMAs (a partial S_{h+1}, the piece's last half, takes the plain
-        // masked softmax after the iteration instead).  SCAN: scores only.
+        // V_h MFMAs, from slot SOFT_LAG on, so that the first value MFMAs issue
+        // while the score chain's results drain (a partial S_{h+1}, the piece's
+        // last half, takes the plain masked softmax after the iteration
+        // instead).  SCAN: scores only.
+        constexpr int SOFT_LAG = 2;
+        static_assert(28 + SOFT_LAG < NV, "the softmax steps fit in the value chain");
         auto iteration_body = [&](auto scan_c, auto soft_c, int h, const lds_u8* __restrict__ sb,
                                   const lds_u8* __restrict__ vb, lds_u8* __restrict__ cb,
                                   const lds_u8* __restrict__ pb) __attribute__((always_inline)) {
@@ -1205,6 +1228,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
             const __amdgpu_buffer_rsrc_t crs = half_rsrc(h + 3);
             bf16x8 ring[DIST];
             f32x16 sacc = {};
+            VPre pre;
             sv_valid = valid_half(h + 1);
             static_for<0, DIST>([&](auto mc) { ring[decltype(mc)::value] = k_frag(sb, decltype(mc)::value); });
             static_for<0, NS>([&](auto mc) __attribute__((always_inline)) {
@@ -1213,15 +1237,27 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
                 if constexpr (m + DIST < NS) ring[m % DIST] = k_frag(sb, m + DIST);
                 sacc = mfma32(a, qf[m], sacc);
                 if constexpr (m % 4 == 0) issue_half_part(crs, cb, w, lane, m / 4);
+                // the value chain's first operands, read while the scores finish
+                if constexpr (!SCAN && m == NS - DIST) pre = v_prologue(vb, pb);
                 __builtin_amdgcn_sched_barrier(0);
             });
-            // the scores leave the accumulator
+            // the scores leave the accumulator (SOFT: after the first value
+            // MFMA, which does not wait for them)
+            if constexpr (!SOFT) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
+                for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
+            }
             if constexpr (!SCAN) {
                 pw_dst = (lds_u8*)pbuf_of(h + 1);
-                values(vb, pb, [&](auto mc) __attribute__((always_inline)) {
-                    if constexpr (SOFT) softmax_step(mc, std::false_type{}, std::false_type{});
+                values_from(vb, pb, pre, [&](auto mc) __attribute__((always_inline)) {
+                    constexpr int m = decltype(mc)::value;
+                    if constexpr (SOFT && m == 0) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
+                    }
+                    if constexpr (SOFT && m >= SOFT_LAG)
+                        softmax_step(std::integral_constant<int, m - SOFT_LAG>{}, std::false_type{},
+                                     std::false_type{});
                 });
             }
         };
