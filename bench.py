@@ -40,7 +40,7 @@ EVENT_STRIDE = 3               # timed steps per kernel-event sample
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("decode_mfma.hip", "common.hpp", "internal.hpp")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "split_kv_kernel_v3_b64_ctx8k_bf16_hbm_traffic.txt")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "split_kv_ring_kernel_v3_b64_ctx8k_bf16_hbm_traffic.txt")
 
 
 def log(*a):
