@@ -94,6 +94,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // x 16 columns and each lane receives one column's 4 values; the padding puts
 // the 4 rows of a group on disjoint banks.
 constexpr int WT_ROWB = 288;    // bytes per staged W_UK row
+// bytes per staged q_nope row (256 + 16): the 16-byte B-operand reads of 16
+// consecutive rows start 68 dwords apart and cover all 64 banks
+constexpr int QT_ROWB = 272;
 
 __global__ __launch_bounds__(256) void absorb_q_kernel(
     const unsigned short* __restrict__ q_nope,  // [R][H][128]
@@ -102,6 +105,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
     unsigned short* __restrict__ qbuf,          // [R][H][576]
     int R) {
     __shared__ __attribute__((aligned(16))) unsigned char wt[128 * WT_ROWB];
+    __shared__ __attribute__((aligned(16))) unsigned char qt[64 * QT_ROWB];
     const int bid = blockIdx.x;
     const int h = bid % H;
     const int cb = (bid / H) & 3;
@@ -117,17 +121,15 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
         const int i = k * 256 + tid, n = i >> 4, c = i & 15;
         wv[k] = *reinterpret_cast<const u32x4*>(w_uk + ((size_t)h * 128 + n) * DC + cb * 128 + c * 8);
     }
-    // this wave's q_nope fragments (B operands), loaded together with W_UK
-    bf16x8 qv[8][2];
+    // q_nope of the 64 rows for head h: 64 rows x 16 chunks of 16 B, 4 per
+    // thread (16 consecutive threads read one row's 256 bytes), at clamped
+    // rows; staged in LDS for the MFMA B operands
+    u32x4 qv[4];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int r = rb * 64 + nb * 32 + l32;
-            qv[ks][nb] = r < R ? *reinterpret_cast<const bf16x8*>(
-                                     q_nope + ((size_t)r * H + h) * 128 + ks * 16 + hf * 8)
-                               : bf16x8{};
-        }
+    for (int k = 0; k < 4; ++k) {
+        const int i = k * 256 + tid, r = min(rb * 64 + (i >> 4), R - 1), c = i & 15;
+        qv[k] = *reinterpret_cast<const u32x4*>(q_nope + ((size_t)r * H + h) * 128 + c * 8);
+    }
     // q_pe rides along in the workgroups of column block 0: 64 rows x 8
     // chunks of 16 bytes, two per thread, loaded here with everything else
     // (unconditionally, at clamped rows) and stored at the end
@@ -141,6 +143,11 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
     for (int k = 0; k < 8; ++k) {
         const int i = k * 256 + tid, n = i >> 4, c = i & 15;
         *reinterpret_cast<u32x4*>(wt + n * WT_ROWB + c * 16) = wv[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = k * 256 + tid, rl = i >> 4, c = i & 15;
+        *reinterpret_cast<u32x4*>(qt + rl * QT_ROWB + c * 16) = qv[k];
     }
     __syncthreads();
 
@@ -158,7 +165,11 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
         const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(base + 4 * WT_ROWB));
         const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a, qv[ks][nb], acc[nb]);
+        for (int nb = 0; nb < 2; ++nb) {
+            // B operand: row nb*32 + l32, n = 16 ks + 8 hf .. +8
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(qt + (nb * 32 + l32) * QT_ROWB + (ks * 16 + hf * 8) * 2);
+            acc[nb] = mfma32(a, b, acc[nb]);
+        }
     }
     // The output tile (64 query rows x 128 latent columns) goes through LDS so
     // that each row's 256-byte segment is written by one contiguous store:
