@@ -317,14 +317,19 @@ __device__ __forceinline__ void convert_tile_fp8(lds_u8* lstage, lds_u8* ltile, 
 // seq_lens[b] - q_len + s + 1 cache tokens, i.e. tiles(r) 64-token tiles.
 //  - num_splits > 0: row r is cut into num_splits equal ranges of whole tiles,
 //    one workgroup each; partial slot r * num_splits + split.
-//  - num_splits == 0 (balanced): the rows' tiles, concatenated in row order,
-//    are cut into G equal ranges [i T / G, (i+1) T / G), one per workgroup
-//    (T = total tiles, G = min(grid, ceil(T / 4)) <= T, so no range is empty;
-//    workgroups past G have nothing to do).  A range may span several rows; each
-//    (workgroup i, row r) piece writes partial slot i + r.  Slots are unique:
-//    for i < i' the rows of i end no later than the rows of i' begin, so
-//    i + r < i' + r'.  Row r's pieces occupy slots first(r) + r .. last(r) + r,
-//    first / last being the workgroups holding its first / last tile.
+//  - num_splits == 0 (balanced): the tiles are cut into G equal ranges over
+//    "entries" concatenated in order.  With 1 < q_len <= kPairQ an entry is a
+//    sequence (Qs = q_len rows sharing its tiles, tiles(entry) = tiles of its
+//    last row); otherwise an entry is a query row (Qs = 1).  Range g =
+//    [g T / G, (g+1) T / G) of the T entry tiles is walked by Qs workgroups,
+//    one per row s of each entry, on one XCD at the same time, so that the
+//    rows of a sequence read each tile from HBM about once.  The piece of
+//    (range g, entry e, row s) writes partial slot Qs (g + e) + s; a piece
+//    whose row sees none of the range's tiles writes log-sum-exp -inf there.
+//    Slots are unique: for g < g' the entries of g end no later than those of
+//    g' begin, so g + e < g' + e'.  Row (e, s)'s pieces occupy slots
+//    Qs (f + e) + s, Qs (f + 1 + e) + s, .. Qs (l + e) + s, f / l being the
+//    ranges holding its entry's first / last tile; all below kNumCUs + R.
 
 __device__ __forceinline__ int row_tiles(const int* __restrict__ seq_lens, int q_len, int r) {
     const int b = r / q_len;
@@ -339,27 +344,39 @@ __device__ __forceinline__ int row_tiles(const int* __restrict__ seq_lens, int q
 // the tiles outweighs each workgroup's fixed costs (query load, partial write,
 // one more partial to merge).
 constexpr int kMinGroupTiles = 1;
-__device__ __forceinline__ long long balanced_groups(long long grid, long long T) {
-    return min(grid, (T + kMinGroupTiles - 1) / kMinGroupTiles);
+// Largest q_len whose rows share tile ranges (sequence entries).
+constexpr int kPairQ = 8;
+static_assert(kNumCUs % 8 == 0 && kNumCUs / 8 >= kPairQ, "every XCD runs at least one range's rows");
+__device__ __forceinline__ int sched_qs(int q_len) { return q_len <= kPairQ ? q_len : 1; }
+// Tiles of entry e, and the query row of its row s.
+__device__ __forceinline__ int entry_tiles(const int* __restrict__ seq_lens, int q_len, int e) {
+    return q_len <= kPairQ ? row_tiles(seq_lens, q_len, e * q_len + q_len - 1) : row_tiles(seq_lens, q_len, e);
 }
+__device__ __forceinline__ int entry_row(int q_len, int e, int s) { return q_len <= kPairQ ? e * q_len + s : e; }
+// Ranges for T entry tiles on `grid` workgroups (a multiple of the 8 XCDs):
+// each XCD runs ceil(G / 8) ranges x Qs rows, at most grid / 8 workgroups.
+__device__ __forceinline__ long long balanced_groups(long long grid, long long T, int Qs) {
+    return min(8 * ((grid / 8) / Qs), (T + kMinGroupTiles - 1) / kMinGroupTiles);
+}
+
 
 // Workgroup holding tile t of the concatenated tiles (T tiles over G groups).
 __device__ __forceinline__ int group_of_tile(long long t, long long T, long long G) {
     return (int)(((t + 1) * G + T - 1) / T - 1);
 }
 
-// Block-wide scan of row tile counts: thread tid owns rows [tid*per, tid*per+per)
-// (per = ceil(R / 256)).  Returns T; *excl / *mine receive the tiles before this
-// thread's rows and in them.  sc: 260 ints of LDS scratch.
+// Block-wide scan of entry tile counts: thread tid owns entries [tid*per,
+// tid*per+per) (per = ceil(E / 256)).  Returns T; *excl / *mine receive the
+// tiles before this thread's entries and in them.  sc: 260 ints of LDS scratch.
 template <typename LdsInt>
-__device__ __forceinline__ int scan_row_tiles(const int* __restrict__ seq_lens, int q_len, int R,
-                                              LdsInt sc, int* excl, int* mine) {
+__device__ __forceinline__ int scan_entry_tiles(const int* __restrict__ seq_lens, int q_len, int E,
+                                                LdsInt sc, int* excl, int* mine) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int per = (R + 255) / 256;
+    const int per = (E + 255) / 256;
     int local = 0;
     for (int k = 0; k < per; ++k) {
-        const int r = tid * per + k;
-        if (r < R) local += row_tiles(seq_lens, q_len, r);
+        const int e = tid * per + k;
+        if (e < E) local += entry_tiles(seq_lens, q_len, e);
     }
     int incl = local;
 #pragma unroll
@@ -377,16 +394,79 @@ __device__ __forceinline__ int scan_row_tiles(const int* __restrict__ seq_lens, 
     return T;
 }
 
-// A piece (row, tiles [t0, t1)): row = b * q_len + s is query token s of
-// sequence b; the piece covers all 128 heads over those tiles of the row's
-// visible range.  A workgroup handles one piece (fixed partitions) or the
-// consecutive pieces its balanced share of the tile sequence spans.
-// Wave w owns heads 32w .. 32w+31 for the whole tile loop; each 64-token tile
-// is processed as two halves of 32 tokens:
-//   S^T (32 tokens x 32 heads) = K_half (32 x 576) . Q_w^T   [36 MFMA]
-//   O^T (512 cols x 32 heads) += V^T (512 x 32) . P^T         [32 MFMA]
-// so softmax statistics stay inside the wave.  Q_w stays in VGPRs (its rotary
-// part in LDS on the bf16 path) and O^T in AGPRs for the whole loop.
+// One workgroup's walk of the balanced schedule (workgroups of 256 threads).
+// Workgroup id b runs on XCD b % 8; the XCD's ceil(G / 8) consecutive ranges
+// go to its workgroups in order, Qs per range (row s = (b / 8) % Qs), so the
+// rows of one range run side by side and consecutive ranges (a long row's
+// pieces) share an L2.
+struct BalancedWalk {
+    int grp, s, rng_a, rng_b, cur_e, cur_es;
+};
+// Sets up the walk; false: this workgroup has nothing to do (uniform).
+template <typename LdsInt>
+__device__ __forceinline__ bool balanced_start(const int* __restrict__ seq_lens, int q_len, int R,
+                                               LdsInt sc, BalancedWalk& wk) {
+    const int tid = threadIdx.x;
+    const int Qs = sched_qs(q_len), E = R / Qs;
+    int excl, mine;
+    const int T = scan_entry_tiles(seq_lens, q_len, E, sc, &excl, &mine);
+    const long long G = balanced_groups(gridDim.x, T, Qs);
+    const int per = (int)((G + 7) / 8);
+    const int bx = blockIdx.x & 7, bk = blockIdx.x >> 3;
+    const int g = bk < per * Qs ? bx * per + bk / Qs : (int)G;
+    if ((long long)g >= G) return false;
+    wk.grp = g;
+    wk.s = bk % Qs;
+    wk.rng_a = (int)((long long)g * T / G);
+    wk.rng_b = (int)((long long)(g + 1) * T / G);
+    wk.cur_e = 0;
+    wk.cur_es = 0;
+    if (wk.rng_a < wk.rng_b && excl <= wk.rng_a && wk.rng_a < excl + mine) {
+        const int pe = (E + 255) / 256;
+        int es = excl;
+        for (int k = 0; k < pe; ++k) {
+            const int e = tid * pe + k;
+            const int nt = e < E ? entry_tiles(seq_lens, q_len, e) : 0;
+            if (wk.rng_a < es + nt) {
+                sc[260] = e;
+                sc[261] = es;
+                break;
+            }
+            es += nt;
+        }
+    }
+    __syncthreads();
+    if (wk.rng_a < wk.rng_b) {
+        wk.cur_e = sc[260];
+        wk.cur_es = sc[261];
+    }
+    __syncthreads();                     // scratch read before the caller reuses it
+    return true;
+}
+// The walk's next piece (row, tiles [t0, t1), slot); false when done.  A row
+// that sees none of a range's tiles gets log-sum-exp -inf in its slot.
+__device__ __forceinline__ bool balanced_next(BalancedWalk& wk, const int* __restrict__ seq_lens, int q_len,
+                                              int R, float* __restrict__ part_lse, int& row, int& t0,
+                                              int& t1, int& slot) {
+    const int Qs = sched_qs(q_len), E = R / Qs;
+    while (wk.cur_es < wk.rng_b && wk.cur_e < E) {
+        const int e = wk.cur_e, es = wk.cur_es;
+        const int nt = entry_tiles(seq_lens, q_len, e);
+        wk.cur_e += 1;
+        wk.cur_es += nt;
+        const int lo = max(wk.rng_a, es) - es, hi = min(wk.rng_b, es + nt) - es;
+        if (hi > lo) {
+            row = entry_row(q_len, e, wk.s);
+            slot = Qs * (wk.grp + e) + wk.s;
+            t0 = lo;
+            t1 = min(hi, row_tiles(seq_lens, q_len, row));
+            if (t0 < t1) return true;
+            if (threadIdx.x < H) part_lse[(size_t)slot * H + threadIdx.x] = kNegInf;
+        }
+    }
+    return false;
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const unsigned short* __restrict__ qbuf,      // [R][H][576] bf16
@@ -416,37 +496,10 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const int head = w * 32 + l32;
 
     // ---- this workgroup's pieces (row, tiles [t0, t1), partial slot) ---------------
-    int cur_row = 0, cur_rs = 0, rng_a = 0, rng_b = 0;   // balanced: walk state
+    BalancedWalk wk{};
     bool fixed_pending = num_splits > 0;
-    if (num_splits == 0) {
-        MLA_LDS int* sc = reinterpret_cast<MLA_LDS int*>(smem);
-        int excl, mine;
-        const int T = scan_row_tiles(seq_lens, q_len, R, sc, &excl, &mine);
-        const long long G = balanced_groups(gridDim.x, T);
-        if ((long long)blockIdx.x >= G) return;      // uniform: the whole workgroup leaves
-        rng_a = (int)((long long)blockIdx.x * T / G);
-        rng_b = (int)((long long)(blockIdx.x + 1) * T / G);
-        if (rng_a < rng_b && excl <= rng_a && rng_a < excl + mine) {
-            const int per = (R + 255) / 256;
-            int rs = excl;
-            for (int k = 0; k < per; ++k) {
-                const int r = tid * per + k;
-                const int nt = r < R ? row_tiles(seq_lens, q_len, r) : 0;
-                if (rng_a < rs + nt) {
-                    sc[260] = r;
-                    sc[261] = rs;
-                    break;
-                }
-                rs += nt;
-            }
-        }
-        __syncthreads();
-        if (rng_a < rng_b) {
-            cur_row = sc[260];
-            cur_rs = sc[261];
-        }
-        __syncthreads();                 // scratch read before the tiles reuse it
-    }
+    if (num_splits == 0 && !balanced_start(seq_lens, q_len, R, reinterpret_cast<MLA_LDS int*>(smem), wk))
+        return;                          // uniform: the whole workgroup leaves
     auto next_piece = [&](int& row, int& t0, int& t1, int& slot) -> bool {
         if (num_splits > 0) {
             if (!fixed_pending) return false;
@@ -464,21 +517,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
             }
             return true;
         }
-        while (cur_rs < rng_b && cur_row < R) {
-            const int r = cur_row, rs = cur_rs;
-            const int nt = row_tiles(seq_lens, q_len, r);
-            cur_row += 1;
-            cur_rs += nt;
-            const int lo = max(rng_a, rs) - rs, hi = min(rng_b, rs + nt) - rs;
-            if (hi > lo) {
-                row = r;
-                t0 = lo;
-                t1 = hi;
-                slot = blockIdx.x + r;
-                return true;
-            }
-        }
-        return false;
+        return balanced_next(wk, seq_lens, q_len, R, part_lse, row, t0, t1, slot);
     };
 
     int row, t0, t1, slot;
@@ -893,45 +932,10 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
     const int head = w * 32 + l32;
 
     // ---- this workgroup's pieces: as in split_kv_kernel ----------------------------
-    int cur_row = 0, cur_rs = 0, rng_a = 0, rng_b = 0;
-    int grp = blockIdx.x;                // this workgroup's range of the balanced schedule
+    BalancedWalk wk{};
     bool fixed_pending = num_splits > 0;
-    if (num_splits == 0) {
-        MLA_LDS int* sc = reinterpret_cast<MLA_LDS int*>(smem);
-        int excl, mine;
-        const int T = scan_row_tiles(seq_lens, q_len, R, sc, &excl, &mine);
-        const long long G = balanced_groups(gridDim.x, T);
-        // Range L of the balanced schedule runs on workgroup id b with
-        // L = (b % 8) * per + b / 8, per = ceil(G / 8): workgroups share an XCD
-        // (XCD = id % 8 on this grid of 256) in runs of consecutive ranges, so
-        // the workgroups of one query row read its queries through one L2.
-        const int per = (int)((G + 7) / 8);
-        const int bx = blockIdx.x & 7, bk = blockIdx.x >> 3;
-        grp = bk < per ? bx * per + bk : (int)G;
-        if ((long long)grp >= G) return;             // uniform: the whole workgroup leaves
-        rng_a = (int)((long long)grp * T / G);
-        rng_b = (int)((long long)(grp + 1) * T / G);
-        if (rng_a < rng_b && excl <= rng_a && rng_a < excl + mine) {
-            const int per = (R + 255) / 256;
-            int rs = excl;
-            for (int k = 0; k < per; ++k) {
-                const int r = tid * per + k;
-                const int nt = r < R ? row_tiles(seq_lens, q_len, r) : 0;
-                if (rng_a < rs + nt) {
-                    sc[260] = r;
-                    sc[261] = rs;
-                    break;
-                }
-                rs += nt;
-            }
-        }
-        __syncthreads();
-        if (rng_a < rng_b) {
-            cur_row = sc[260];
-            cur_rs = sc[261];
-        }
-        __syncthreads();                 // scratch read before the ring reuses it
-    }
+    if (num_splits == 0 && !balanced_start(seq_lens, q_len, R, reinterpret_cast<MLA_LDS int*>(smem), wk))
+        return;                          // uniform: the whole workgroup leaves
     auto next_piece = [&](int& row, int& t0, int& t1, int& slot) -> bool {
         if (num_splits > 0) {
             if (!fixed_pending) return false;
@@ -949,21 +953,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
             }
             return true;
         }
-        while (cur_rs < rng_b && cur_row < R) {
-            const int r = cur_row, rs = cur_rs;
-            const int nt = row_tiles(seq_lens, q_len, r);
-            cur_row += 1;
-            cur_rs += nt;
-            const int lo = max(rng_a, rs) - rs, hi = min(rng_b, rs + nt) - rs;
-            if (hi > lo) {
-                row = r;
-                t0 = lo;
-                t1 = hi;
-                slot = grp + r;
-                return true;
-            }
-        }
-        return false;
+        return balanced_next(wk, seq_lens, q_len, R, part_lse, row, t0, t1, slot);
     };
 
     lds_u8* pbuf = smem + P_OFF;
@@ -1452,7 +1442,11 @@ __global__ __launch_bounds__(CMB_THREADS) void combine_kernel(
     // flight): thread tid reads the length behind row tid (and, past 512
     // rows, every 512th after it); lanes 0..31 of wave 0 read this block's rows.
     const bool balanced = num_splits == 0;
-    const int len_main = seq_lens[min(tid, R - 1) / q_len];
+    // balanced: entries of the schedule (sequences when Qs > 1, else rows);
+    // a row's partials sit Qs slots apart
+    const int Qs = sched_qs(q_len), E = R / Qs;
+    const int pstr = balanced ? Qs : 1;
+    const int len_main = seq_lens[entry_row(q_len, min(tid, E - 1), Qs - 1) / q_len];
     const int len_blk = seq_lens[min(r0 + (lane & 31), R - 1) / q_len];
     // tiles of a row from its sequence length
     auto tiles_of = [&](int r, int len) {
@@ -1477,17 +1471,18 @@ __global__ __launch_bounds__(CMB_THREADS) void combine_kernel(
     // branch-free form keeps the length loads ahead of W_UV's); a fixed
     // partition overrides it.
     {
-        // tiles of all rows (T) and of the rows before this block's
+        // tiles of all entries (T) and of the entries before this block's first
+        const int e0 = r0 / Qs;
         int total = 0, before = 0;
         {
-            const int nt = tiles_of(tid, len_main) * (tid < R ? 1 : 0);
+            const int nt = tiles_of(entry_row(q_len, tid, Qs - 1), len_main) * (tid < E ? 1 : 0);
             total = nt;
-            before = tid < r0 ? nt : 0;
+            before = tid < e0 ? nt : 0;
         }
-        for (int r = tid + CMB_THREADS; r < R; r += CMB_THREADS) {
-            const int nt = row_tiles(seq_lens, q_len, r);
+        for (int e = tid + CMB_THREADS; e < E; e += CMB_THREADS) {
+            const int nt = entry_tiles(seq_lens, q_len, e);
             total += nt;
-            before += r < r0 ? nt : 0;
+            before += e < e0 ? nt : 0;
         }
 #pragma unroll
         for (int d = 32; d > 0; d >>= 1) {
@@ -1506,22 +1501,27 @@ __global__ __launch_bounds__(CMB_THREADS) void combine_kernel(
                 T += red[0][k];
                 rs += red[1][k];
             }
-            // lanes 0..31: the block's rows, an exclusive scan of their tiles
+            // lanes 0..31: the block's rows; an exclusive scan over their
+            // entries (each entry counted at its first lane in the block)
+            // gives the tiles before each row's entry
             const int r = r0 + (lane & 31);
-            const int nt = tiles_of(r, len_blk) * ((lane < 32 && r < R) ? 1 : 0);
-            int incl = nt;
+            const int e = r / Qs, s = r - e * Qs;
+            const int nt = tiles_of(entry_row(q_len, e, Qs - 1), len_blk) * ((lane < 32 && r < R) ? 1 : 0);
+            const int c = (s == 0 || lane == 0) ? nt : 0;
+            int incl = c;
 #pragma unroll
             for (int d = 1; d < 32; d <<= 1) {
                 const int y = __shfl_up(incl, d, 64);
                 if ((lane & 31) >= d) incl += y;
             }
-            rs += incl - nt;
+            const int first_lane = max(0, (lane & 31) - s);
+            rs += __shfl(incl - c, first_lane, 64);
             if (lane < 32) {
                 if (balanced) {
-                    const int G = (int)balanced_groups(groups, T);
+                    const int G = (int)balanced_groups(groups, T, Qs);
                     const int f = nt > 0 ? group_of_tile(rs, T, G) : 0;
                     const int l = nt > 0 ? group_of_tile(rs + nt - 1, T, G) : -1;
-                    pbase[lane] = f + r;
+                    pbase[lane] = Qs * (f + e) + s;
                     pcnt[lane] = nt > 0 ? l - f + 1 : 0;
                 } else {
                     pbase[lane] = r < R ? r * num_splits : 0;
@@ -1600,14 +1600,14 @@ __global__ __launch_bounds__(CMB_THREADS) void combine_kernel(
         for (int c = 0; c < 8; ++c) acc[c] = 0.f;
         if (rl < rows_b) {
             const int base = pbase[rl], cnt = pcnt[rl];
-            const __amdgpu_buffer_rsrc_t prs = make_rsrc(part_o + (size_t)base * H * DC, cnt * H * DC * 2);
-            const __amdgpu_buffer_rsrc_t lrs = make_rsrc(part_lse + (size_t)base * H, cnt * H * 4);
+            const __amdgpu_buffer_rsrc_t prs = make_rsrc(part_o + (size_t)base * H * DC, cnt * pstr * H * DC * 2);
+            const __amdgpu_buffer_rsrc_t lrs = make_rsrc(part_lse + (size_t)base * H, cnt * pstr * H * 4);
             for (int p0 = sub; p0 < cnt; p0 += NB * wpr) {
                 u32x4 v[NB];
                 float lv[NB];
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    const int sp = p0 + j * wpr;
+                    const int sp = (p0 + j * wpr) * pstr;
                     v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                         prs, lane * 16, sp * (H * DC * 2) + h * (DC * 2), 0));
                     lv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -1666,8 +1666,8 @@ __global__ __launch_bounds__(CMB_THREADS) void combine_kernel(
         __amdgpu_buffer_rsrc_t prs[4], lrs[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            prs[rr] = make_rsrc(part_o + (size_t)base[rr] * H * DC, cnt[rr] * H * DC * 2);
-            lrs[rr] = make_rsrc(part_lse + (size_t)base[rr] * H, cnt[rr] * H * 4);
+            prs[rr] = make_rsrc(part_o + (size_t)base[rr] * H * DC, cnt[rr] * pstr * H * DC * 2);
+            lrs[rr] = make_rsrc(part_lse + (size_t)base[rr] * H, cnt[rr] * pstr * H * 4);
         }
         for (int p0 = 0; p0 < S; p0 += CMB_CHUNK) {
             u32x4 v[4][CMB_CHUNK];
@@ -1676,7 +1676,7 @@ __global__ __launch_bounds__(CMB_THREADS) void combine_kernel(
             for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
                 for (int j = 0; j < CMB_CHUNK; ++j) {
-                    const int sp = p0 + j;
+                    const int sp = (p0 + j) * pstr;
                     v[rr][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                              prs[rr], lane * 16, sp * (H * DC * 2) + h * (DC * 2), 0));
                     lv[rr][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
