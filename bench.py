@@ -8,7 +8,9 @@
 One step = the whole hot path for one layer over one batch: the cache append
 of the new tokens (wkv_a projection, RMSNorm, RoPE, paged write; workloads
 that define one) followed by the absorbed decode (q absorption, split-KV
-attention over the paged latent cache, log-sum-exp combine, W_UV).  Steps rotate over NL
+attention over the paged latent cache, log-sum-exp combine, W_UV) -- one
+mla_decode_step call when the workload appends, called stage by stage so
+that HIP events bracket the split-KV launch.  Steps rotate over NL
 independent layer copies (own pool, weights, queries) so the working set is
 far larger than the 256 MB last-level cache; inputs are resident in HBM before
 timing starts.  Prints ONE JSON line on stdout; details go to stderr.
@@ -258,8 +260,8 @@ def main():
     ws_q = (torch.empty(max(1, b.query_workspace_size(dims, B, Sq, wl.d_model, ql)), dtype=torch.uint8,
                         device=dev) if args.query_path else None)
     ws_dec = torch.empty(b.decode_workspace_size(dims, B, Sq, splits), dtype=torch.uint8, device=dev)
-    ws_app = torch.empty(max(1, b.append_workspace_size(dims, B, Sq, wl.d_model)),
-                         dtype=torch.uint8, device=dev)
+    ws_step = (torch.empty(b.step_workspace_size(dims, B, Sq, wl.d_model, splits), dtype=torch.uint8,
+                           device=dev) if wl.append else None)
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s: {args.layers} layers, "
         f"pool {layers[0].pool.numel() * layers[0].pool.element_size() / 1e6:.1f} MB each, "
@@ -268,9 +270,6 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(L, ev=None, qev=None):
-        if wl.append:
-            b.append(dims, L.h, L.w_kv_a, L.gamma, L.block_table, L.start_pos, L.pool, L.scale,
-                     rms_eps=1e-6, rope_base=10000.0, workspace=ws_app)
         if args.query_path:              # the decode's queries from the layer input
             if qev is not None:
                 qev[0].record(stream)
@@ -281,6 +280,22 @@ def main():
                 qev[1].record(stream)
         common = (dims, L.q_nope, L.q_pe, L.w_uk, L.w_uv, L.pool, L.scale, L.block_table,
                   L.seq_lens)
+        if wl.append:
+            # mla_decode_step: the append of the step's tokens and the decode,
+            # its stages called in turn so that events bracket the split-KV pass
+            def stp(stages):
+                b.decode_step(dims, L.h, L.w_kv_a, L.gamma, L.start_pos, L.q_nope, L.q_pe, L.w_uk,
+                              L.w_uv, L.pool, L.scale, L.block_table, L.seq_lens, num_splits=splits,
+                              rms_eps=1e-6, rope_base=10000.0, out=L.out, lse=L.lse,
+                              workspace=ws_step, stages=stages)
+            stp(b.STEP_PROJECT | b.STEP_FINALIZE_ABSORB)
+            if ev is not None:
+                ev[0].record(stream)
+            stp(b.STEP_SPLIT_KV)
+            if ev is not None:
+                ev[1].record(stream)
+            stp(b.STEP_COMBINE)
+            return
         b.decode(*common, num_splits=splits, out=L.out, lse=L.lse, workspace=ws_dec,
                  stages=b.STAGE_ABSORB_Q)
         if ev is not None:

@@ -265,6 +265,56 @@ mla_status mla_decode_absorbed_noalloc(const mla_dims* dims, int32_t batch, int3
                                        const int32_t* seq_lens, int32_t num_splits,
                                        void* out, float* lse, void* stream);
 
+/* ---- one decode step with its cache append ---------------------------------
+ *
+ * mla_cache_append of the step's new tokens, then mla_decode_absorbed over
+ * the cache that holds them, in one call.  Sequence b appends q_len tokens
+ * (hidden states h [batch][q_len][d_model], positions start_pos[b] ..
+ * start_pos[b] + q_len - 1) and the same tokens' queries attend to every
+ * cached token, themselves included: seq_lens[b] = start_pos[b] + q_len,
+ * which the caller keeps consistent (the two arrays are read on the device).
+ * The path is the one of "DeepSeek-V2: MLA Explained", "MLA Full Formulas"
+ * sections 2-3, in the absorbed form of its "Optimization Note".
+ *
+ * Results -- out, lse and every byte of the pool -- are bit for bit those of
+ * the two calls made in that order on one stream.  With bf16 activations on
+ * the DeepSeek-V3 head shape the append's per-token finalize (norm, rotation,
+ * store) and the decode's query absorption, which do not depend on each
+ * other, run as one launch.
+ *  arguments   as mla_cache_append (n_new = q_len) and mla_decode_absorbed
+ *  workspace   mla_decode_step_workspace_size bytes, 16-byte aligned: the
+ *              decode's workspace, then the append's
+ * Errors: those of the two calls (checked before anything is launched). */
+enum {
+    MLA_STEP_PROJECT = 1,          /* the append's projection x = W_kv,a h          */
+    MLA_STEP_FINALIZE_ABSORB = 2,  /* the append's finalize + the query absorption  */
+    MLA_STEP_SPLIT_KV = 4,         /* the decode's split-KV pass                     */
+    MLA_STEP_COMBINE = 8,          /* the decode's combine and W_UV                  */
+    MLA_STEP_ALL = 15
+};
+mla_status mla_decode_step_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                          int32_t d_model, int32_t num_splits, size_t* bytes);
+mla_status mla_decode_step(const mla_dims* dims, int32_t batch, int32_t q_len, int32_t d_model,
+                           const void* h, const void* w_kv_a, const void* kv_norm_gamma,
+                           float rms_eps, float rope_base, const int32_t* start_pos,
+                           const void* q_nope, const void* q_pe, const void* w_uk, const void* w_uv,
+                           void* cache_pool, float* cache_scale, const int32_t* block_table,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_splits,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+/* mla_decode_step restricted to the MLA_STEP_* stages in `stages` (run in the
+ * order above, each reading what the earlier ones left in the workspace and
+ * the pool), for per-kernel timing; all of them equal one mla_decode_step. */
+mla_status mla_decode_step_stages(const mla_dims* dims, int32_t batch, int32_t q_len, int32_t d_model,
+                                  const void* h, const void* w_kv_a, const void* kv_norm_gamma,
+                                  float rms_eps, float rope_base, const int32_t* start_pos,
+                                  const void* q_nope, const void* q_pe, const void* w_uk,
+                                  const void* w_uv, void* cache_pool, float* cache_scale,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* seq_lens, int32_t num_splits, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, uint32_t stages,
+                                  void* stream);
+
 /* ---- debug check of the device-side contract --------------------------------
  *
  * The decode and the append read block_table and seq_lens on the device

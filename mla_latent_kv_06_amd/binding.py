@@ -32,6 +32,7 @@ STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_BAD_SHAPE",
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 STAGE_ABSORB_Q, STAGE_SPLIT_KV, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 PREFILL_GATHER, PREFILL_DECOMPRESS, PREFILL_ATTEND, PREFILL_ALL = 1, 2, 4, 7
+STEP_PROJECT, STEP_FINALIZE_ABSORB, STEP_SPLIT_KV, STEP_COMBINE, STEP_ALL = 1, 2, 4, 8, 15
 
 DTYPE_CODES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 _TORCH_OF = {MLA_F32: (torch.float32,), MLA_BF16: (torch.bfloat16,),
@@ -43,7 +44,8 @@ EXPORTED = ("mla_status_string", "mla_last_error", "mla_cache_row_bytes",
             "mla_decode_absorbed_stages", "mla_query_workspace_size", "mla_query_project",
             "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_stages",
             "mla_decode_absorbed_noalloc", "mla_output_workspace_size", "mla_output_project",
-            "mla_decode_output_workspace_size", "mla_decode_output", "mla_check_block_table")
+            "mla_decode_output_workspace_size", "mla_decode_output", "mla_check_block_table",
+            "mla_decode_step_workspace_size", "mla_decode_step", "mla_decode_step_stages")
 
 
 class Dims(ctypes.Structure):
@@ -86,6 +88,14 @@ _lib.mla_cache_append_workspace_size.argtypes = [_DP, _I, _I, _I, ctypes.POINTER
 _lib.mla_cache_append.restype = ctypes.c_int
 _lib.mla_cache_append.argtypes = [_DP, _I, _I, _I, _P, _P, _P, ctypes.c_float, ctypes.c_float,
                                   _P, _I, _P, _P, _P, _P, _SZ, _P]
+_lib.mla_decode_step_workspace_size.restype = ctypes.c_int
+_lib.mla_decode_step_workspace_size.argtypes = [_DP, _I, _I, _I, _I, ctypes.POINTER(_SZ)]
+_lib.mla_decode_step_stages.restype = ctypes.c_int
+_lib.mla_decode_step_stages.argtypes = [_DP, _I, _I, _I, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P,
+                                        _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _SZ,
+                                        ctypes.c_uint32, _P]
+_lib.mla_decode_step.restype = ctypes.c_int
+_lib.mla_decode_step.argtypes = _lib.mla_decode_step_stages.argtypes[:-2] + [_P]
 _lib.mla_decode_default_splits.restype = _I
 _lib.mla_decode_default_splits.argtypes = [_DP, _I, _I]
 _lib.mla_decode_workspace_size.restype = ctypes.c_int
@@ -438,6 +448,43 @@ def append(dims: Dims, h, w_kv_a, kv_norm_gamma, block_table, start_pos, cache_p
         workspace.numel(), _stream(dev))
     _check(st, "mla_cache_append")
 
+
+
+def step_workspace_size(dims: Dims, batch: int, q_len: int, d_model: int, num_splits: int = 0) -> int:
+    n = _SZ(0)
+    _check(_lib.mla_decode_step_workspace_size(ctypes.byref(dims), batch, q_len, d_model, num_splits,
+                                               ctypes.byref(n)), "mla_decode_step_workspace_size")
+    return n.value
+
+
+def decode_step(dims: Dims, h, w_kv_a, kv_norm_gamma, start_pos, q_nope, q_pe, w_uk, w_uv,
+                cache_pool, cache_scale, block_table, seq_lens, num_splits: int = 0,
+                rms_eps: float = 1e-6, rope_base: float = 10000.0, out=None, lse=None,
+                workspace=None, stages: int = STEP_ALL, want_lse: bool = True):
+    """One decode step with its cache append (mla_decode_step[_stages]): the
+    q_len new tokens h [B, q_len, d] are appended at start_pos, then their
+    queries q_nope / q_pe attend over the cache (seq_lens = start_pos + q_len).
+    Other arguments as append() and decode().  Returns (out, lse)."""
+    act = _TORCH_OF[dims.act_dtype]
+    B, Sq, dev, out, lse = _decode_tensors(dims, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                                           block_table, seq_lens, out, lse, want_lse)
+    dc, R = dims.kv_lora_rank, dims.qk_rope_dim
+    d = h.shape[-1]
+    _need(h, "h", act, (B, Sq, d), dev)
+    _need(w_kv_a, "w_kv_a", act, (dc + R, d), dev)
+    _need(kv_norm_gamma, "kv_norm_gamma", act, (dc,), dev)
+    _need(start_pos, "start_pos", (torch.int32,), (B,), dev)
+    ws_bytes = step_workspace_size(dims, B, Sq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (torch.uint8,), None, dev)
+    st = _lib.mla_decode_step_stages(
+        ctypes.byref(dims), B, Sq, d, _ptr(h), _ptr(w_kv_a), _ptr(kv_norm_gamma), float(rms_eps),
+        float(rope_base), _ptr(start_pos), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+        _ptr(cache_pool), _ptr(cache_scale), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+        num_splits, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), stages, _stream(dev))
+    _check(st, "mla_decode_step_stages")
+    return out, lse
 
 
 def query_project(dims: Dims, h, w_dq, q_norm_gamma, w_uq, w_qr, start_pos,

@@ -133,12 +133,15 @@ bool append_uses_mfma(const mla_dims& d, int d_model) {
            d_model % 16 == 0;
 }
 
-mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
-                       const void* q_pe, const void* w_uk, const void* w_uv, const void* cache_pool,
-                       const float* cache_scale, const int32_t* block_table,
-                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_splits,
-                       void* out, float* lse, void* workspace, size_t workspace_bytes,
-                       unsigned stages, void* stream) {
+// Validates a decode call and fills its launch description; *empty: nothing
+// to launch (batch 0).
+mla_status decode_prepare(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
+                          const void* q_pe, const void* w_uk, const void* w_uv, const void* cache_pool,
+                          const float* cache_scale, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_splits,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          unsigned stages, void* stream, mla::DecodeLaunch& a, bool& mfma, bool& empty) {
+    empty = false;
     if (mla_status st = check_dims(dims); st != MLA_OK) return st;
     const mla_dims& d = *dims;
     if (batch < 0 || q_len < 1 || q_len > 1024)
@@ -147,7 +150,10 @@ mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const
         return fail(MLA_ERR_BAD_SHAPE, "num_splits=%d outside [0, %d]", num_splits, mla::kMaxSplits);
     if (stages == 0 || (stages & ~(unsigned)MLA_STAGE_ALL))
         return fail(MLA_ERR_BAD_SHAPE, "stages=0x%x: use MLA_STAGE_* bits", stages);
-    if (batch == 0) return ok();
+    if (batch == 0) {
+        empty = true;
+        return ok();
+    }
     if (max_blocks_per_seq < 1) return fail(MLA_ERR_BAD_SHAPE, "max_blocks_per_seq must be >= 1");
     // 0: balanced scheduling on the MFMA path, the default split count otherwise
     const int splits = (num_splits == 0 && !mla::is_v3_shape(d)) ? default_splits(batch, q_len)
@@ -164,7 +170,7 @@ mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const
     const DecodeWs ws = decode_ws(d, batch, q_len, num_splits);
     if (workspace_bytes < ws.total)
         return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu", workspace_bytes, ws.total);
-    const bool mfma = mla::is_v3_shape(d);
+    mfma = mla::is_v3_shape(d);
     if (mfma) {
         const void* ptrs[] = {q_nope, q_pe, w_uk, w_uv, cache_pool, out, workspace};
         for (const void* p : ptrs)
@@ -174,7 +180,7 @@ mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const
     } else if (!aligned16(workspace)) {
         return fail(MLA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
     }
-    mla::DecodeLaunch a;
+    a = mla::DecodeLaunch{};
     a.H = d.n_heads;
     a.DC = d.kv_lora_rank;
     a.DR = d.qk_rope_dim;
@@ -203,9 +209,28 @@ mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const
     a.part_o = base + ws.part_o;
     a.part_lse = reinterpret_cast<float*>(base + ws.part_lse);
     a.stream = static_cast<hipStream_t>(stream);
-    const hipError_t e = mfma ? mla::launch_decode_mfma(a, stages) : mla::launch_decode_generic(a, stages);
+    return ok();
+}
+
+mla_status launch_status(hipError_t e) {
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+mla_status decode_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
+                       const void* q_pe, const void* w_uk, const void* w_uv, const void* cache_pool,
+                       const float* cache_scale, const int32_t* block_table,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_splits,
+                       void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       unsigned stages, void* stream) {
+    mla::DecodeLaunch a;
+    bool mfma = false, empty = false;
+    if (mla_status st = decode_prepare(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                                       block_table, max_blocks_per_seq, seq_lens, num_splits, out, lse,
+                                       workspace, workspace_bytes, stages, stream, a, mfma, empty);
+        st != MLA_OK || empty)
+        return st;
+    return launch_status(mfma ? mla::launch_decode_mfma(a, stages) : mla::launch_decode_generic(a, stages));
 }
 
 // Query path: shape checks shared by the sizing call and the entry point.
@@ -444,6 +469,67 @@ mla_status noalloc_scratch(void** ptr) {
     return MLA_OK;
 }
 
+// Validates an append call and fills its launch description; *empty: nothing
+// to launch (no new token).
+mla_status append_prepare(const mla_dims* dims, int32_t batch, int32_t n_new, int32_t d_model,
+                          const void* h, const void* w_kv_a, const void* kv_norm_gamma, float rms_eps,
+                          float rope_base, const int32_t* block_table, int32_t max_blocks_per_seq,
+                          const int32_t* start_pos, void* cache_pool, float* cache_scale, void* workspace,
+                          size_t workspace_bytes, void* stream, mla::AppendLaunch& a, bool& mfma,
+                          bool& empty) {
+    empty = false;
+    if (mla_status st = check_dims(dims); st != MLA_OK) return st;
+    const mla_dims& d = *dims;
+    if (batch < 0 || n_new < 0 || d_model < 1 || d_model % 8)
+        return fail(MLA_ERR_BAD_SHAPE, "batch=%d n_new=%d d_model=%d (multiple of 8 required)", batch,
+                    n_new, d_model);
+    if (batch == 0 || n_new == 0) {
+        empty = true;
+        return ok();
+    }
+    if (!h || !w_kv_a || !kv_norm_gamma || !block_table || !start_pos || !cache_pool || !workspace)
+        return fail(MLA_ERR_NULL_POINTER, "h, w_kv_a, kv_norm_gamma, block_table, start_pos, "
+                                          "cache_pool and workspace are required");
+    if (d.cache_dtype == MLA_FP8_E4M3 && !cache_scale)
+        return fail(MLA_ERR_NULL_POINTER, "cache_scale is required for an FP8 cache");
+    if (max_blocks_per_seq < 1) return fail(MLA_ERR_BAD_SHAPE, "max_blocks_per_seq must be >= 1");
+    if (!(rms_eps >= 0.f) || !(rope_base > 0.f) || std::isinf(rope_base))
+        return fail(MLA_ERR_BAD_SHAPE, "rms_eps must be >= 0 and rope_base finite and > 0");
+    size_t need = 0;
+    mla_cache_append_workspace_size(dims, batch, n_new, d_model, &need);
+    if (workspace_bytes < need)
+        return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu", workspace_bytes, need);
+    mfma = append_uses_mfma(d, d_model);
+    if (mfma && (!aligned16(h) || !aligned16(w_kv_a)))
+        return fail(MLA_ERR_ALIGNMENT, "h and w_kv_a must be 16-byte aligned");
+    if (!aligned16(workspace)) return fail(MLA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+    a = mla::AppendLaunch{};
+    a.DC = d.kv_lora_rank;
+    a.DR = d.qk_rope_dim;
+    a.BS = d.block_size;
+    a.cache_dtype = d.cache_dtype;
+    a.act_dtype = d.act_dtype;
+    a.batch = batch;
+    a.n_new = n_new;
+    a.d_model = d_model;
+    a.h = h;
+    a.w_kv_a = w_kv_a;
+    a.gamma = kv_norm_gamma;
+    a.eps = rms_eps;
+    a.rope_base = rope_base;
+    a.block_table = block_table;
+    a.max_blocks = max_blocks_per_seq;
+    a.start_pos = start_pos;
+    a.pool = cache_pool;
+    a.pool_scale = cache_scale;
+    a.part = static_cast<float*>(workspace);
+    a.stream_gemm = mfma && append_streams(d, (long long)batch * n_new, d_model);
+    a.kc = mfma ? append_slices(d, (long long)batch * n_new, d_model) : 1;
+    a.kchunk = mfma ? mla::kAppendChunk : d_model;
+    a.stream = static_cast<hipStream_t>(stream);
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -492,55 +578,14 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t n_new, 
                             int32_t max_blocks_per_seq, const int32_t* start_pos, void* cache_pool,
                             float* cache_scale, void* workspace, size_t workspace_bytes,
                             void* stream) {
-    if (mla_status st = check_dims(dims); st != MLA_OK) return st;
-    const mla_dims& d = *dims;
-    if (batch < 0 || n_new < 0 || d_model < 1 || d_model % 8)
-        return fail(MLA_ERR_BAD_SHAPE, "batch=%d n_new=%d d_model=%d (multiple of 8 required)", batch,
-                    n_new, d_model);
-    if (batch == 0 || n_new == 0) return ok();
-    if (!h || !w_kv_a || !kv_norm_gamma || !block_table || !start_pos || !cache_pool || !workspace)
-        return fail(MLA_ERR_NULL_POINTER, "h, w_kv_a, kv_norm_gamma, block_table, start_pos, "
-                                          "cache_pool and workspace are required");
-    if (d.cache_dtype == MLA_FP8_E4M3 && !cache_scale)
-        return fail(MLA_ERR_NULL_POINTER, "cache_scale is required for an FP8 cache");
-    if (max_blocks_per_seq < 1) return fail(MLA_ERR_BAD_SHAPE, "max_blocks_per_seq must be >= 1");
-    if (!(rms_eps >= 0.f) || !(rope_base > 0.f) || std::isinf(rope_base))
-        return fail(MLA_ERR_BAD_SHAPE, "rms_eps must be >= 0 and rope_base finite and > 0");
-    size_t need = 0;
-    mla_cache_append_workspace_size(dims, batch, n_new, d_model, &need);
-    if (workspace_bytes < need)
-        return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu", workspace_bytes, need);
-    const bool mfma = append_uses_mfma(d, d_model);
-    if (mfma && (!aligned16(h) || !aligned16(w_kv_a)))
-        return fail(MLA_ERR_ALIGNMENT, "h and w_kv_a must be 16-byte aligned");
-    if (!aligned16(workspace)) return fail(MLA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
     mla::AppendLaunch a;
-    a.DC = d.kv_lora_rank;
-    a.DR = d.qk_rope_dim;
-    a.BS = d.block_size;
-    a.cache_dtype = d.cache_dtype;
-    a.act_dtype = d.act_dtype;
-    a.batch = batch;
-    a.n_new = n_new;
-    a.d_model = d_model;
-    a.h = h;
-    a.w_kv_a = w_kv_a;
-    a.gamma = kv_norm_gamma;
-    a.eps = rms_eps;
-    a.rope_base = rope_base;
-    a.block_table = block_table;
-    a.max_blocks = max_blocks_per_seq;
-    a.start_pos = start_pos;
-    a.pool = cache_pool;
-    a.pool_scale = cache_scale;
-    a.part = static_cast<float*>(workspace);
-    a.stream_gemm = mfma && append_streams(d, (long long)batch * n_new, d_model);
-    a.kc = mfma ? append_slices(d, (long long)batch * n_new, d_model) : 1;
-    a.kchunk = mfma ? mla::kAppendChunk : d_model;
-    a.stream = static_cast<hipStream_t>(stream);
-    const hipError_t e = mla::launch_append(a, mfma);
-    if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
+    bool mfma = false, empty = false;
+    if (mla_status st = append_prepare(dims, batch, n_new, d_model, h, w_kv_a, kv_norm_gamma, rms_eps,
+                                       rope_base, block_table, max_blocks_per_seq, start_pos, cache_pool,
+                                       cache_scale, workspace, workspace_bytes, stream, a, mfma, empty);
+        st != MLA_OK || empty)
+        return st;
+    return launch_status(mla::launch_append(a, mfma));
 }
 
 int32_t mla_decode_default_splits(const mla_dims* dims, int32_t batch, int32_t q_len) {
@@ -760,6 +805,89 @@ mla_status mla_prefill_stages(const mla_dims* dims, int32_t batch, int32_t q_len
     return prefill_impl(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
                         block_table, max_blocks_per_seq, seq_lens, out, lse, workspace,
                         workspace_bytes, stages, stream);
+}
+
+mla_status mla_decode_step_workspace_size(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                          int32_t d_model, int32_t num_splits, size_t* bytes) {
+    if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes is NULL");
+    size_t dec = 0, app = 0;
+    if (mla_status st = mla_decode_workspace_size(dims, batch, q_len, num_splits, &dec); st != MLA_OK)
+        return st;
+    if (mla_status st = mla_cache_append_workspace_size(dims, batch, q_len, d_model, &app); st != MLA_OK)
+        return st;
+    *bytes = align_up(dec, 256) + app;
+    return ok();
+}
+
+mla_status mla_decode_step_stages(const mla_dims* dims, int32_t batch, int32_t q_len, int32_t d_model,
+                                  const void* h, const void* w_kv_a, const void* kv_norm_gamma,
+                                  float rms_eps, float rope_base, const int32_t* start_pos,
+                                  const void* q_nope, const void* q_pe, const void* w_uk,
+                                  const void* w_uv, void* cache_pool, float* cache_scale,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* seq_lens, int32_t num_splits, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, uint32_t stages,
+                                  void* stream) {
+    if (stages == 0 || (stages & ~(uint32_t)MLA_STEP_ALL))
+        return fail(MLA_ERR_BAD_SHAPE, "stages=0x%x: use MLA_STEP_* bits", stages);
+    size_t need = 0;
+    if (mla_status st = mla_decode_step_workspace_size(dims, batch, q_len, d_model, num_splits, &need);
+        st != MLA_OK)
+        return st;
+    if (batch == 0) return ok();
+    if (!workspace) return fail(MLA_ERR_NULL_POINTER, "workspace is NULL");
+    if (workspace_bytes < need)
+        return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes=%zu < %zu", workspace_bytes, need);
+    size_t dec_bytes = 0;
+    mla_decode_workspace_size(dims, batch, q_len, num_splits, &dec_bytes);
+    dec_bytes = align_up(dec_bytes, 256);
+    char* ws = static_cast<char*>(workspace);
+    mla::AppendLaunch ap;
+    bool app_mfma = false, app_empty = false;
+    if (mla_status st = append_prepare(dims, batch, q_len, d_model, h, w_kv_a, kv_norm_gamma, rms_eps,
+                                       rope_base, block_table, max_blocks_per_seq, start_pos, cache_pool,
+                                       cache_scale, ws + dec_bytes, workspace_bytes - dec_bytes, stream, ap,
+                                       app_mfma, app_empty);
+        st != MLA_OK)
+        return st;
+    mla::DecodeLaunch dp;
+    bool dec_mfma = false, dec_empty = false;
+    if (mla_status st = decode_prepare(dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale,
+                                       block_table, max_blocks_per_seq, seq_lens, num_splits, out, lse, ws,
+                                       dec_bytes, MLA_STAGE_ALL, stream, dp, dec_mfma, dec_empty);
+        st != MLA_OK)
+        return st;
+    auto decode = [&](unsigned st) {
+        return dec_mfma ? mla::launch_decode_mfma(dp, st) : mla::launch_decode_generic(dp, st);
+    };
+    if (stages & MLA_STEP_PROJECT)
+        if (hipError_t e = mla::launch_append_project(ap, app_mfma); e != hipSuccess) return launch_status(e);
+    if (stages & MLA_STEP_FINALIZE_ABSORB) {
+        if (dec_mfma) {                  // bf16 activations, V3 shape: one launch
+            if (hipError_t e = mla::launch_finalize_absorb(ap, dp); e != hipSuccess) return launch_status(e);
+        } else {
+            if (hipError_t e = mla::launch_append_finalize(ap); e != hipSuccess) return launch_status(e);
+            if (hipError_t e = decode(MLA_STAGE_ABSORB_Q); e != hipSuccess) return launch_status(e);
+        }
+    }
+    const unsigned rest = ((stages & MLA_STEP_SPLIT_KV) ? MLA_STAGE_SPLIT_KV : 0u) |
+                          ((stages & MLA_STEP_COMBINE) ? MLA_STAGE_COMBINE : 0u);
+    if (rest) return launch_status(decode(rest));
+    return ok();
+}
+
+mla_status mla_decode_step(const mla_dims* dims, int32_t batch, int32_t q_len, int32_t d_model,
+                           const void* h, const void* w_kv_a, const void* kv_norm_gamma,
+                           float rms_eps, float rope_base, const int32_t* start_pos,
+                           const void* q_nope, const void* q_pe, const void* w_uk, const void* w_uv,
+                           void* cache_pool, float* cache_scale, const int32_t* block_table,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_splits,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    return mla_decode_step_stages(dims, batch, q_len, d_model, h, w_kv_a, kv_norm_gamma, rms_eps, rope_base,
+                                  start_pos, q_nope, q_pe, w_uk, w_uv, cache_pool, cache_scale, block_table,
+                                  max_blocks_per_seq, seq_lens, num_splits, out, lse, workspace,
+                                  workspace_bytes, MLA_STEP_ALL, stream);
 }
 
 }  // extern "C"

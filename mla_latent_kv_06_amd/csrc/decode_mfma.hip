@@ -25,6 +25,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "append_finalize.hpp"
 
 namespace mla {
 namespace {
@@ -98,7 +99,8 @@ constexpr int WT_ROWB = 288;    // bytes per staged W_UK row
 // consecutive rows start 68 dwords apart and cover all 64 banks
 constexpr int QT_ROWB = 272;
 
-__global__ __launch_bounds__(256) void absorb_q_kernel(
+__device__ __forceinline__ void absorb_q_block(
+    int bid,                                    // workgroup of the grid above
     const unsigned short* __restrict__ q_nope,  // [R][H][128]
     const unsigned short* __restrict__ q_pe,    // [R][H][64]
     const unsigned short* __restrict__ w_uk,    // [H][128][512]
@@ -106,7 +108,6 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
     int R) {
     __shared__ __attribute__((aligned(16))) unsigned char wt[128 * WT_ROWB];
     __shared__ __attribute__((aligned(16))) unsigned char qt[64 * QT_ROWB];
-    const int bid = blockIdx.x;
     const int h = bid % H;
     const int cb = (bid / H) & 3;
     const int rb = bid / (H * 4);
@@ -204,6 +205,43 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
             if (r < R) *reinterpret_cast<u32x4*>(qbuf + ((size_t)r * H + h) * D + DC + c8 * 8) = pe[k];
         }
     }
+}
+
+__global__ __launch_bounds__(256) void absorb_q_kernel(const unsigned short* __restrict__ q_nope,
+                                                      const unsigned short* __restrict__ q_pe,
+                                                      const unsigned short* __restrict__ w_uk,
+                                                      unsigned short* __restrict__ qbuf, int R) {
+    absorb_q_block(blockIdx.x, q_nope, q_pe, w_uk, qbuf, R);
+}
+
+// The cache append's finalize (workgroups 0 .. T-1, one token each) and the
+// query absorption (the rest) in one launch: they do not depend on each
+// other, and the finalize's 64-odd latency-bound workgroups then run beside
+// the absorption's bandwidth-bound ones instead of after them.
+struct FinalizeArgs {
+    const float* part;
+    int kc, T, DC, DR;
+    const void* gamma;
+    float eps, rope_base;
+    const int* block_table;
+    int max_blocks;
+    const int* start_pos;
+    int n_new, BSZ;
+    void* pool;
+    float* pool_scale;
+};
+template <int CDT>
+__global__ __launch_bounds__(256) void finalize_absorb_kernel(FinalizeArgs f,
+                                                              const unsigned short* __restrict__ q_nope,
+                                                              const unsigned short* __restrict__ q_pe,
+                                                              const unsigned short* __restrict__ w_uk,
+                                                              unsigned short* __restrict__ qbuf, int R) {
+    if ((int)blockIdx.x < f.T)
+        append_finalize_token<MLA_BF16, CDT>(blockIdx.x, f.part, f.kc, f.T, f.DC, f.DR, f.gamma, f.eps,
+                                             f.rope_base, f.block_table, f.max_blocks, f.start_pos,
+                                             f.n_new, f.BSZ, f.pool, f.pool_scale);
+    else
+        absorb_q_block(blockIdx.x - f.T, q_nope, q_pe, w_uk, qbuf, R);
 }
 
 // ---------------------------------------------------------------------------
@@ -1742,6 +1780,23 @@ bool is_v3_shape(const mla_dims& d) {
     return d.n_heads == H && d.kv_lora_rank == DC && d.qk_rope_dim == DR && d.qk_nope_dim == 128 &&
            d.v_head_dim == 128 && d.block_size == BS && d.act_dtype == MLA_BF16 &&
            (d.cache_dtype == MLA_BF16 || d.cache_dtype == MLA_FP8_E4M3);
+}
+
+hipError_t launch_finalize_absorb(const AppendLaunch& ap, const DecodeLaunch& dp) {
+    const int T = ap.batch * ap.n_new, R = dp.batch * dp.q_len;
+    const int n_abs = R > 0 ? H * 4 * ((R + 63) / 64) : 0;
+    if (T + n_abs == 0) return hipSuccess;
+    const FinalizeArgs f{ap.part, ap.kc, T, ap.DC, ap.DR, ap.gamma, ap.eps, ap.rope_base, ap.block_table,
+                         ap.max_blocks, ap.start_pos, ap.n_new, ap.BS, ap.pool, ap.pool_scale};
+    const auto* qn = static_cast<const unsigned short*>(dp.q_nope);
+    const auto* qp = static_cast<const unsigned short*>(dp.q_pe);
+    const auto* wk = static_cast<const unsigned short*>(dp.w_uk);
+    auto* qbuf = static_cast<unsigned short*>(dp.qbuf);
+    if (ap.cache_dtype == MLA_FP8_E4M3)
+        finalize_absorb_kernel<MLA_FP8_E4M3><<<T + n_abs, 256, 0, ap.stream>>>(f, qn, qp, wk, qbuf, R);
+    else
+        finalize_absorb_kernel<MLA_BF16><<<T + n_abs, 256, 0, ap.stream>>>(f, qn, qp, wk, qbuf, R);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_mfma(const DecodeLaunch& a, unsigned stages) {

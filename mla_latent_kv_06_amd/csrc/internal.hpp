@@ -65,6 +65,13 @@ bool is_v3_shape(const mla_dims& d);
 hipError_t launch_decode_mfma(const DecodeLaunch& a, unsigned stages);
 hipError_t launch_decode_generic(const DecodeLaunch& a, unsigned stages);
 hipError_t launch_append(const AppendLaunch& a, bool mfma_gemm);
+// the append's two launches on their own: the projection into the partial
+// sums, then the per-token finalize (launch_append runs both)
+hipError_t launch_append_project(const AppendLaunch& a, bool mfma_gemm);
+hipError_t launch_append_finalize(const AppendLaunch& a);
+// the append's finalize and the decode's query absorption as one launch
+// (bf16 activations, V3 decode shape; they are independent of each other)
+hipError_t launch_finalize_absorb(const AppendLaunch& ap, const DecodeLaunch& dp);
 hipError_t launch_check_block_table(const int* block_table, int batch, int max_blocks, const int* seq_lens,
                                     int block_size, int num_blocks, int* report, hipStream_t stream);
 
