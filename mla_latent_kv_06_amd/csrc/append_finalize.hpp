@@ -39,6 +39,73 @@ __device__ __forceinline__ void append_finalize_token(
     // Loads below are unconditional, at clamped (valid) addresses, with the
     // unused values selected away afterwards: a load under a branch would be
     // waited for inside that branch, one round trip each.
+    if (Dout % 4 == 0 && DC % 2 == 0 && Dout <= 4 * 256 && kc_count <= 32) {
+        // common shapes: thread tid owns outputs 4 tid .. 4 tid + 3 (16-byte
+        // partial loads, every one in flight at once; a rotary pair (x[2k],
+        // x[2k+1]) sits in one thread)
+        const int o0 = 4 * tid, oc = min(o0, Dout - 4);
+        const float keep_o = o0 < Dout ? 1.f : 0.f;
+        f32x4 pv[32];
+#pragma unroll
+        for (int kc = 0; kc < 32; ++kc)
+            pv[kc] = *reinterpret_cast<const f32x4*>(part + ((size_t)min(kc, kc_count - 1) * T + t) * Dout + oc);
+        float g4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            g4[e] = load_act<ADT>(gamma, min(o0 + e, DC - 1)) * (o0 + e < DC ? 1.f : 0.f);
+        if (tid < DR / 2) {
+            const double ang = (double)pos * pow((double)rope_base, -2.0 * tid / (double)DR);
+            const double turns = rint(ang * 0.15915494309189535);
+            sincosf((float)fma(-turns, 6.283185307179586, ang), &rsn[tid], &rcs[tid]);
+        }
+        float x4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 32; ++kc) {
+            const float keep = kc < kc_count ? keep_o : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x4[e] += pv[kc][e] * keep;
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (o0 + e < DC) ss += x4[e] * x4[e];
+        ss = block_sum(ss, red);                // also publishes rsn[], rcs[]
+        const float inv = 1.0f / sqrtf(ss / (float)DC + eps);
+        float yo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int o = o0 + e;
+            if (o < DC) {
+                yo[e] = x4[e] * inv * g4[e];
+            } else {
+                const int k = min((o - DC) >> 1, 127);
+                const float x0 = x4[e & ~1], x1 = x4[e | 1];
+                yo[e] = (e & 1) ? x0 * rsn[k] + x1 * rcs[k] : x0 * rcs[k] - x1 * rsn[k];
+            }
+        }
+        if constexpr (CDT == MLA_FP8_E4M3) {
+            float amax = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(yo[e]) * keep_o);
+            amax = block_max(amax, red);
+            const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+            unsigned int codes = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) codes |= (unsigned int)f32_to_e4m3_rne_sat(yo[e] / sc) << (8 * e);
+            if (o0 < Dout)
+                *reinterpret_cast<unsigned int*>(static_cast<unsigned char*>(pool) + phys * Dout + o0) = codes;
+            if (tid == 0) pool_scale[phys] = sc;
+        } else if (o0 < Dout) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (CDT == MLA_BF16)
+                    store_act<CDT>(pool, bf16_cache_offset(phys, o0 + e, Dout, BSZ), yo[e]);
+                else
+                    store_act<CDT>(pool, phys * Dout + o0 + e, yo[e]);
+            }
+        }
+        return;
+    }
     constexpr int U = 5;                        // outputs per thread: o = tid + 256 u
     float gm[U];
 #pragma unroll

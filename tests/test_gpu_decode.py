@@ -158,11 +158,15 @@ def test_edge_lengths(L, splits):
         assert np.all(out[~vis] == 0) and np.all(np.isneginf(lse[~vis]))
 
 
-@pytest.mark.parametrize("q_len,lo,hi,batch", [(1, 64, 700, 100), (2, 1, 300, 40)])
+@pytest.mark.parametrize("q_len,lo,hi,batch", [(1, 64, 700, 100), (2, 1, 300, 40), (3, 1, 400, 20),
+                                                (8, 5, 260, 9), (9, 1, 200, 6)])
 def test_balanced_schedule_ragged(q_len, lo, hi, batch):
-    """Balanced scheduling (num_splits 0): the concatenated tiles of all rows
-    are cut into equal ranges, so workgroups cover several short rows or
-    pieces of rows.  Every row is checked against the oracle on 8 heads."""
+    """Balanced scheduling (num_splits 0): the concatenated tiles of all
+    entries (rows; sequences when 1 < q_len <= 8, walked by one workgroup per
+    query row) are cut into equal ranges, so workgroups cover several short
+    entries or pieces of entries.  q_len 3 and 8 run the sequence form with
+    80 and 32 ranges; q_len 9 the row form.  Every row is checked against the
+    oracle on 8 heads."""
     wl = MID.replace(name="v3_balanced", batch=batch, q_len=q_len, ctx_lo=lo, ctx_hi=hi)
     announce("v3_balanced", "q_len", q_len, "batch", batch, "ctx", lo, hi)
     case = build_case(wl)
