@@ -527,3 +527,34 @@ def query_project(dims: Dims, h, w_dq, q_norm_gamma, w_uq, w_qr, start_pos,
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev))
     _check(st, "mla_query_project")
     return q_nope, q_pe
+
+
+# ---- streaming-read probe (include/mla_probe.h; a separate library) -----------
+
+PROBE_SINK_BYTES = 8192
+_probe = None
+
+
+def probe_read(buf, sink=None):
+    """Enqueue libmla_probe's streaming read of every byte of the contiguous
+    device tensor `buf` on torch's current stream; returns the sink tensor
+    (allocated here when not given)."""
+    global _probe
+    if _probe is None:
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_probe.so")
+        if not os.path.exists(path):
+            raise ImportError(f"libmla_probe.so not found at {path}; build it with "
+                              "`python -m mla_latent_kv_06_amd.build`")
+        lp = ctypes.CDLL(path)
+        lp.mla_probe_read.restype = ctypes.c_int
+        lp.mla_probe_read.argtypes = [_P, _SZ, _P, _P]
+        _probe = lp
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("probe_read: buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(PROBE_SINK_BYTES, dtype=torch.uint8, device=buf.device)
+    st = _probe.mla_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                               _stream(buf.device))
+    if st != 0:
+        raise RuntimeError(f"mla_probe_read failed with status {st}")
+    return sink

@@ -3,7 +3,9 @@
     python -m mla_latent_kv_06_amd.build [--verbose]
 
 Every .hip file under csrc/ is compiled to an object in _build/, then linked
-into mla_latent_kv_06_amd/libmla.so.  Always rebuilds (no staleness check).
+into mla_latent_kv_06_amd/libmla.so.  The streaming-read probe (probe/, a
+measurement yardstick, not part of the attention path) becomes
+mla_latent_kv_06_amd/libmla_probe.so.  Always rebuilds (no staleness check).
 """
 
 from __future__ import annotations
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
+PROBE_SRC = os.path.join(PKG, "probe", "read_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libmla_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -71,8 +75,11 @@ def build(verbose: bool = False) -> str:
     srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
     objs = [os.path.join(BUILD, f[:-4] + ".o") for f in srcs]
     cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(srcs, objs)]
+    probe_tmp = PROBE_LIB + ".tmp"
+    cmds.append([HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", probe_tmp])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
+    os.replace(probe_tmp, PROBE_LIB)
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

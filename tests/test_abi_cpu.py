@@ -36,6 +36,26 @@ def test_header_functions_are_exported():
     assert not missing, missing
 
 
+def test_probe_library_exports_and_validates():
+    """libmla_probe (the streaming-read yardstick) exports what its header
+    declares and rejects bad arguments before touching a GPU."""
+    plib = os.path.join(ROOT, "mla_latent_kv_06_amd", "libmla_probe.so")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mla_probe.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+    out = subprocess.run(["nm", "-D", "--defined-only", plib], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert declared == ["mla_probe_read"] and set(declared) <= exported
+    lp = ctypes.CDLL(plib)
+    lp.mla_probe_read.restype = ctypes.c_int
+    lp.mla_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert lp.mla_probe_read(None, 16, ctypes.c_void_p(4096), None) == 1
+    assert lp.mla_probe_read(ctypes.c_void_p(4096), 16, None, None) == 1
+    assert lp.mla_probe_read(ctypes.c_void_p(4096), 24, ctypes.c_void_p(4096), None) == 2
+    assert lp.mla_probe_read(ctypes.c_void_p(4104), 16, ctypes.c_void_p(4096), None) == 4
+    assert lp.mla_probe_read(ctypes.c_void_p(4096), 0, ctypes.c_void_p(4096), None) == 0
+
+
 @pytest.fixture(scope="module")
 def b():
     from mla_latent_kv_06_amd import binding
