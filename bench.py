@@ -336,20 +336,23 @@ def main():
     k_avg_s = float(k_ms.mean()) / 1e3
 
     # Reference for the roofline on this GPU: libmla_probe's streaming read
-    # (16-byte loads, 512 workgroups, each over one contiguous range) of the
-    # layers' pools in turn, each larger than the 256 MB last-level cache;
-    # median of 12 reads after 2 warm-up reads, outside the timed region.
-    sink = b.probe_read(layers[0].pool)
+    # (16-byte loads, 512 workgroups, each over one contiguous range) of a
+    # 1 GiB buffer (four times the 256 MB last-level cache, whatever the
+    # workload's pool size); median of 12 reads after 2 warm-ups, outside the
+    # timed region.
+    probe_buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    sink = b.probe_read(probe_buf)
     s_ms = []
     for i in range(14):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        b.probe_read(layers[i % len(layers)].pool, sink)
+        b.probe_read(probe_buf, sink)
         e1.record(stream)
         torch.cuda.synchronize()
         s_ms.append(e0.elapsed_time(e1))
-    pool_bytes = layers[0].pool.numel() * layers[0].pool.element_size()
-    stream_gbs = pool_bytes / (float(np.median(s_ms[2:])) / 1e3) / 1e9
+    del probe_buf
+    probe_bytes = 1 << 30
+    stream_gbs = probe_bytes / (float(np.median(s_ms[2:])) / 1e3) / 1e9
 
     tokens_per_step = B * Sq
     value = tokens_per_step / (ms_step / 1e3)
@@ -371,7 +374,7 @@ def main():
     log(f"cache {cache_bytes / 1e6:.1f} MB: kernel {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s), "
         f"step {step_gbs:.0f} GB/s; kernel {flops / k_avg_s / 1e12:.0f} TFLOP/s "
         f"({flops / k_avg_s / 1e12 / mfma_peak:.1%} of the {mfma_peak:.0f} TFLOP/s MFMA peak)")
-    log(f"streaming read of a pool (libmla_probe) on this GPU: {stream_gbs:.0f} GB/s; the split-KV kernel reaches "
+    log(f"streaming read of 1 GiB (libmla_probe) on this GPU: {stream_gbs:.0f} GB/s; the split-KV kernel reaches "
         f"{achieved / stream_gbs:.1%} of it")
 
     result = {
