@@ -369,10 +369,14 @@ __device__ __forceinline__ void convert_tile_fp8(lds_u8* lstage, lds_u8* ltile, 
 //    Qs (f + e) + s, Qs (f + 1 + e) + s, .. Qs (l + e) + s, f / l being the
 //    ranges holding its entry's first / last tile; all below kNumCUs + R.
 
+// Tiles seen by row s of a sequence of len tokens (q_len query rows).
+__device__ __forceinline__ int tiles_from_len(int len, int q_len, int s) {
+    const int n_vis = len - q_len + s + 1;
+    return n_vis > 0 ? (n_vis + BS - 1) / BS : 0;
+}
 __device__ __forceinline__ int row_tiles(const int* __restrict__ seq_lens, int q_len, int r) {
     const int b = r / q_len;
-    const int n_vis = seq_lens[b] - q_len + (r - b * q_len) + 1;
-    return n_vis > 0 ? (n_vis + BS - 1) / BS : 0;
+    return tiles_from_len(seq_lens[b], q_len, r - b * q_len);
 }
 
 // Workgroups of the balanced schedule for T tiles: at most one per compute
@@ -391,6 +395,9 @@ __device__ __forceinline__ int entry_tiles(const int* __restrict__ seq_lens, int
     return q_len <= kPairQ ? row_tiles(seq_lens, q_len, e * q_len + q_len - 1) : row_tiles(seq_lens, q_len, e);
 }
 __device__ __forceinline__ int entry_row(int q_len, int e, int s) { return q_len <= kPairQ ? e * q_len + s : e; }
+// Sequence of entry e, and the row (within its sequence) whose tiles are the entry's.
+__device__ __forceinline__ int entry_seq(int q_len, int e) { return q_len <= kPairQ ? e : e / q_len; }
+__device__ __forceinline__ int entry_last_s(int q_len, int e) { return q_len <= kPairQ ? q_len - 1 : e % q_len; }
 // Ranges for T entry tiles on `grid` workgroups (a multiple of the 8 XCDs):
 // each XCD runs ceil(G / 8) ranges x Qs rows, at most grid / 8 workgroups.
 __device__ __forceinline__ long long balanced_groups(long long grid, long long T, int Qs) {
@@ -405,16 +412,22 @@ __device__ __forceinline__ int group_of_tile(long long t, long long T, long long
 
 // Block-wide scan of entry tile counts: thread tid owns entries [tid*per,
 // tid*per+per) (per = ceil(E / 256)).  Returns T; *excl / *mine receive the
-// tiles before this thread's entries and in them.  sc: 260 ints of LDS scratch.
+// tiles before this thread's entries and in them, *len0 the sequence length
+// of its first entry (when it has one).  sc: 260 ints of LDS scratch.
 template <typename LdsInt>
 __device__ __forceinline__ int scan_entry_tiles(const int* __restrict__ seq_lens, int q_len, int E,
-                                                LdsInt sc, int* excl, int* mine) {
+                                                LdsInt sc, int* excl, int* mine, int* len0) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int per = (E + 255) / 256;
     int local = 0;
+    *len0 = 0;
     for (int k = 0; k < per; ++k) {
         const int e = tid * per + k;
-        if (e < E) local += entry_tiles(seq_lens, q_len, e);
+        if (e < E) {
+            const int len = seq_lens[entry_seq(q_len, e)];
+            if (k == 0) *len0 = len;
+            local += tiles_from_len(len, q_len, entry_last_s(q_len, e));
+        }
     }
     int incl = local;
 #pragma unroll
@@ -439,6 +452,7 @@ __device__ __forceinline__ int scan_entry_tiles(const int* __restrict__ seq_lens
 // pieces) share an L2.
 struct BalancedWalk {
     int grp, s, rng_a, rng_b, cur_e, cur_es;
+    int len_e, len;                      // sequence length of entry len_e, known from the scan
 };
 // Sets up the walk; false: this workgroup has nothing to do (uniform).
 template <typename LdsInt>
@@ -446,8 +460,8 @@ __device__ __forceinline__ bool balanced_start(const int* __restrict__ seq_lens,
                                                LdsInt sc, BalancedWalk& wk) {
     const int tid = threadIdx.x;
     const int Qs = sched_qs(q_len), E = R / Qs;
-    int excl, mine;
-    const int T = scan_entry_tiles(seq_lens, q_len, E, sc, &excl, &mine);
+    int excl, mine, len0;
+    const int T = scan_entry_tiles(seq_lens, q_len, E, sc, &excl, &mine, &len0);
     const long long G = balanced_groups(gridDim.x, T, Qs);
     const int per = (int)((G + 7) / 8);
     const int bx = blockIdx.x & 7, bk = blockIdx.x >> 3;
@@ -459,15 +473,21 @@ __device__ __forceinline__ bool balanced_start(const int* __restrict__ seq_lens,
     wk.rng_b = (int)((long long)(g + 1) * T / G);
     wk.cur_e = 0;
     wk.cur_es = 0;
+    wk.len_e = -1;
+    wk.len = 0;
     if (wk.rng_a < wk.rng_b && excl <= wk.rng_a && wk.rng_a < excl + mine) {
+        // this thread's entries hold the range's first tile; with one entry
+        // per thread (E <= 256) its tiles and length came with the scan
         const int pe = (E + 255) / 256;
         int es = excl;
         for (int k = 0; k < pe; ++k) {
             const int e = tid * pe + k;
-            const int nt = e < E ? entry_tiles(seq_lens, q_len, e) : 0;
+            const int len = pe == 1 ? len0 : e < E ? seq_lens[entry_seq(q_len, e)] : 0;
+            const int nt = pe == 1 ? mine : e < E ? tiles_from_len(len, q_len, entry_last_s(q_len, e)) : 0;
             if (wk.rng_a < es + nt) {
                 sc[260] = e;
                 sc[261] = es;
+                sc[262] = len;
                 break;
             }
             es += nt;
@@ -477,19 +497,23 @@ __device__ __forceinline__ bool balanced_start(const int* __restrict__ seq_lens,
     if (wk.rng_a < wk.rng_b) {
         wk.cur_e = sc[260];
         wk.cur_es = sc[261];
+        wk.len_e = wk.cur_e;
+        wk.len = sc[262];
     }
     __syncthreads();                     // scratch read before the caller reuses it
     return true;
 }
-// The walk's next piece (row, tiles [t0, t1), slot); false when done.  A row
-// that sees none of a range's tiles gets log-sum-exp -inf in its slot.
+// The walk's next piece (row, tiles [t0, t1), slot, and len, the length of
+// the row's sequence); false when done.  A row that sees none of a range's
+// tiles gets log-sum-exp -inf in its slot.
 __device__ __forceinline__ bool balanced_next(BalancedWalk& wk, const int* __restrict__ seq_lens, int q_len,
                                               int R, float* __restrict__ part_lse, int& row, int& t0,
-                                              int& t1, int& slot) {
+                                              int& t1, int& slot, int& len) {
     const int Qs = sched_qs(q_len), E = R / Qs;
     while (wk.cur_es < wk.rng_b && wk.cur_e < E) {
         const int e = wk.cur_e, es = wk.cur_es;
-        const int nt = entry_tiles(seq_lens, q_len, e);
+        len = e == wk.len_e ? wk.len : seq_lens[entry_seq(q_len, e)];
+        const int nt = tiles_from_len(len, q_len, entry_last_s(q_len, e));
         wk.cur_e += 1;
         wk.cur_es += nt;
         const int lo = max(wk.rng_a, es) - es, hi = min(wk.rng_b, es + nt) - es;
@@ -497,7 +521,7 @@ __device__ __forceinline__ bool balanced_next(BalancedWalk& wk, const int* __res
             row = entry_row(q_len, e, wk.s);
             slot = Qs * (wk.grp + e) + wk.s;
             t0 = lo;
-            t1 = min(hi, row_tiles(seq_lens, q_len, row));
+            t1 = min(hi, tiles_from_len(len, q_len, row - (row / q_len) * q_len));
             if (t0 < t1) return true;
             if (threadIdx.x < H) part_lse[(size_t)slot * H + threadIdx.x] = kNegInf;
         }
@@ -538,13 +562,14 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     bool fixed_pending = num_splits > 0;
     if (num_splits == 0 && !balanced_start(seq_lens, q_len, R, reinterpret_cast<MLA_LDS int*>(smem), wk))
         return;                          // uniform: the whole workgroup leaves
-    auto next_piece = [&](int& row, int& t0, int& t1, int& slot) -> bool {
+    auto next_piece = [&](int& row, int& t0, int& t1, int& slot, int& len) -> bool {
         if (num_splits > 0) {
             if (!fixed_pending) return false;
             fixed_pending = false;
             row = blockIdx.x / num_splits;
             const int split = blockIdx.x - row * num_splits;
-            const int n_tiles = row_tiles(seq_lens, q_len, row);
+            len = seq_lens[row / q_len];
+            const int n_tiles = tiles_from_len(len, q_len, row - (row / q_len) * q_len);
             const int tps = (n_tiles + num_splits - 1) / num_splits;
             t0 = split * tps;
             t1 = min(n_tiles, t0 + tps);
@@ -555,14 +580,14 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
             }
             return true;
         }
-        return balanced_next(wk, seq_lens, q_len, R, part_lse, row, t0, t1, slot);
+        return balanced_next(wk, seq_lens, q_len, R, part_lse, row, t0, t1, slot, len);
     };
 
-    int row, t0, t1, slot;
-    for (int piece = 0; next_piece(row, t0, t1, slot); ++piece) {
+    int row, t0, t1, slot, seq_len;
+    for (int piece = 0; next_piece(row, t0, t1, slot, seq_len); ++piece) {
         if (piece > 0) __syncthreads();      // the previous piece's epilogue is done with LDS
         const int b = row / q_len, s = row - b * q_len;
-        const int n_vis = seq_lens[b] - q_len + s + 1;
+        const int n_vis = seq_len - q_len + s + 1;
         float* lse_dst = part_lse + (size_t)slot * H;
         const int* btab = block_table + (size_t)b * max_blocks;
 
@@ -974,13 +999,14 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
     bool fixed_pending = num_splits > 0;
     if (num_splits == 0 && !balanced_start(seq_lens, q_len, R, reinterpret_cast<MLA_LDS int*>(smem), wk))
         return;                          // uniform: the whole workgroup leaves
-    auto next_piece = [&](int& row, int& t0, int& t1, int& slot) -> bool {
+    auto next_piece = [&](int& row, int& t0, int& t1, int& slot, int& len) -> bool {
         if (num_splits > 0) {
             if (!fixed_pending) return false;
             fixed_pending = false;
             row = blockIdx.x / num_splits;
             const int split = blockIdx.x - row * num_splits;
-            const int n_tiles = row_tiles(seq_lens, q_len, row);
+            len = seq_lens[row / q_len];
+            const int n_tiles = tiles_from_len(len, q_len, row - (row / q_len) * q_len);
             const int tps = (n_tiles + num_splits - 1) / num_splits;
             t0 = split * tps;
             t1 = min(n_tiles, t0 + tps);
@@ -991,15 +1017,15 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
             }
             return true;
         }
-        return balanced_next(wk, seq_lens, q_len, R, part_lse, row, t0, t1, slot);
+        return balanced_next(wk, seq_lens, q_len, R, part_lse, row, t0, t1, slot, len);
     };
 
     lds_u8* pbuf = smem + P_OFF;
-    int row, t0, t1, pslot;
-    for (int piece = 0; next_piece(row, t0, t1, pslot); ++piece) {
+    int row, t0, t1, pslot, seq_len;
+    for (int piece = 0; next_piece(row, t0, t1, pslot, seq_len); ++piece) {
         if (piece > 0) __syncthreads();      // the previous piece's epilogue is done with LDS
         const int b = row / q_len, s = row - b * q_len;
-        const int n_vis = seq_lens[b] - q_len + s + 1;
+        const int n_vis = seq_len - q_len + s + 1;
         float* lse_dst = part_lse + (size_t)pslot * H;
         const int* btab = block_table + (size_t)b * max_blocks;
         // halves hfirst .. hlast of the row hold the piece's visible tokens;
