@@ -87,6 +87,18 @@ __device__ __forceinline__ void static_for(F&& f) {
 // 1. q absorption
 // ---------------------------------------------------------------------------
 
+// The absorbed queries [q_lat ; q_pe] (576 bf16 per row and head) are stored
+// in the order the split-KV kernels load them as MFMA B fragments: wave w of
+// a workgroup holds heads 32 w .. 32 w + 31, and its K-step ks (channels
+// 16 ks .. +16) is 64 lanes x 8 channels, lane hf * 32 + (head % 32) taking
+// channels 16 ks + 8 hf .. +8.  So each fragment load is one contiguous
+// 1 KB read.  Element offset of 8 channels c .. c + 7 (c a multiple of 8) of
+// row r, head h:
+__device__ __forceinline__ size_t q_frag_offset(int r, int h, int c) {
+    return (((size_t)r * 4 + (h >> 5)) * 36 + (c >> 4)) * 512 + (((c >> 3) & 1) * 32 + (h & 31)) * 8;
+}
+static_assert(H == 128 && D == 576, "q_frag_offset assumes 4 head groups of 32 and 36 K-steps");
+
 // grid: H * 4 * ceil(R / 64) workgroups of 256 threads.  Workgroup (h, cb, rb)
 // produces q_lat[rb*64 .. +64][h][cb*128 .. +128]: q_lat^T = W_UK[h]^T q_nope^T
 // with W_UK[h][:, cb*128 .. +128] staged in LDS as [n][col] rows of 288 bytes
@@ -104,11 +116,16 @@ __device__ __forceinline__ void absorb_q_block(
     const unsigned short* __restrict__ q_nope,  // [R][H][128]
     const unsigned short* __restrict__ q_pe,    // [R][H][64]
     const unsigned short* __restrict__ w_uk,    // [H][128][512]
-    unsigned short* __restrict__ qbuf,          // [R][H][576]
+    unsigned short* __restrict__ qbuf,          // [R][H][576], fragment order (q_frag_offset)
     int R) {
     __shared__ __attribute__((aligned(16))) unsigned char wt[128 * WT_ROWB];
     __shared__ __attribute__((aligned(16))) unsigned char qt[64 * QT_ROWB];
-    const int h = bid % H;
+    // head h = 16 (bid % 8) + (bid / 8) % 16: workgroup ids that share bid % 8
+    // run on one XCD, so each XCD produces 16 consecutive heads, and the 128-byte
+    // lines of the fragment-ordered query buffer (8 heads each) are filled
+    // within one L2 rather than written in 16-byte pieces from eight
+    static_assert(H == 128, "eight XCDs x 16 heads");
+    const int h = (bid & 7) * 16 + ((bid >> 3) & 15);
     const int cb = (bid / H) & 3;
     const int rb = bid / (H * 4);
     const int tid = threadIdx.x, lane = tid & 63;
@@ -195,14 +212,14 @@ __device__ __forceinline__ void absorb_q_block(
         const int i = k * 256 + tid, rl = i >> 4, c = i & 15;
         const int r = rb * 64 + rl;
         if (r < R)
-            *reinterpret_cast<u32x4*>(qbuf + ((size_t)r * H + h) * D + cb * 128 + c * 8) =
+            *reinterpret_cast<u32x4*>(qbuf + q_frag_offset(r, h, cb * 128 + c * 8)) =
                 *reinterpret_cast<const u32x4*>(wt + rl * OROWB + c * 16);
     }
     if (cb == 0) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int i = k * 256 + tid, r = rb * 64 + (i >> 3), c8 = i & 7;
-            if (r < R) *reinterpret_cast<u32x4*>(qbuf + ((size_t)r * H + h) * D + DC + c8 * 8) = pe[k];
+            if (r < R) *reinterpret_cast<u32x4*>(qbuf + q_frag_offset(r, h, DC + c8 * 8)) = pe[k];
         }
     }
 }
@@ -531,7 +548,7 @@ __device__ __forceinline__ bool balanced_next(BalancedWalk& wk, const int* __res
 
 template <bool FP8>
 __global__ __launch_bounds__(256, 1) void split_kv_kernel(
-    const unsigned short* __restrict__ qbuf,      // [R][H][576] bf16
+    const unsigned short* __restrict__ qbuf,      // [R][H][576] bf16, fragment order (q_frag_offset)
     const unsigned char* __restrict__ pool,       // [blocks][64][576] bf16 | fp8
     const float* __restrict__ pool_scale,         // [blocks][64] (fp8)
     const int* __restrict__ block_table, int max_blocks,
@@ -542,13 +559,11 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     // which reads the channel-major bf16 blocks.  (The FP8 = false branches
     // below, which read token-major bf16 tiles, are never instantiated.)
     static_assert(FP8, "split_kv_kernel serves the fp8 cache");
-    // bf16: two tiles + the rotary queries of all heads (16 KB) = 160 KiB;
-    // fp8: one bf16 tile + two fp8 staging tiles with scales (rotary queries in VGPRs)
-    constexpr bool QPE_LDS = !FP8;
-    constexpr int QPE_BYTES = H * DR * 2;
+    // one bf16 tile + two fp8 staging tiles with scales; the queries (rotary
+    // part included) stay in VGPRs
     constexpr int STAGE = F8TILE + 256;                     // fp8 staging buffer: codes + scales
-    constexpr int LDS_BYTES = FP8 ? (TILE + 2 * STAGE) : (2 * TILE + QPE_BYTES);
-    constexpr int NQ = QPE_LDS ? 32 : 36;               // bf16 query K-steps kept in VGPRs
+    constexpr int LDS_BYTES = TILE + 2 * STAGE;
+    constexpr int NQ = 36;                                  // bf16 query K-steps kept in VGPRs
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[LDS_BYTES];
     lds_u8* smem = (lds_u8*)smem_raw;
 
@@ -591,9 +606,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         float* lse_dst = part_lse + (size_t)slot * H;
         const int* btab = block_table + (size_t)b * max_blocks;
 
-        // bf16: tiles at 0 and TILE, rotary queries at 2 TILE.
-        // fp8: the bf16 tile at 0, staging buffers at TILE and TILE + STAGE.
-        lds_u8* qpe = smem + 2 * TILE;
+        // the bf16 tile at 0, staging buffers at TILE and TILE + STAGE
 
         auto valid_of = [&](int t) { return min(BS, n_vis - t * BS); };
         // asynchronous load of tile t into `dst` (a bf16 tile, or fp8 staging)
@@ -611,25 +624,14 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         bool t0_in_flight = true;
 
         // this wave's 32 query rows, as MFMA B fragments: lane (hf, l32) holds
-        // channels 16 ks + 8 hf .. +8 of head 32 w + l32
+        // channels 16 ks + 8 hf .. +8 of head 32 w + l32 (one 1 KB read per
+        // K-step, q_frag_offset)
         bf16x8 qf[NQ];
         {
-            const unsigned short* qrow = qbuf + ((size_t)row * H + head) * D + hf * 8;
+            const unsigned short* qrow = qbuf + q_frag_offset(row, 32 * w, 0) + lane * 8;
 #pragma unroll
-            for (int ks = 0; ks < NQ; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+            for (int ks = 0; ks < NQ; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 512);
         }
-        if constexpr (QPE_LDS) {
-            // q_pe of all heads: head h's chunk c (8 channels) at h*128 + ((c ^ g(h)) << 4)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int i = k * 256 + tid;               // 1024 chunks
-                const int h = i >> 3, c = i & 7;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(qbuf + ((size_t)row * H + h) * D + DC + c * 8);
-                *reinterpret_cast<MLA_LDS u32x4*>(qpe + h * 128 + ((c ^ fswz(h & 15)) << 4)) = v;
-            }
-        }
-        const lds_u8* qpe_lane = qpe + head * 128;
-        const int qpe_g = fswz(head & 15);
 
 
         // Per-lane LDS byte offsets.  Score operand (chunk 2 ks + hf of row
@@ -690,11 +692,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                 auto ka = [&](int ks) {
                     return *reinterpret_cast<const MLA_LDS bf16x8*>(kbase + qk_off[ks & 3] + (ks >> 2) * 8192);
                 };
-                auto qb = [&](int ks) -> bf16x8 {
-                    if (ks < NQ) return qf[ks];
-                    const int c = 2 * (ks - 32) + hf;
-                    return *reinterpret_cast<const MLA_LDS bf16x8*>(qpe_lane + ((c ^ qpe_g) << 4));
-                };
+                auto qb = [&](int ks) -> bf16x8 { return qf[ks]; };
                 f32x16 sacc = {};
                 float sv[16];
                 // fp8: token scales of the lane's rows 32 hb + 8 (i/4) + 4 hf + (i%4)
@@ -976,7 +974,7 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
-    const unsigned short* __restrict__ qbuf,      // [R][H][576] bf16
+    const unsigned short* __restrict__ qbuf,      // [R][H][576] bf16, fragment order (q_frag_offset)
     const unsigned char* __restrict__ pool,       // [blocks][64][576] bf16
     const int* __restrict__ block_table, int max_blocks,
     const int* __restrict__ seq_lens, int R, int q_len, int num_splits, float scale_log2,
@@ -1060,12 +1058,13 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
         // complete in order).
         issue_half(hfirst);
         // this wave's 32 query rows, as MFMA B fragments: lane (hf, l32) holds
-        // channels 16 ks + 8 hf .. +8 of head 32 w + l32 (latent 0..31, rotary 32..35)
+        // channels 16 ks + 8 hf .. +8 of head 32 w + l32 (latent 0..31, rotary
+        // 32..35), one 1 KB read per K-step (q_frag_offset)
         bf16x8 qf[36];
         {
-            const unsigned short* qrow = qbuf + ((size_t)row * H + head) * D + hf * 8;
+            const unsigned short* qrow = qbuf + q_frag_offset(row, 32 * w, 0) + lane * 8;
 #pragma unroll
-            for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
+            for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 512);
         }
         issue_half(hfirst + 1);
         issue_half(hfirst + 2);

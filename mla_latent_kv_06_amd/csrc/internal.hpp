@@ -34,7 +34,8 @@ struct DecodeLaunch {
     void* out;
     float* lse;
     // workspace carve-up
-    void* qbuf;                  // [R][H][DC+DR]: bf16 (MFMA path) or f32 (portable)
+    void* qbuf;                  // [R][H][DC+DR]: bf16 in the split-KV kernels' fragment order
+                                 // (MFMA path, q_frag_offset) or f32 row-major (portable)
     void* part_o;                // [R][S][H][DC]: fp16 on the MFMA path, fp32 otherwise
     float* part_lse;             // [R][S][H]
     hipStream_t stream;
