@@ -5,7 +5,10 @@
 Every .hip file under csrc/ is compiled to an object in _build/, then linked
 into mla_latent_kv_06_amd/libmla.so.  The streaming-read probe (probe/, a
 measurement yardstick, not part of the attention path) becomes
-mla_latent_kv_06_amd/libmla_probe.so.  Always rebuilds (no staleness check).
+mla_latent_kv_06_amd/libmla_probe.so.  The same sources compiled with
+-DMLA_PHASE_STAMPS (the split-KV kernel's phase timers, include/mla_debug.h)
+become mla_latent_kv_06_amd/libmla_phases.so.  Always rebuilds (no staleness
+check).
 """
 
 from __future__ import annotations
@@ -22,6 +25,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 PROBE_SRC = os.path.join(PKG, "probe", "read_probe.hip")
 PROBE_LIB = os.path.join(PKG, "libmla_probe.so")
+PHASES_LIB = os.path.join(PKG, "libmla_phases.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -75,14 +79,20 @@ def build(verbose: bool = False) -> str:
     srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
     objs = [os.path.join(BUILD, f[:-4] + ".o") for f in srcs]
     cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(srcs, objs)]
+    pdir = os.path.join(BUILD, "phases")
+    os.makedirs(pdir, exist_ok=True)
+    pobjs = [os.path.join(pdir, f[:-4] + ".o") for f in srcs]
+    cmds += [[HIPCC, *FLAGS, "-DMLA_PHASE_STAMPS", "-c", os.path.join(CSRC, s), "-o", o]
+             for s, o in zip(srcs, pobjs)]
     probe_tmp = PROBE_LIB + ".tmp"
     cmds.append([HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", probe_tmp])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     os.replace(probe_tmp, PROBE_LIB)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    for lib, ob in ((PHASES_LIB, pobjs), (LIB, objs)):
+        tmp = lib + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *ob, "-o", tmp], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

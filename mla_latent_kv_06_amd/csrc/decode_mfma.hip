@@ -973,6 +973,42 @@ __device__ __forceinline__ void barrier_lds() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Phase timers of the split-KV ring kernel, compiled only into the
+// instrumented build (-DMLA_PHASE_STAMPS, libmla_phases.so; include/mla_debug.h).
+// Each wave keeps lap timers in shader cycles (s_memtime): lap k adds the
+// cycles since the previous lap, so the laps of a wave sum to its whole run.
+// Laps: 0 / 1 / 2 the steady-state half-tiles' barrier wait, score chain and
+// value chain (with the softmax threaded in); 8 kernel start (or the previous
+// piece's end) to the piece's start (the schedule walk); 9 to the first
+// half-tile landed (block table, queries, first copies); 10 the first half's
+// scores and softmax; 12 the piece's last two half-tiles and the final value
+// chain; 13 the vote (and any repeated pass); 14 the epilogue (partial o_lat
+// and lse written).  Word 3 counts steady-state half-tiles, 4 the wave's
+// cycles, 5 its pieces, 6 / 7 the low 32 bits of s_memrealtime (100 MHz) at
+// its start and end.  Wave w of workgroup b < kNumCUs writes words
+// 64 b + 16 w .. +16 of g_phase_stamps at its end.
+#ifdef MLA_PHASE_STAMPS
+constexpr int kPhaseWords = kNumCUs * 4 * 16;
+}  // namespace
+// (external linkage, so that the runtime finds the symbol by name)
+__device__ unsigned g_phase_stamps[kPhaseWords];
+namespace {
+#define MLA_LAP(k)                                                                  \
+    do {                                                                            \
+        const unsigned long long t_ = __builtin_readcyclecounter();                 \
+        ph_[k] += (unsigned)(t_ - ph_last_);                                        \
+        ph_last_ = t_;                                                              \
+    } while (0)
+#define MLA_PHASE_COUNT(k) (++ph_[k])
+#else
+#define MLA_LAP(k) \
+    do {           \
+    } while (0)
+#define MLA_PHASE_COUNT(k) \
+    do {                   \
+    } while (0)
+#endif
+
 __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
     const unsigned short* __restrict__ qbuf,      // [R][H][576] bf16, fragment order (q_frag_offset)
     const unsigned char* __restrict__ pool,       // [blocks][64][576] bf16
@@ -991,6 +1027,12 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in an SGPR
     const int l32 = lane & 31, hf = lane >> 5;
     const int head = w * 32 + l32;
+#ifdef MLA_PHASE_STAMPS
+    unsigned ph_[16] = {};
+    const unsigned long long ph_start_ = __builtin_readcyclecounter();
+    const unsigned long long ph_rt0_ = __builtin_amdgcn_s_memrealtime();
+    unsigned long long ph_last_ = ph_start_;
+#endif
 
     // ---- this workgroup's pieces: as in split_kv_kernel ----------------------------
     BalancedWalk wk{};
@@ -1021,6 +1063,8 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
     lds_u8* pbuf = smem + P_OFF;
     int row, t0, t1, pslot, seq_len;
     for (int piece = 0; next_piece(row, t0, t1, pslot, seq_len); ++piece) {
+        MLA_LAP(8);
+        MLA_PHASE_COUNT(5);
         if (piece > 0) __syncthreads();      // the previous piece's epilogue is done with LDS
         const int b = row / q_len, s = row - b * q_len;
         const int n_vis = seq_len - q_len + s + 1;
@@ -1305,6 +1349,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
                 if constexpr (!SCAN && m == NS - DIST) pre = v_prologue(vb, pb);
                 __builtin_amdgcn_sched_barrier(0);
             });
+            if constexpr (SOFT) MLA_LAP(1);
             // the scores leave the accumulator (SOFT: after the first value
             // MFMA, which does not wait for them)
             if constexpr (!SOFT) {
@@ -1352,6 +1397,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
             }
             first_in_flight = false;
             landed(hfirst, true);
+            MLA_LAP(9);
             first_scores(hfirst);
             sv_valid = valid_half(hfirst);
             pw_dst = (lds_u8*)pbuf_of(hfirst);
@@ -1379,9 +1425,13 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
                 plain_softmax(std::false_type{});
                 // every half but the last is full: their softmax runs inside the
                 // iteration that computes their scores
+                MLA_LAP(10);
                 for (int h = hfirst; h < hlast - 1; ++h) {
                     landed(h + 1, false);
+                    MLA_LAP(0);
                     iteration(std::false_type{}, std::true_type{}, h);
+                    MLA_LAP(2);
+                    MLA_PHASE_COUNT(3);
                 }
                 if (hlast > hfirst) {
                     landed(hlast, false);
@@ -1391,6 +1441,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
                 }
                 barrier_lds();                   // the last half's weights are in LDS
                 values(slot_of(hlast), pbuf_of(hlast), [](auto) {});
+                MLA_LAP(12);
             }
             // ---- vote: did any wave's weights run past the reference? ------------------
             wait_vmem_all();                 // (record-less copies included)
@@ -1412,6 +1463,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
             }
             break;
         }
+        MLA_LAP(13);
         l_run += __shfl_xor(l_run, 32, 64);  // the head's two lanes hold disjoint tokens
 
         // ---- epilogue: normalised partial o_lat (fp16) and log-sum-exp ---------------
@@ -1458,7 +1510,19 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
             __builtin_amdgcn_raw_buffer_store_b128(v, prs, (hh * DC + w * 128 + (lane & 15) * 8) * 2, 0, 0);
         }
         if (hf == 0) lse_dst[head] = (m_ref + __builtin_log2f(l_run)) * kLn2;
+        MLA_LAP(14);
     }
+#ifdef MLA_PHASE_STAMPS
+    ph_[4] = (unsigned)(ph_last_ - ph_start_);
+    ph_[6] = (unsigned)ph_rt0_;
+    ph_[7] = (unsigned)__builtin_amdgcn_s_memrealtime();
+    if (blockIdx.x < (unsigned)kNumCUs && lane < 16) {
+        unsigned v = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v = lane == j ? ph_[j] : v;
+        g_phase_stamps[blockIdx.x * 64 + w * 16 + lane] = v;
+    }
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -1868,3 +1932,17 @@ hipError_t launch_decode_mfma(const DecodeLaunch& a, unsigned stages) {
 }
 
 }  // namespace mla
+
+#ifdef MLA_PHASE_STAMPS
+// Copies the ring kernel's phase timers (see g_phase_stamps) to host memory and
+// clears them.  Only the instrumented build exports it.
+extern "C" mla_status mla_debug_phase_stamps(void* host_dst, size_t bytes) {
+    if (host_dst == nullptr) return MLA_ERR_NULL_POINTER;
+    if (bytes != sizeof(unsigned) * mla::kPhaseWords) return MLA_ERR_BAD_SHAPE;
+    if (hipDeviceSynchronize() != hipSuccess) return MLA_ERR_HIP;
+    if (hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(mla::g_phase_stamps), bytes) != hipSuccess) return MLA_ERR_HIP;
+    static unsigned zeros[mla::kPhaseWords];
+    if (hipMemcpyToSymbol(HIP_SYMBOL(mla::g_phase_stamps), zeros, bytes) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+#endif

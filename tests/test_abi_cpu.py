@@ -56,6 +56,26 @@ def test_probe_library_exports_and_validates():
     assert lp.mla_probe_read(ctypes.c_void_p(4096), 0, ctypes.c_void_p(4096), None) == 0
 
 
+def test_phases_build_exports_the_timer_readout_and_nothing_else_differs():
+    """libmla_phases.so (-DMLA_PHASE_STAMPS) exports mla.h's functions plus
+    mla_debug_phase_stamps; libmla.so does not export the latter."""
+    plib = os.path.join(ROOT, "mla_latent_kv_06_amd", "libmla_phases.so")
+
+    def exported(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                             check=True).stdout
+        return {l.split()[-1] for l in out.splitlines() if " T " in l and "mla_" in l}
+    base, ph = exported(LIB), exported(plib)
+    assert "mla_debug_phase_stamps" not in base
+    assert ph == base | {"mla_debug_phase_stamps"}
+    lp = ctypes.CDLL(plib)
+    lp.mla_debug_phase_stamps.restype = ctypes.c_int
+    lp.mla_debug_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    assert lp.mla_debug_phase_stamps(None, 4 * 16384) == 1      # MLA_ERR_NULL_POINTER
+    buf = ctypes.create_string_buffer(16)
+    assert lp.mla_debug_phase_stamps(buf, 16) == 2              # MLA_ERR_BAD_SHAPE
+
+
 @pytest.fixture(scope="module")
 def b():
     from mla_latent_kv_06_amd import binding
