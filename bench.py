@@ -224,7 +224,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the hot path is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "(the library runs the decode of one GPU's share; it has no cross-GPU path)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     from mla_latent_kv_06_amd import synth

@@ -22,7 +22,7 @@ Sources, by page title and section:
   per-head keys and values at every step.  That "decompress" form is what
   ``decode_naive`` computes; it never uses the weight-absorbed shortcut.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent (the plainest reading the rest supports):
 
 * RMSNorm is y = x / sqrt(mean(x^2) + eps) * gamma (the pages name it only).
 * RoPE rotates interleaved pairs (x[2k], x[2k+1]) by angle
