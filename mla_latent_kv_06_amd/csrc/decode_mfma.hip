@@ -269,46 +269,6 @@ __global__ __launch_bounds__(256) void finalize_absorb_kernel(FinalizeArgs f,
 // alias analysis can tell the tile being read from the one being filled.
 typedef MLA_LDS unsigned char lds_u8;
 
-// Issue the asynchronous copy of one bf16 cache block (64 rows x 1152 B,
-// contiguous in memory) into an LDS tile.  Instruction i = 8 cg + q fills
-// positions 64 i .. 64 i + 63: rows 8q .. 8q+7, chunk group cg.  Lane l takes
-// row 8q + l/8 and slot l%8, i.e. chunk 8 cg + ((l%8) ^ g(8q + l/8)).
-__device__ __forceinline__ void issue_tile_bf16(const unsigned char* __restrict__ gtile,
-                                                lds_u8* ltile, int w, int lane) {
-    // row 8q + l/8 has g = f(l/8) ^ 2 (q & 1): two per-lane offsets
-    const unsigned off0 = (lane >> 3) * ROWB + (((lane & 7) ^ fswz(lane >> 3)) << 4);
-    const unsigned off1 = (lane >> 3) * ROWB + (((lane & 7) ^ fswz((lane >> 3) + 8)) << 4);
-    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(gtile, GTILE);
-#pragma unroll
-    for (int k = 0; k < 18; ++k) {
-        const int i = w * 18 + k;                      // wave-uniform
-        const int cg = i >> 3, q = i & 7;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(ltile + i * 1024), 16,
-                                                 (q & 1) ? off1 : off0, q * 8 * ROWB + cg * 128,
-                                                 0, 0);
-    }
-}
-
-// Copy instruction k (0..17) of wave w of the bf16 tile copy above.
-__device__ __forceinline__ void issue_tile_bf16_part(__amdgpu_buffer_rsrc_t rsrc, lds_u8* ltile,
-                                                     int w, int lane, int k) {
-    const unsigned off0 = (lane >> 3) * ROWB + (((lane & 7) ^ fswz(lane >> 3)) << 4);
-    const int i = w * 18 + k;
-    const int cg = i >> 3, q = i & 7;
-    // rows 8q + 8 .. +7 (q odd) have g = f(l/8) ^ 2: chunk slot bit 1 flips
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(ltile + i * 1024), 16,
-                                             (q & 1) ? (off0 ^ 32u) : off0, q * 8 * ROWB + cg * 128,
-                                             0, 0);
-}
-
-// Zero rows valid .. 63 of an LDS tile (their cache slots hold no token).
-__device__ __forceinline__ void zero_rows(lds_u8* ltile, int valid, int tid) {
-    for (int p = valid * NCH + tid; p < BS * NCH; p += 256) {
-        const int t = p / NCH, c = p - t * NCH;
-        *reinterpret_cast<MLA_LDS u32x4*>(ltile + tpos(t, c) * 16) = u32x4{0, 0, 0, 0};
-    }
-}
-
 // Asynchronous copy of one fp8 cache block (64 rows x 576 B, contiguous) into
 // row-major LDS staging, plus its 64 per-token scales after it.
 __device__ __forceinline__ void issue_tile_fp8(const unsigned char* __restrict__ gtile,
@@ -555,9 +515,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
     const int* __restrict__ seq_lens, int R, int q_len, int num_splits, float scale_log2,
     unsigned short* __restrict__ part_o,          // [slots][H][512] fp16
     float* __restrict__ part_lse) {               // [slots][H]
-    // Only the fp8 cache runs here: a bf16 cache runs on split_kv_ring_kernel,
-    // which reads the channel-major bf16 blocks.  (The FP8 = false branches
-    // below, which read token-major bf16 tiles, are never instantiated.)
+    // Only the fp8 cache runs here (a bf16 cache runs on split_kv_ring_kernel).
     static_assert(FP8, "split_kv_kernel serves the fp8 cache");
     // one bf16 tile + two fp8 staging tiles with scales; the queries (rotary
     // part included) stay in VGPRs
@@ -609,18 +567,14 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         // the bf16 tile at 0, staging buffers at TILE and TILE + STAGE
 
         auto valid_of = [&](int t) { return min(BS, n_vis - t * BS); };
-        // asynchronous load of tile t into `dst` (a bf16 tile, or fp8 staging)
+        // asynchronous load of tile t into the fp8 staging buffer `dst`
         auto issue = [&](int t, lds_u8* dst) {
             const size_t blk = (size_t)btab[t];
-            if constexpr (FP8) {
-                issue_tile_fp8(pool + blk * F8TILE, pool_scale + blk * BS, dst, w, lane);
-            } else {
-                issue_tile_bf16(pool + blk * GTILE, dst, w, lane);
-            }
+            issue_tile_fp8(pool + blk * F8TILE, pool_scale + blk * BS, dst, w, lane);
         };
         // The first tile's copy goes out before the query loads, so that the two
         // memory round trips of a piece's start overlap.
-        issue(t0, FP8 ? smem + TILE : smem);
+        issue(t0, smem + TILE);
         bool t0_in_flight = true;
 
         // this wave's 32 query rows, as MFMA B fragments: lane (hf, l32) holds
@@ -671,19 +625,8 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
         // transposed value reads from waiting on the load in flight.
         auto run_tile = [&](int t, const lds_u8* __restrict__ tile, lds_u8* __restrict__ nxt,
                             const lds_u8* __restrict__ stg, bool has_next) __attribute__((always_inline)) {
-            (void)stg;
             const int valid = valid_of(t);
-            // bf16: the next tile's 18 copy instructions of this wave are spread
-            // over the two score chains (one every 4 MFMAs); issued as one burst
-            // they hold the wave at issue while the address unit works through
-            // the workgroup's 72 copies.  Without a next tile the resource has no
-            // records and the copies read nothing.
-            [[maybe_unused]] __amdgpu_buffer_rsrc_t nrs;
-            if constexpr (FP8) {
-                if (has_next) issue(t + 1, nxt);
-            } else {
-                nrs = make_rsrc(pool + (size_t)btab[has_next ? t + 1 : t] * GTILE, has_next ? GTILE : 0);
-            }
+            if (has_next) issue(t + 1, nxt);
 #pragma unroll 1
             for (int hb = 0; hb < 2; ++hb) {
                 if (hb * 32 >= valid) break;
@@ -699,8 +642,8 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                 // (zero past the sequence end), applied to the scores and folded
                 // into the weights, so that keys and values enter the products as
                 // the codes' exact values
-                [[maybe_unused]] float tsc[16];
-                if constexpr (FP8) {
+                float tsc[16];
+                {
                     const MLA_LDS float* lsc =
                         reinterpret_cast<const MLA_LDS float*>(stg + F8TILE);
 #pragma unroll
@@ -716,14 +659,11 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                     for (int ks = 0; ks < 36; ++ks) {
                         if (ks + 2 < 36) a2 = ka(ks + 2);
                         sacc = mfma32(a0, qb(ks), sacc);
-                        if constexpr (!FP8) {
-                            if ((ks & 3) == 0) issue_tile_bf16_part(nrs, nxt, w, lane, hb * 9 + (ks >> 2));
-                        }
                         a0 = a1;
                         a1 = a2;
                     }
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) sv[i] = FP8 ? sacc[i] * tsc[i] : sacc[i];
+                    for (int i = 0; i < 16; ++i) sv[i] = sacc[i] * tsc[i];
                 }
                 // lane holds head `head`, tokens 32 hb + 8 (i/4) + 4 hf + (i%4)
                 if (valid < BS) {
@@ -759,7 +699,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
                     for (int j = 0; j < 8; ++j) {
                         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[k2 * 8 + j], scale_log2, -m_ref));
                         psum += pv;
-                        pu[j] = f32_to_bf16_bits(FP8 ? pv * tsc[k2 * 8 + j] : pv);
+                        pu[j] = f32_to_bf16_bits(pv * tsc[k2 * 8 + j]);
                     }
                     pf[k2] = __builtin_bit_cast(bf16x8, pu);
                 }
@@ -794,31 +734,21 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
             for (int i = 0; i < 16; ++i) o[i] = f32x16{};
             l_run = 0.f;
             overflow = false;
-            if (!t0_in_flight) issue(t0, FP8 ? smem + TILE : smem);   // a later pass
+            if (!t0_in_flight) issue(t0, smem + TILE);   // a later pass
             t0_in_flight = false;
             for (int t = t0; t < t1; ++t) {
                 const int cur = (t - t0) & 1;
                 wait_vmem_all();
                 __syncthreads();             // tile t landed; previous tile fully consumed
                 const bool has_next = t + 1 < t1;
-                if constexpr (FP8) {
-                    lds_u8* st_cur = smem + TILE + cur * STAGE;
-                    lds_u8* st_nxt = smem + TILE + (cur ^ 1) * STAGE;
-                    convert_tile_fp8(st_cur, smem, tid, valid_of(t));
-                    __syncthreads();
-                    run_tile(t, smem, st_nxt, st_cur, has_next);
-                } else {
-                    lds_u8* cur_tile = smem + cur * TILE;
-                    lds_u8* nxt_tile = smem + (cur ^ 1) * TILE;
-                    if (valid_of(t) < BS) {  // last, partial tile of the sequence
-                        zero_rows(cur_tile, valid_of(t), tid);
-                        __syncthreads();
-                    }
-                    run_tile(t, cur_tile, nxt_tile, nullptr, has_next);
-                }
+                lds_u8* st_cur = smem + TILE + cur * STAGE;
+                lds_u8* st_nxt = smem + TILE + (cur ^ 1) * STAGE;
+                convert_tile_fp8(st_cur, smem, tid, valid_of(t));
+                __syncthreads();
+                run_tile(t, smem, st_nxt, st_cur, has_next);
             }
             // ---- vote: did any wave's weights run past the reference? ------------------
-            wait_vmem_all();                 // (record-less copies of the last tile included)
+            wait_vmem_all();
             __syncthreads();                 // all waves are done with the tiles
             MLA_LDS int* votes = reinterpret_cast<MLA_LDS int*>(smem);
             if (lane == 0) votes[w] = __builtin_amdgcn_ballot_w64(overflow) != 0;
