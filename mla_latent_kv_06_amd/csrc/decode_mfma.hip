@@ -1026,20 +1026,21 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
 #pragma unroll
             for (int k = 0; k < 9; ++k) issue_half_part(rs, slot_of(h), w, lane, k);
         };
-        // A piece's start: the first half's copy, this wave's query rows, then
-        // the next two halves' copies, so that the first scores wait only for
-        // the first two groups of memory operations (vector memory operations
-        // complete in order).
-        issue_half(hfirst);
-        // this wave's 32 query rows, as MFMA B fragments: lane (hf, l32) holds
-        // channels 16 ks + 8 hf .. +8 of head 32 w + l32 (latent 0..31, rotary
-        // 32..35), one 1 KB read per K-step (q_frag_offset)
+        // A piece's start: this wave's query rows (their addresses need only
+        // the row, so they go out while the block table is read), the first
+        // half's copy, then the next two halves' copies, so that the first
+        // scores wait only for the first two groups of memory operations
+        // (vector memory operations complete in order).
+        // The query rows, as MFMA B fragments: lane (hf, l32) holds channels
+        // 16 ks + 8 hf .. +8 of head 32 w + l32 (latent 0..31, rotary 32..35),
+        // one 1 KB read per K-step (q_frag_offset).
         bf16x8 qf[36];
         {
             const unsigned short* qrow = qbuf + q_frag_offset(row, 32 * w, 0) + lane * 8;
 #pragma unroll
             for (int ks = 0; ks < 36; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 512);
         }
+        issue_half(hfirst);
         issue_half(hfirst + 1);
         issue_half(hfirst + 2);
         bool first_in_flight = true;
