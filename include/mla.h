@@ -118,13 +118,9 @@ size_t mla_cache_row_bytes(const mla_dims* dims);
 
 /* Bytes of one cache block: block_size * mla_cache_row_bytes(dims).  The pool
  * is an array of these, num_blocks blocks of block_size * D elements
- * (D = kv_lora_rank + qk_rope_dim).  Inside a block:
- *  - FP8_E4M3 and F32 caches are token-major: token t's row at t * D;
- *  - BF16 caches hold sub-blocks of sub = 32 tokens (sub = block_size when
- *    block_size is not a multiple of 32), each channel-major: element
- *    (token t, channel c) at ((t / sub) * D + c) * sub + t % sub.  The
- *    decode's value product then reads 8 consecutive tokens of one latent
- *    channel as one 16-byte unit.
+ * (D = kv_lora_rank + qk_rope_dim).  Inside a block the rows are
+ * token-major for every cache dtype: token t's row of D elements at t * D
+ * (latent channels 0 .. kv_lora_rank - 1, then the rotary key).
  * Only the library's own calls (mla_cache_append) need to write a pool; the
  * layout matters to callers that fill or read pools themselves.
  * With FP8_E4M3 the per-token fp32 scales live in a separate array

@@ -95,14 +95,17 @@ __device__ __forceinline__ void append_finalize_token(
             if (o0 < Dout)
                 *reinterpret_cast<unsigned int*>(static_cast<unsigned char*>(pool) + phys * Dout + o0) = codes;
             if (tid == 0) pool_scale[phys] = sc;
+        } else if constexpr (CDT == MLA_BF16) {
+            // the token's row is contiguous: four outputs, one 8-byte store
+            if (o0 < Dout) {
+                u16x4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = f32_to_bf16_bits(yo[e]);
+                *reinterpret_cast<u16x4*>(static_cast<unsigned short*>(pool) + cache_offset(phys, o0, Dout)) = hv;
+            }
         } else if (o0 < Dout) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if constexpr (CDT == MLA_BF16)
-                    store_act<CDT>(pool, bf16_cache_offset(phys, o0 + e, Dout, BSZ), yo[e]);
-                else
-                    store_act<CDT>(pool, phys * Dout + o0 + e, yo[e]);
-            }
+            for (int e = 0; e < 4; ++e) store_act<CDT>(pool, cache_offset(phys, o0 + e, Dout), yo[e]);
         }
         return;
     }
@@ -189,12 +192,7 @@ __device__ __forceinline__ void append_finalize_token(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int o = tid + 256 * u;
-            if (o < Dout) {
-                if constexpr (CDT == MLA_BF16)
-                    store_act<CDT>(pool, bf16_cache_offset(phys, o, Dout, BSZ), yo[u]);
-                else
-                    store_act<CDT>(pool, phys * Dout + o, yo[u]);
-            }
+            if (o < Dout) store_act<CDT>(pool, cache_offset(phys, o, Dout), yo[u]);
         }
     }
 }

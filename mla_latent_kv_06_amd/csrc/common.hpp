@@ -26,20 +26,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// bf16 cache layout.  A block of bs tokens is stored as sub-blocks of
-// kCacheSub tokens (the whole block when bs is not a multiple of kCacheSub),
-// each channel-major: element (token t, channel c) of a block at
-//   ((t / sub) * D + c) * sub + t % sub.
-// A sub-block's channel rows are then 64 contiguous bytes, and the decode
-// reads 8 consecutive tokens of one channel (its value operand) with one
-// 16-byte load.  (fp8 and fp32 caches stay token-major: t * D + c.)
-constexpr int kCacheSub = 32;
-__host__ __device__ __forceinline__ int cache_sub(int bs) { return bs % kCacheSub == 0 ? kCacheSub : bs; }
-// element offset of (slot = block * bs + t, channel c) in a bf16 pool
-__host__ __device__ __forceinline__ size_t bf16_cache_offset(size_t slot, int c, int D, int bs) {
-    const size_t blk = slot / bs;
-    const int t = (int)(slot - blk * bs), sub = cache_sub(bs);
-    return blk * (size_t)bs * D + ((size_t)(t / sub) * D + c) * sub + t % sub;
+// Cache layout: blocks of bs token rows, token-major for every dtype, so
+// element (slot = block * bs + t, channel c) sits at slot * D + c.
+__host__ __device__ __forceinline__ size_t cache_offset(size_t slot, int c, int D) {
+    return slot * (size_t)D + c;
 }
 
 // ---- scalar conversions ---------------------------------------------------

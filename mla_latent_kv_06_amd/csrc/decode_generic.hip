@@ -22,7 +22,7 @@ __device__ __forceinline__ float cache_val(const void* pool, const float* pscale
         const unsigned char code = static_cast<const unsigned char*>(pool)[phys * D + c];
         return e4m3_to_f32(code) * pscale[phys];
     } else if constexpr (CDT == MLA_BF16) {
-        return bf16_bits_to_f32(static_cast<const unsigned short*>(pool)[bf16_cache_offset(phys, c, D, bs)]);
+        return bf16_bits_to_f32(static_cast<const unsigned short*>(pool)[cache_offset(phys, c, D)]);
     } else {
         return static_cast<const float*>(pool)[phys * D + c];
     }

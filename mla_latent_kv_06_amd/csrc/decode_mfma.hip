@@ -819,14 +819,10 @@ __global__ __launch_bounds__(256, 1) void split_kv_kernel(
 //      O^T (128 cols x 128 heads) += V^T (128 x 32) . P^T          32 MFMA
 //    with every head block's weights read from LDS.  Each value fragment
 //    then feeds four MFMAs (one per head block).
-// The cache's bf16 blocks are channel-major in sub-blocks of 32 tokens (one
-// half-tile: 576 channel rows of 64 bytes), so the value operand -- 8
-// consecutive tokens of one latent channel -- is one 16-byte LDS read, and
-// the score operand -- 8 channels of one token -- comes from the transposing
-// 8-byte reads.  Measured on MI355X, 8-byte LDS reads (transposing or not)
-// run at about half speed while buffer-to-LDS copies land, 16-byte reads
-// barely slow down; the copies issued during S land during V, so V, which
-// has the most LDS reads per MFMA, gets the 16-byte ones.
+// The cache's blocks are token-major (1152-byte rows) and a half-tile stays
+// token-major in LDS, so the score operand -- 8 channels of one token -- is
+// one 16-byte LDS read, and the value operand -- 8 consecutive tokens of one
+// latent channel -- comes from two transposing 8-byte reads.
 // Loop iteration h (half h of the piece) runs, per wave:
 //   S_{h+1} (36 MFMA, with the copy of half h+3: 9 instructions)
 //   V_h     (32 MFMA, with the softmax of S_{h+1} threaded between them;
@@ -844,46 +840,47 @@ constexpr int HROWS = 32;                 // tokens per half-tile (= the cache's
 constexpr int HALF = HROWS * ROWB;        // 36864 bytes
 constexpr int NRING = 4;                  // ring slots
 constexpr int PBUF = 4 * 2 * 1024;        // weights of one half: 4 head blocks x 2 K-steps x 1 KB
-static_assert(HROWS == kCacheSub, "a half-tile is one channel-major sub-block of the cache");
+static_assert(HALF == 36 * 1024 && BS == 2 * HROWS, "a half-tile is 36 copies of 1 KB, half a block");
 
-// Half-tile layout in LDS.  Channel row ch (64 bytes: 4 chunks of 8 tokens)
-// keeps its chunk c at 16-byte slot 4 ch + (c ^ hswz(ch)), hswz(ch) =
-// bit2(ch) | (bit1(ch) ^ bit3(ch)) << 1.  The value operand's 16-byte reads
-// (one chunk of consecutive rows) then fall on distinct banks for any 8
-// (32 banks) or 16 (64 banks) aligned rows -- hswz is one-to-one in
-// (bit1, bit2) for a fixed bit3 and in (bit2, bit3) for a fixed bit1 --
-// and so do the score operand's transposing 8-byte reads (16 lanes: 4
-// consecutive rows x 4 groups of 4 tokens; rows 2 apart differ in hswz's
-// high bit).  Each copy instruction still moves 1 KB contiguous in memory
-// (16 channel rows).
-__device__ __forceinline__ int hswz(int ch) { return ((ch >> 2) & 1) | ((((ch >> 1) ^ (ch >> 3)) & 1) << 1); }
+// Half-tile layout in LDS.  Token t's row (1152 bytes: 9 groups of 128
+// bytes, 8 chunks of 8 channels each) sits at t * 1152, as in memory, with
+// the chunks of every group permuted: logical chunk x of a group at 16-byte
+// position x ^ tswz(t), tswz(t) = bit1(t) << 2 | bits 2..3 of t.  Rows are
+// 4.5 x 256 bytes apart, so a row's bank offset is 128 (t & 1), and tswz
+// separates the rest:
+//  - score operand (16-byte reads of one chunk of 16 aligned rows): over
+//    the 8 even or the 8 odd rows, tswz takes each of its 8 values once;
+//  - value operand (transposing 8-byte reads, 32 lanes: 4 aligned rows x
+//    4 aligned chunks): of the two even (odd) rows, tswz differs in bit 2,
+//    so they fall on the two different 4-chunk halves of the group.
+__device__ __forceinline__ int tswz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
 
 // Copy instruction k (0..8) of wave w for one half-tile: instruction
-// i = 9 w + k fills slots 64 i .. 64 i + 63, i.e. channel rows 16 i .. +16;
-// lane l takes row 16 i + l/4, slot l%4, i.e. chunk (l%4) ^ hswz(l/4) of it
-// (16 i leaves bits 0..3 of the row to l/4), at byte 1024 i + 64 (l/4) +
-// 16 chunk of the sub-block.
+// i = 9 w + k moves bytes 1024 i .. +1024 of the half into the same bytes of
+// the slot.  Lanes 8 j .. 8 j + 7 fill 128-byte group G = 8 i + j, i.e.
+// group G % 9 of token G / 9 = 8 w + (8 k + j) / 9, and lane 8 j + p fills
+// position p with logical chunk p ^ tswz(token).  copy_swizzles packs the 9
+// tswz values of a lane (3 bits each, instruction k at bit 3 k).
+__device__ __forceinline__ unsigned copy_swizzles(int w, int lane) {
+    unsigned packed = 0;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) packed |= (unsigned)tswz(8 * w + (8 * k + (lane >> 3)) / 9) << (3 * k);
+    return packed;
+}
 __device__ __forceinline__ void issue_half_part(__amdgpu_buffer_rsrc_t rsrc, lds_u8* slot, int w,
-                                                int lane, int k) {
+                                                int lane, unsigned swz, int k) {
     const int i = w * 9 + k;
-    const unsigned off = (lane >> 2) * 64 + (((lane & 3) ^ hswz(lane >> 2)) << 4);
+    const unsigned off = ((lane >> 3) << 7) + ((((unsigned)lane ^ (swz >> (3 * k))) & 7) << 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MLA_LDS void*)(slot + i * 1024), 16, off, i * 1024,
                                              0, 0);
 }
 
-// Zero tokens valid .. 31 of a half-tile slot's latent rows (their cache
-// slots hold no token; the value product must not meet NaN there).
+// Zero the latent channels (the first 1024 bytes of the row, whatever the
+// chunk order) of tokens valid .. 31 of a half-tile slot: their cache slots
+// hold no token, and the value product must not meet NaN there.
 __device__ __forceinline__ void zero_half_tokens(lds_u8* slot, int valid, int tid) {
-    for (int p = tid; p < DC * 4; p += 256) {
-        const int ch = p >> 2, c = p & 3;
-        if (8 * c + 8 <= valid) continue;
-        MLA_LDS u16x8* q = reinterpret_cast<MLA_LDS u16x8*>(slot + (4 * ch + (c ^ hswz(ch))) * 16);
-        u16x8 v = *q;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (8 * c + e >= valid) v[e] = 0;
-        *q = v;
-    }
+    for (int p = valid * 64 + tid; p < HROWS * 64; p += 256)
+        *reinterpret_cast<MLA_LDS u16x8*>(slot + (p >> 6) * ROWB + (p & 63) * 16) = u16x8{};
 }
 
 // Workgroup barrier after this wave's vector memory operations up to the 9
@@ -957,6 +954,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in an SGPR
     const int l32 = lane & 31, hf = lane >> 5;
     const int head = w * 32 + l32;
+    const unsigned cswz = copy_swizzles(w, lane);   // this lane's copy swizzles
 #ifdef MLA_PHASE_STAMPS
     unsigned ph_[16] = {};
     const unsigned long long ph_start_ = __builtin_readcyclecounter();
@@ -1024,7 +1022,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
         auto issue_half = [&](int h) {
             const __amdgpu_buffer_rsrc_t rs = half_rsrc(h);
 #pragma unroll
-            for (int k = 0; k < 9; ++k) issue_half_part(rs, slot_of(h), w, lane, k);
+            for (int k = 0; k < 9; ++k) issue_half_part(rs, slot_of(h), w, lane, cswz, k);
         };
         // A piece's start: this wave's query rows (their addresses need only
         // the row, so they go out while the block table is read), the first
@@ -1047,36 +1045,45 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
 
         // Per-lane LDS byte offsets.
         // Score operand of K-step ks (channels 16 ks + 8 hf .. +8 of one token
-        // per lane), two transposing reads (channels +0..3, +4..7): in
-        // 16-lane group g, lane j = 4 r + b points at channel row
-        // 16 ks + 8 hf + 4 e + r and 4 tokens 16 (g & 1) + 4 perm(b), and
-        // receives token 16 (g & 1) + 4 perm(j / 4) + j % 4 -- the MFMA row
-        // l32 with bits 2 and 3 exchanged (perm(b) exchanges b's two bits).
-        // So the scores' accumulator row m holds token m with bits 2 and 3
-        // exchanged: lane (hf, l32) ends up with tokens 16 (i/8) + 8 hf + i%8
-        // in sv[i], the order in which the value operand reads them.
-        int s_off[2], v_off[2];
+        // per lane): one 16-byte read of chunk 2 ks + hf of token ts = l32
+        // with bits 2 and 3 exchanged, i.e. group ks / 4, position
+        // (2 (ks % 4)) ^ hf ^ tswz(ts).  So the scores' accumulator row m
+        // holds token m with bits 2 and 3 exchanged: lane (hf, l32) ends up
+        // with tokens 16 (i/8) + 8 hf + i%8 in sv[i], the order in which the
+        // value operand reads them.
+        int s_off[4], v_off[2][2];
         {
-            const int j = lane & 15, r = j >> 2, b = j & 3;
-            const int tq = 4 * ((lane >> 4) & 1) + (((b & 1) << 1) | (b >> 1));   // 4-token group
+            const int ts = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 >> 1) & 4);
+            const int tau = tswz(ts) ^ hf;
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int row = 8 * hf + 4 * e + r;
-                s_off[e] = row * 64 + (((tq >> 1) ^ hswz(row)) << 4) + (tq & 1) * 8;
-            }
+            for (int c = 0; c < 4; ++c) s_off[c] = ts * ROWB + (((2 * c) ^ tau) << 4);
         }
         // Value operand: V^T for latent channels 32 cm + l32, K-step k2:
-        // tokens 16 k2 + 8 hf .. +8, one chunk of the channel row.
+        // tokens 16 k2 + 8 hf .. +8, two transposing reads (tokens +0..3,
+        // +4..7).  In 16-lane group g, lane 4 r + b points at token row
+        // 16 k2 + 8 (g >> 1) + 4 e + r, channels 32 cm + 16 (g & 1) + 4 b .. +3
+        // -- chunk 4 (cm & 1) + 2 (g & 1) + b / 2 of group cm / 2, half b & 1 --
+        // and receives channel 32 cm + l32's four tokens.  v_off[cm & 1][e];
+        // k2 adds 16 rows, which leaves tswz unchanged.
+        {
+            const int g = lane >> 4, r = (lane >> 2) & 3, b = lane & 3;
+            const int x = 2 * (g & 1) + (b >> 1);
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) v_off[k2] = l32 * 64 + (((2 * k2 + hf) ^ hswz(l32)) << 4);
+            for (int e = 0; e < 2; ++e) {
+                const int t = 8 * (g >> 1) + 4 * e + r;
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    v_off[p][e] = t * ROWB + (((4 * p + x) ^ tswz(t)) << 4) + 8 * (b & 1);
+            }
+        }
         auto k_frag = [&](const lds_u8* sbase, int ks) __attribute__((always_inline)) -> bf16x8 {
-            const lds_u8* kb = sbase + ks * 1024;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(kb + s_off[0]));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(kb + s_off[1]));
-            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            return *reinterpret_cast<const MLA_LDS bf16x8*>(sbase + s_off[ks & 3] + (ks >> 2) * 128);
         };
         auto v_frag = [&](const lds_u8* vbase, int cm, int k2) __attribute__((always_inline)) -> bf16x8 {
-            return *reinterpret_cast<const MLA_LDS bf16x8*>(vbase + cm * 2048 + v_off[k2]);
+            const lds_u8* vb = vbase + (cm >> 1) * 128 + k2 * 16 * ROWB;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + v_off[cm & 1][0]));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + v_off[cm & 1][1]));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         };
         // weights of head block hb, K-step k2, as the MFMA B operand: 1 KB,
         // lane l at 16 l
@@ -1275,7 +1282,7 @@ __global__ __launch_bounds__(256, 1) void split_kv_ring_kernel(
                 const bf16x8 a = ring[m % DIST];
                 if constexpr (m + DIST < NS) ring[m % DIST] = k_frag(sb, m + DIST);
                 sacc = mfma32(a, qf[m], sacc);
-                if constexpr (m % 4 == 0) issue_half_part(crs, cb, w, lane, m / 4);
+                if constexpr (m % 4 == 0) issue_half_part(crs, cb, w, lane, cswz, m / 4);
                 // the value chain's first operands, read while the scores finish
                 if constexpr (!SCAN && m == NS - DIST) pre = v_prologue(vb, pb);
                 __builtin_amdgcn_sched_barrier(0);

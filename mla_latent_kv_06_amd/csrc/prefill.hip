@@ -101,18 +101,14 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(
     const size_t row0 = (size_t)b * Tpad + (size_t)k * PBS;
     const int tid = threadIdx.x;
     if (!fp8) {
-        // The block's two 32-token sub-blocks are channel-major (channel rows
-        // of 32 tokens): thread p takes token r = p % 64 and 8 channels
-        // 8 c .. +8, so the 2-byte reads of consecutive threads are adjacent
-        // tokens of one channel row, and writes token r's 16 bytes.
+        // token-major rows: thread p takes chunk c (8 channels) of token r, so
+        // consecutive threads read and write consecutive 16 bytes
         const unsigned short* src = reinterpret_cast<const unsigned short*>(pool) + (size_t)blk * PBS * (PDC + PDR);
         for (int p = tid; p < PBS * 72; p += 256) {          // 72 chunks of 8 channels per token
-            const int r = p & (PBS - 1), c = p / PBS;
+            const int r = p / 72, c = p - r * 72;
             const int t = k * PBS + r;
-            const unsigned short* col = src + ((size_t)(r / kCacheSub) * (PDC + PDR) + c * 8) * kCacheSub + r % kCacheSub;
-            u16x8 v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = t < len ? col[e * kCacheSub] : (unsigned short)0;
+            const u16x8 v = t < len ? *reinterpret_cast<const u16x8*>(src + (size_t)r * (PDC + PDR) + c * 8)
+                                    : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
             unsigned short* dst = c < 64 ? x + (row0 + r) * PDC + c * 8 : kr + (row0 + r) * PDR + (c - 64) * 8;
             *reinterpret_cast<u16x8*>(dst) = v;
         }

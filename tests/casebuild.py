@@ -10,8 +10,8 @@ the oracle's float64 functions, then stored in the cache dtype:
 
 Unused pool slots and spare blocks are poisoned with NaN so a kernel that
 reads outside the visible tokens shows it.  Pools are held in the library's
-layout (``mla_latent_kv_06_amd.layout``: bf16 blocks channel-major in
-sub-blocks of 32 tokens); ``Case.rows`` gives token rows.
+layout (``mla_latent_kv_06_amd.layout``: token-major blocks);
+``Case.rows`` gives token rows.
 """
 
 from __future__ import annotations

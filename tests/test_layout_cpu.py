@@ -1,10 +1,8 @@
 """The host-side pool views (``mla_latent_kv_06_amd.layout``) against the block
 layout include/mla.h states for cache_pool, element by element with plain
-loops: bf16 blocks hold sub-blocks of 32 tokens (the whole block when the
-block size is not a multiple of 32), each channel-major -- element (token t,
-channel c) of a block at ((t / sub) * D + c) * sub + t % sub; fp8 and fp32
-blocks are token-major.  The GPU tests feed the oracle through these views,
-so they are pinned here against the stated formula rather than against
+loops: every cache dtype is token-major -- element (token t, channel c) of a
+block at t * D + c.  The GPU tests feed the oracle through these views, so
+they are pinned here against the stated formula rather than against
 themselves."""
 
 from __future__ import annotations
@@ -16,11 +14,8 @@ import torch
 from mla_latent_kv_06_amd import layout
 
 
-def stated_offset(t, c, D, bs, channel_major):
-    if not channel_major:
-        return t * D + c
-    sub = 32 if bs % 32 == 0 else bs
-    return ((t // sub) * D + c) * sub + t % sub
+def stated_offset(t, c, D):
+    return t * D + c
 
 
 @pytest.mark.parametrize("bs,D,dtype", [(64, 7, "bf16"), (96, 5, "bf16"), (48, 3, "bf16"),
@@ -30,12 +25,11 @@ def test_pool_rows_follows_the_stated_layout(bs, D, dtype):
     rng = np.random.default_rng(7)
     pool = rng.integers(0, 60000, size=(nblk, bs, D)).astype(np.uint16)
     flat = pool.reshape(nblk, bs * D)
-    cm = dtype == "bf16"
     want = np.empty((nblk * bs, D), np.uint16)
     for blk in range(nblk):
         for t in range(bs):
             for c in range(D):
-                want[blk * bs + t, c] = flat[blk, stated_offset(t, c, D, bs, cm)]
+                want[blk * bs + t, c] = flat[blk, stated_offset(t, c, D)]
     got = layout.pool_rows(pool, dtype)
     assert np.array_equal(got, want)
     # torch tensors take the same path
@@ -49,7 +43,9 @@ def test_pool_rows_follows_the_stated_layout(bs, D, dtype):
 
 
 def test_planted_transpose_is_caught():
-    """A token-major reading of a bf16 pool differs from the stated layout."""
+    """A channel-major reading of a block differs from the stated layout, so
+    the element-by-element check above would catch a transposed view."""
     bs, D = 64, 5
     pool = np.arange(2 * bs * D, dtype=np.uint16).reshape(2, bs, D)
-    assert not np.array_equal(layout.pool_rows(pool, "bf16"), pool.reshape(-1, D))
+    transposed = pool.reshape(2, D, bs).transpose(0, 2, 1).reshape(-1, D)
+    assert not np.array_equal(layout.pool_rows(pool, "bf16"), transposed)
